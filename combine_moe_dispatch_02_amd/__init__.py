@@ -1,0 +1,25 @@
+"""MI355X-native single-GPU MoE dispatch -> expert FFN -> combine (libmoe355, C ABI + HIP).
+
+The product path is the in-tree ``libmoe355.so``; importing this package does not
+load it, the first call does, and fails loudly if it has not been built.
+"""
+from .layer import (  # noqa: F401
+    MOE_BF16,
+    MOE_FP8_E4M3_G128,
+    MoeError,
+    Plan,
+    StreamMoE,
+    TileConfig,
+    Workspace,
+    device_cu_count,
+    make_streams,
+    moe_combine,
+    moe_dispatch,
+    moe_expert_ffn,
+    moe_get_error,
+    moe_plan,
+    moe_query_pool_rows,
+    pool_rows_upper_bound,
+    stream_moe,
+    workspace_bytes,
+)

@@ -1,0 +1,177 @@
+// C ABI of libmoe355: argument validation, workspace layout, launches.
+// The contract of each entry point is stated in include/moe355.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n;
+}
+
+static bool valid_tile(int32_t tile) { return tile == 16 || tile == 32 || tile == 64 || tile == 128; }
+
+// shape checks common to every call that takes a plan
+static int check_plan(const moe_plan_t* p) {
+  if (!p) return MOE_ERR_INVALID;
+  if (p->T < 1 || p->K < 1 || p->K > 16 || p->E_local < 1 || p->E_local > 1024 || p->expert_begin < 0)
+    return MOE_ERR_INVALID;
+  if (!valid_tile(p->tile)) return MOE_ERR_INVALID;
+  if ((int64_t)p->T * p->K > (int64_t)1 << 30) return MOE_ERR_UNSUPPORTED;
+  const int64_t bound = pool_rows_bound(p->T, p->K, p->E_local, p->tile);
+  if (bound > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (p->rows_cap < bound || p->rows_cap % p->tile != 0) return MOE_ERR_INVALID;
+  if (!p->counts || !p->offsets || !p->pos || !p->src || !p->tile_expert || !p->num_tiles || !p->tile_ready)
+    return MOE_ERR_INVALID;
+  return MOE_OK;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+MOE355_API size_t moe_pool_rows_upper_bound(int32_t T, int32_t K, int32_t E_local, int32_t tile) {
+  if (T < 1 || K < 1 || K > 16 || E_local < 1 || E_local > 1024 || !valid_tile(tile)) return 0;
+  return (size_t)pool_rows_bound(T, K, E_local, tile);
+}
+
+MOE355_API size_t moe_workspace_bytes(int32_t T, int32_t K, int32_t E_local, int32_t tile, int32_t pool_rows,
+                                      int32_t I, int32_t dtype) {
+  if (T < 1 || K < 1 || K > 16 || E_local < 1 || E_local > 1024 || !valid_tile(tile)) return 0;
+  if (pool_rows < 0 || I < 0 || (dtype != MOE_BF16 && dtype != MOE_FP8_E4M3_G128)) return 0;
+  if (dtype == MOE_FP8_E4M3_G128 && I % 128 != 0) return 0;
+  return ws_layout(T, K, E_local, tile, pool_rows, I, dtype).total;
+}
+
+MOE355_API int moe_plan(const int32_t* topk_idx, const moe_plan_t* plan, void* ws, size_t ws_bytes,
+                        void* stream) {
+  int rc = check_plan(plan);
+  if (rc != MOE_OK) return rc;
+  if (!topk_idx || !ws) return MOE_ERR_INVALID;
+  const WsLayout L = ws_layout(plan->T, plan->K, plan->E_local, plan->tile, 0, 0, MOE_BF16);
+  if (ws_bytes < L.plan_end) return MOE_ERR_INVALID;
+  return launch_plan(topk_idx, *plan, L, static_cast<char*>(ws), static_cast<hipStream_t>(stream));
+}
+
+MOE355_API int moe_query_pool_rows(const moe_plan_t* plan, int32_t* host_P, void* stream) {
+  int rc = check_plan(plan);
+  if (rc != MOE_OK) return rc;
+  if (!host_P) return MOE_ERR_INVALID;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(host_P, plan->offsets + plan->E_local, sizeof(int32_t), hipMemcpyDeviceToHost, s) !=
+      hipSuccess)
+    return MOE_ERR_HIP;
+  return hipStreamSynchronize(s) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+MOE355_API int moe_dispatch(const void* x, int32_t H, int32_t act_dtype, const moe_plan_t* plan,
+                            int32_t pool_rows, void* pool, float* pool_s, uint32_t epoch, void* ws,
+                            size_t ws_bytes, void* stream) {
+  int rc = check_plan(plan);
+  if (rc != MOE_OK) return rc;
+  if (!x || !pool || !ws || epoch == 0 || H < 8 || pool_rows < 0) return MOE_ERR_INVALID;
+  if (act_dtype == MOE_BF16) {
+    if (pool_s) return MOE_ERR_INVALID;
+  } else if (act_dtype == MOE_FP8_E4M3_G128) {
+    if (!pool_s) return MOE_ERR_INVALID;
+    if (H % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  } else {
+    return MOE_ERR_INVALID;
+  }
+  if (H % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)H * 2 > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  const WsLayout L = ws_layout(plan->T, plan->K, plan->E_local, plan->tile, 0, 0, MOE_BF16);
+  if (ws_bytes < L.plan_end) return MOE_ERR_INVALID;
+  return launch_dispatch(x, H, act_dtype, *plan, pool_rows, pool, pool_s, epoch, L, static_cast<char*>(ws),
+                         static_cast<hipStream_t>(stream));
+}
+
+MOE355_API int moe_expert_ffn(const moe_plan_t* plan, int32_t pool_rows, const void* pool, const float* pool_s,
+                              const void* w1, const float* w1_s, const void* w2, const float* w2_s, int32_t H,
+                              int32_t I, int32_t dtype, uint32_t epoch, void* ws, size_t ws_bytes, void* y_pool,
+                              const moe_tile_config* cfg, void* stream) {
+  int rc = check_plan(plan);
+  if (rc != MOE_OK) return rc;
+  if (!pool || !w1 || !w2 || !ws || !y_pool || epoch == 0 || H < 1 || I < 1) return MOE_ERR_INVALID;
+  if (pool_rows < 1 || pool_rows % plan->tile != 0) return MOE_ERR_INVALID;
+  const bool fp8 = dtype == MOE_FP8_E4M3_G128;
+  if (dtype != MOE_BF16 && !fp8) return MOE_ERR_INVALID;
+  if (fp8 && (!pool_s || !w1_s || !w2_s)) return MOE_ERR_INVALID;
+  if (!fp8 && (pool_s || w1_s || w2_s)) return MOE_ERR_INVALID;
+  const int32_t block_n = cfg ? cfg->block_n : 0;
+  rc = ffn_supported(H, I, dtype, plan->tile, block_n);
+  if (rc != MOE_OK) return rc;
+  if ((int64_t)pool_rows * H * 2 > ((int64_t)1 << 40)) return MOE_ERR_UNSUPPORTED;
+  const WsLayout L = ws_layout(plan->T, plan->K, plan->E_local, plan->tile, pool_rows, I, dtype);
+  if (ws_bytes < L.total) return MOE_ERR_INVALID;
+  if (cfg && cfg->gemm_workgroups < 0) return MOE_ERR_INVALID;
+  FfnLaunch f;
+  f.plan = plan;
+  f.pool_rows = pool_rows;
+  f.pool = pool;
+  f.pool_s = pool_s;
+  f.w1 = w1;
+  f.w1_s = w1_s;
+  f.w2 = w2;
+  f.w2_s = w2_s;
+  f.H = H;
+  f.I = I;
+  f.dtype = dtype;
+  f.epoch = epoch;
+  f.y_pool = y_pool;
+  f.block_n = block_n;
+  f.workgroups = cfg ? cfg->gemm_workgroups : 0;
+  const uint64_t us = (cfg && cfg->spin_timeout_us) ? cfg->spin_timeout_us : 2000000u;
+  f.timeout_ticks = us * 100u;  // s_memrealtime counts at 100 MHz
+  return launch_expert_ffn(f, L, static_cast<char*>(ws), static_cast<hipStream_t>(stream));
+}
+
+MOE355_API int moe_combine(const void* y_pool, int32_t pool_rows, const float* topk_weights,
+                           const moe_plan_t* plan, int32_t H, void* out, void* stream) {
+  int rc = check_plan(plan);
+  if (rc != MOE_OK) return rc;
+  if (!y_pool || !topk_weights || !out || H < 8 || pool_rows < 0) return MOE_ERR_INVALID;
+  if (H % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)H * 2 > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  return launch_combine(y_pool, pool_rows, topk_weights, *plan, H, out, static_cast<hipStream_t>(stream));
+}
+
+MOE355_API int moe_get_error(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws || ws_bytes < 256) return MOE_ERR_INVALID;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t code = 0;
+  uint32_t* err = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + WsLayout{}.err);
+  if (hipMemcpyAsync(&code, err, sizeof(code), hipMemcpyDeviceToHost, s) != hipSuccess) return MOE_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return MOE_ERR_HIP;
+  if (code != 0) {
+    if (hipMemsetAsync(err, 0, sizeof(uint32_t), s) != hipSuccess) return MOE_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return MOE_ERR_HIP;
+  }
+  return (int)code;
+}
+
+MOE355_API const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    case MOE_ERR_TIMEOUT: return "ready-flag wait timed out";
+  }
+  return "unknown status";
+}
+
+MOE355_API int moe_device_cu_count(void) { return device_cu_count(); }
+
+}  // extern "C"

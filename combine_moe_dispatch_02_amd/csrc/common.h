@@ -1,0 +1,192 @@
+// Internal device helpers of libmoe355 (gfx950, wave64). Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe355.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+// --------------------------------------------------------------------------
+// workspace layout (shared by every entry point; offsets depend only on shape)
+// --------------------------------------------------------------------------
+constexpr int kPlanWaves = 4;            // waves per plan block
+constexpr int kPairsPerWave = 1024;      // pairs one plan wave ranks
+constexpr int kPairsPerBlock = kPlanWaves * kPairsPerWave;
+
+struct WsLayout {
+  size_t err = 0;        // uint32: first device error code (0 = none)
+  size_t done = 64;      // uint32: plan blocks finished (reset by the last one)
+  size_t hist = 256;     // int32 [ncols][E_local]: per-wave expert counts, then bases
+  size_t fill = 0;       // uint32 [ntiles_cap]: rows stored per tile by dispatch
+  size_t h = 0;          // h [pool_rows][I]: bf16, or e4m3 codes
+  size_t hs = 0;         // float [pool_rows][I/128] (fp8 only)
+  size_t plan_end = 0;   // end of what plan/dispatch need
+  size_t total = 0;
+  int32_t ncols = 0;
+  int32_t ntiles_cap = 0;
+};
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+inline int64_t pool_rows_bound(int64_t T, int64_t K, int64_t E, int64_t tile) {
+  return (T * K + E * (tile - 1)) / tile * tile;
+}
+
+inline WsLayout ws_layout(int32_t T, int32_t K, int32_t E, int32_t tile, int64_t pool_rows,
+                          int32_t I, int32_t dtype) {
+  WsLayout L;
+  const int64_t pairs = (int64_t)T * K;
+  const int64_t cap = pool_rows_bound(T, K, E, tile);
+  L.ncols = (int32_t)((pairs + kPairsPerWave - 1) / kPairsPerWave);
+  L.ntiles_cap = (int32_t)(cap / tile);
+  L.fill = align_up(L.hist + (size_t)L.ncols * E * 4, 256);
+  L.plan_end = align_up(L.fill + (size_t)L.ntiles_cap * 4, 256);
+  if (pool_rows <= 0) pool_rows = cap;
+  size_t off = L.plan_end;
+  if (I > 0) {
+    const size_t elem = dtype == MOE_FP8_E4M3_G128 ? 1 : 2;
+    L.h = off;
+    off = align_up(off + (size_t)pool_rows * I * elem, 256);
+    if (dtype == MOE_FP8_E4M3_G128) {
+      L.hs = off;
+      off = align_up(off + (size_t)pool_rows * (I / 128) * 4, 256);
+    }
+  }
+  L.total = off;
+  return L;
+}
+
+// --------------------------------------------------------------------------
+// device error word: the first error recorded wins
+// --------------------------------------------------------------------------
+__device__ inline void record_error(uint32_t* err, uint32_t code) {
+  uint32_t expected = 0;
+  __hip_atomic_compare_exchange_strong(err, &expected, code, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline uint32_t load_error(const uint32_t* err) {
+  return __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// --------------------------------------------------------------------------
+// wave primitives
+// --------------------------------------------------------------------------
+__device__ inline int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0)); }
+
+__device__ inline uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+
+// number of set bits of `mask` in lanes below this one
+__device__ inline int mask_rank(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+}
+
+// Lanes of the wave whose `key` is equal form one group; returns this lane's
+// group as a lane mask. One ballot per key bit: a lane's peers are the valid
+// lanes that agree with it on every bit. Must be called by the whole wave.
+__device__ inline uint64_t match_key(uint32_t key, bool valid, int nbits) {
+  uint64_t peers = ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (key >> b) & 1u;
+    const uint64_t m = ballot(bit);
+    peers &= bit ? m : ~m;
+  }
+  return peers;
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ inline int dpp_or_zero(int v) {
+  // lanes without a valid source (outside the row, or rows masked off) read 0
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xf, false);
+}
+
+// Inclusive prefix sum over the 64 lanes from DPP moves: a Hillis-Steele scan
+// inside each 16-lane row (row_shr 1, 2, 4, 8), then row 15 -> rows 1 and 3
+// (row_bcast:15) and lane 31 -> rows 2 and 3 (row_bcast:31).
+__device__ inline int wave_inclusive_scan(int v) {
+  v += dpp_or_zero<0x111, 0xf>(v);
+  v += dpp_or_zero<0x112, 0xf>(v);
+  v += dpp_or_zero<0x114, 0xf>(v);
+  v += dpp_or_zero<0x118, 0xf>(v);
+  v += dpp_or_zero<0x142, 0xa>(v);
+  v += dpp_or_zero<0x143, 0xc>(v);
+  return v;
+}
+
+__device__ inline int readlane(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+
+// max over the 16 lanes of a DPP row (rotations by 8, 4, 2, 1); every lane gets it
+__device__ inline float row16_max(float v) {
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xf, 0xf, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xf, 0xf, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x122, 0xf, 0xf, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x121, 0xf, 0xf, false)));
+  return v;
+}
+
+// --------------------------------------------------------------------------
+// number formats
+// --------------------------------------------------------------------------
+__device__ inline float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+// two floats -> packed bf16 pair (round to nearest even; the hardware convert)
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// OCP E4M3 ("fn") encoder from the format definition: round to nearest, ties to
+// even; magnitudes >= 448 saturate to 448; the sign is kept (also for zero).
+// Expects a finite input.
+__device__ inline uint32_t e4m3_from_f32(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  uint32_t code;
+  if (a >= 0x43e00000u) {                 // |v| >= 448
+    code = 0x7e;
+  } else if (a < 0x3c800000u) {           // |v| < 2^-6: subnormal step 2^-9
+    code = (uint32_t)__builtin_rintf(__builtin_bit_cast(float, a) * 512.0f);   // 0..8, exact scaling
+  } else {                                // normal: keep 3 of 23 mantissa bits
+    uint32_t r = a >> 20;                 // exponent and top 3 mantissa bits
+    const uint32_t rem = a & 0xfffffu;
+    if (rem > 0x80000u || (rem == 0x80000u && (r & 1u))) r += 1;
+    code = r - ((127u - 7u) << 3);        // rebias exponent 127 -> 7
+  }
+  return sign | code;
+}
+
+// four e4m3 codes packed little-endian
+__device__ inline uint32_t pack_e4m3x4(float a, float b, float c, float d) {
+  return e4m3_from_f32(a) | (e4m3_from_f32(b) << 8) | (e4m3_from_f32(c) << 16) | (e4m3_from_f32(d) << 24);
+}
+
+// --------------------------------------------------------------------------
+// buffer resources: hardware range checks (out-of-range loads read 0, stores drop)
+// --------------------------------------------------------------------------
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ inline u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ inline void buf_store16(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+__device__ inline void buf_store8(u32x2 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+}
+
+}  // namespace moe

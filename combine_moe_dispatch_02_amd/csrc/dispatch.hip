@@ -1,0 +1,156 @@
+// A2 -- dispatch: copy every local (token, k) pair's activation row into its
+// pool row and raise the per-tile ready flags.
+//
+// StreamEP README, "How it works": received pairs land directly in the
+// expert-major, tile-padded pool (pool-layout dispatch), and dispatch signals
+// each pool tile as it fills (per-tile streaming).
+//
+// One wave per token: the token's row is read once (16-byte lanes) and stored
+// to each of its local pairs' rows, so x is read T*H*2 bytes once and the pool
+// written once per pair. In fp8 mode each 1x128 group (16 lanes x 8 values) is
+// quantised on the way: scale = amax/448 in fp32 (1 for an all-zero group),
+// code = e4m3(x / scale) with IEEE division, round to nearest even, saturating.
+// After its stores a wave releases them (device scope) and bumps each touched
+// tile's fill counter; the wave that completes a tile's real rows stores the
+// epoch into tile_ready with release ordering.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+struct DispatchArgs {
+  const uint16_t* x;
+  int32_t T, K, H;
+  int32_t tile, tile_shift;
+  const int32_t* pos;
+  const int32_t* tile_expert;
+  const int32_t* offsets;
+  const int32_t* counts;
+  uint8_t* pool;
+  float* pool_s;
+  int32_t pool_rows;
+  uint32_t* tile_fill;
+  uint32_t* tile_ready;
+  uint32_t epoch;
+  uint32_t* err;
+};
+
+template <int CPL, bool FP8>
+__global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs a) {
+  const int lane = lane_id();
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  int p = lane < a.K ? a.pos[(int64_t)t * a.K + lane] : -1;
+  if (p >= a.pool_rows) {
+    record_error(a.err, MOE_ERR_INVALID);
+    p = -1;
+  }
+  const uint64_t dest = ballot(p >= 0);
+  if (dest == 0) return;
+
+  const int H = a.H;
+  const int nch = H >> 3;  // 16-byte chunks of 8 bf16 in a row
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x + (int64_t)t * H, (uint32_t)H * 2u);
+  const int64_t out_row_bytes = FP8 ? H : (int64_t)H * 2;
+
+  for (int c0 = 0; c0 < nch; c0 += kWave * CPL) {
+    u32x4 v[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) v[i] = buf_load16(xr, (uint32_t)(c0 + i * kWave + lane) * 16u);
+    if constexpr (!FP8) {
+      for (int k = 0; k < a.K; ++k) {
+        if (!((dest >> k) & 1ull)) continue;
+        const int pk = readlane(p, k);
+        const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.pool + (int64_t)pk * out_row_bytes, (uint32_t)out_row_bytes);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) buf_store16(v[i], pr, (uint32_t)(c0 + i * kWave + lane) * 16u);
+      }
+    } else {
+      u32x2 q[CPL];
+      float s[CPL];
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        float f[8];
+        f[0] = bf16_lo(v[i].x); f[1] = bf16_hi(v[i].x);
+        f[2] = bf16_lo(v[i].y); f[3] = bf16_hi(v[i].y);
+        f[4] = bf16_lo(v[i].z); f[5] = bf16_hi(v[i].z);
+        f[6] = bf16_lo(v[i].w); f[7] = bf16_hi(v[i].w);
+        float m = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(f[j]));
+        m = row16_max(m);                      // the 16 lanes of a DPP row hold one group
+        const float sc = m > 0.f ? m / 448.0f : 1.0f;
+        s[i] = sc;
+        q[i].x = pack_e4m3x4(f[0] / sc, f[1] / sc, f[2] / sc, f[3] / sc);
+        q[i].y = pack_e4m3x4(f[4] / sc, f[5] / sc, f[6] / sc, f[7] / sc);
+      }
+      const int groups = H >> 7;
+      for (int k = 0; k < a.K; ++k) {
+        if (!((dest >> k) & 1ull)) continue;
+        const int pk = readlane(p, k);
+        const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.pool + (int64_t)pk * out_row_bytes, (uint32_t)out_row_bytes);
+        float* srow = a.pool_s + (int64_t)pk * groups;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+          const int c = c0 + i * kWave + lane;
+          buf_store8(q[i], pr, (uint32_t)c * 8u);
+          if ((lane & 15) == 0 && c < nch) srow[c >> 4] = s[i];
+        }
+      }
+    }
+  }
+
+  // publish: this wave's stores, then one fill count per stored row
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  if (p >= 0) {
+    const int ti = p >> a.tile_shift;
+    const uint32_t old = __hip_atomic_fetch_add(&a.tile_fill[ti], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const int e = a.tile_expert[ti];
+    const int real = min(a.tile, a.offsets[e] + a.counts[e] - (ti << a.tile_shift));
+    if ((int)old + 1 == real)
+      __hip_atomic_store(&a.tile_ready[ti], a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+template <bool FP8>
+static void launch_cpl(int cpl, dim3 grid, hipStream_t s, const DispatchArgs& a) {
+  switch (cpl) {
+    case 1: hipLaunchKernelGGL((dispatch_kernel<1, FP8>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((dispatch_kernel<2, FP8>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((dispatch_kernel<4, FP8>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((dispatch_kernel<8, FP8>), grid, dim3(256), 0, s, a); break;
+  }
+}
+
+int launch_dispatch(const void* x, int32_t H, int32_t dtype, const moe_plan_t& p, int32_t pool_rows,
+                    void* pool, float* pool_s, uint32_t epoch, const WsLayout& L, char* ws,
+                    hipStream_t stream) {
+  DispatchArgs a;
+  a.x = static_cast<const uint16_t*>(x);
+  a.T = p.T;
+  a.K = p.K;
+  a.H = H;
+  a.tile = p.tile;
+  a.tile_shift = __builtin_ctz((unsigned)p.tile);
+  a.pos = p.pos;
+  a.tile_expert = p.tile_expert;
+  a.offsets = p.offsets;
+  a.counts = p.counts;
+  a.pool = static_cast<uint8_t*>(pool);
+  a.pool_s = pool_s;
+  a.pool_rows = pool_rows;
+  a.tile_fill = reinterpret_cast<uint32_t*>(ws + L.fill);
+  a.tile_ready = p.tile_ready;
+  a.epoch = epoch;
+  a.err = reinterpret_cast<uint32_t*>(ws + L.err);
+  const int nch = H / 8;
+  const int cpl = nch <= 64 ? 1 : nch <= 128 ? 2 : nch <= 256 ? 4 : 8;
+  const dim3 grid((p.T + 3) / 4);
+  if (dtype == MOE_FP8_E4M3_G128)
+    launch_cpl<true>(cpl, grid, stream, a);
+  else
+    launch_cpl<false>(cpl, grid, stream, a);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+}  // namespace moe

@@ -1,0 +1,44 @@
+// Host-side launchers of libmoe355's kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+
+namespace moe {
+
+int launch_plan(const int32_t* topk_idx, const moe_plan_t& p, const WsLayout& L, char* ws,
+                hipStream_t stream);
+
+int launch_dispatch(const void* x, int32_t H, int32_t dtype, const moe_plan_t& p, int32_t pool_rows,
+                    void* pool, float* pool_s, uint32_t epoch, const WsLayout& L, char* ws,
+                    hipStream_t stream);
+
+struct FfnLaunch {
+  const moe_plan_t* plan;
+  int32_t pool_rows;
+  const void* pool;
+  const float* pool_s;
+  const void* w1;
+  const float* w1_s;
+  const void* w2;
+  const float* w2_s;
+  int32_t H, I, dtype;
+  uint32_t epoch;
+  void* y_pool;
+  int32_t block_n;
+  int32_t workgroups;
+  uint64_t timeout_ticks;   // s_memrealtime ticks (100 MHz)
+};
+
+int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream_t stream);
+
+int launch_combine(const void* y_pool, int32_t pool_rows, const float* topk_weights, const moe_plan_t& p,
+                   int32_t H, void* out, hipStream_t stream);
+
+// what the FFN supports (host-side check shared by validation and launch)
+int ffn_supported(int32_t H, int32_t I, int32_t dtype, int32_t tile, int32_t block_n);
+
+int device_cu_count();
+
+}  // namespace moe

@@ -1,0 +1,274 @@
+"""Python binding of libmoe355: the MoE dispatch -> expert FFN -> combine path.
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+torch supplies device memory and streams. The entry points keep the C ABI's
+names (include/moe355.h); ``StreamMoE`` / ``stream_moe`` string them together
+the way the StreamEP README's usage sample calls ``stream_moe_func``
+(x, topk_idx, topk_weights, w1_local, w2_local, streams).
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import torch
+
+from . import _abi
+from ._abi import MOE_BF16, MOE_FP8_E4M3_G128, MoeError, PlanT, TileConfig, check, load
+
+__all__ = [
+    "MOE_BF16", "MOE_FP8_E4M3_G128", "MoeError", "Plan", "Workspace", "TileConfig",
+    "pool_rows_upper_bound", "workspace_bytes", "moe_plan", "moe_query_pool_rows",
+    "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_get_error", "device_cu_count",
+    "make_streams", "StreamMoE", "stream_moe",
+]
+
+
+def _vp(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(s) -> ctypes.c_void_p:
+    if s is None:
+        s = torch.cuda.current_stream()
+    if isinstance(s, torch.cuda.Stream):
+        return ctypes.c_void_p(s.cuda_stream)
+    return ctypes.c_void_p(int(s))
+
+
+def _dtype_code(dtype) -> int:
+    if dtype in ("bf16", MOE_BF16):
+        return MOE_BF16
+    if dtype in ("fp8", MOE_FP8_E4M3_G128):
+        return MOE_FP8_E4M3_G128
+    raise ValueError(f"dtype {dtype!r}")
+
+
+def _need_cuda(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def pool_rows_upper_bound(T: int, K: int, E_local: int, tile: int) -> int:
+    return int(load().moe_pool_rows_upper_bound(T, K, E_local, tile))
+
+
+def workspace_bytes(T: int, K: int, E_local: int, tile: int, pool_rows: int = 0, I: int = 0,
+                    dtype="bf16") -> int:
+    return int(load().moe_workspace_bytes(T, K, E_local, tile, pool_rows, I, _dtype_code(dtype)))
+
+
+def device_cu_count() -> int:
+    return int(load().moe_device_cu_count())
+
+
+@dataclass
+class Plan:
+    """Caller-owned plan arrays (moe_plan_t) on one device."""
+
+    T: int
+    K: int
+    expert_begin: int
+    E_local: int
+    tile: int
+    rows_cap: int
+    counts: torch.Tensor
+    offsets: torch.Tensor
+    pos: torch.Tensor
+    src: torch.Tensor
+    tile_expert: torch.Tensor
+    num_tiles: torch.Tensor
+    tile_ready: torch.Tensor
+
+    @classmethod
+    def allocate(cls, T, K, expert_begin, E_local, tile, device="cuda") -> "Plan":
+        cap = pool_rows_upper_bound(T, K, E_local, tile)
+        if cap == 0:
+            raise MoeError("moe_pool_rows_upper_bound", _abi.MOE_ERR_INVALID)
+        i32 = dict(dtype=torch.int32, device=device)
+        return cls(T, K, expert_begin, E_local, tile, cap,
+                   torch.empty(E_local, **i32), torch.empty(E_local + 1, **i32),
+                   torch.empty(T * K, **i32), torch.empty(cap, **i32),
+                   torch.empty(cap // tile, **i32), torch.empty(1, **i32),
+                   torch.zeros(cap // tile, dtype=torch.int32, device=device))
+
+    def c(self) -> PlanT:
+        return PlanT(self.T, self.K, self.expert_begin, self.E_local, self.tile, self.rows_cap,
+                     self.counts.data_ptr(), self.offsets.data_ptr(), self.pos.data_ptr(),
+                     self.src.data_ptr(), self.tile_expert.data_ptr(), self.num_tiles.data_ptr(),
+                     self.tile_ready.data_ptr())
+
+
+class Workspace:
+    """Zero-initialised device workspace shared by plan, dispatch, FFN and error queries."""
+
+    def __init__(self, T, K, E_local, tile, pool_rows=0, I=0, dtype="bf16", device="cuda"):
+        n = workspace_bytes(T, K, E_local, tile, pool_rows, I, dtype)
+        if n == 0:
+            raise MoeError("moe_workspace_bytes", _abi.MOE_ERR_INVALID)
+        self.buf = torch.zeros(n, dtype=torch.uint8, device=device)
+
+    @property
+    def nbytes(self) -> int:
+        return self.buf.numel()
+
+
+def moe_plan(topk_idx: torch.Tensor, plan: Plan, ws: Workspace, stream=None) -> None:
+    _need_cuda(topk_idx, "topk_idx", torch.int32)
+    if topk_idx.shape != (plan.T, plan.K):
+        raise ValueError(f"topk_idx shape {tuple(topk_idx.shape)} != {(plan.T, plan.K)}")
+    c = plan.c()
+    check("moe_plan", load().moe_plan(_vp(topk_idx), ctypes.byref(c), _vp(ws.buf), ws.nbytes,
+                                      _stream(stream)))
+
+
+def moe_query_pool_rows(plan: Plan, stream=None) -> int:
+    out = ctypes.c_int32(0)
+    c = plan.c()
+    check("moe_query_pool_rows", load().moe_query_pool_rows(ctypes.byref(c), ctypes.byref(out),
+                                                            _stream(stream)))
+    return int(out.value)
+
+
+def moe_dispatch(x: torch.Tensor, plan: Plan, pool: torch.Tensor, pool_s: Optional[torch.Tensor],
+                 epoch: int, ws: Workspace, dtype="bf16", stream=None) -> None:
+    _need_cuda(x, "x", torch.bfloat16)
+    _need_cuda(pool, "pool")
+    if x.shape[0] != plan.T:
+        raise ValueError("x rows != T")
+    code = _dtype_code(dtype)
+    H = x.shape[1]
+    rows = pool.shape[0]
+    c = plan.c()
+    check("moe_dispatch", load().moe_dispatch(_vp(x), H, code, ctypes.byref(c), rows, _vp(pool),
+                                              _vp(pool_s), epoch, _vp(ws.buf), ws.nbytes,
+                                              _stream(stream)))
+
+
+def moe_expert_ffn(plan: Plan, pool: torch.Tensor, pool_s: Optional[torch.Tensor],
+                   w1: torch.Tensor, w1_s: Optional[torch.Tensor], w2: torch.Tensor,
+                   w2_s: Optional[torch.Tensor], epoch: int, ws: Workspace, y_pool: torch.Tensor,
+                   dtype="bf16", cfg: Optional[TileConfig] = None, stream=None) -> None:
+    for t, n in ((pool, "pool"), (w1, "w1"), (w2, "w2"), (y_pool, "y_pool")):
+        _need_cuda(t, n)
+    E, twoI, H = w1.shape
+    if E != plan.E_local or w2.shape != (E, H, twoI // 2):
+        raise ValueError("w1 [E_local, 2I, H] / w2 [E_local, H, I] shapes do not match")
+    if y_pool.shape[0] != pool.shape[0] or y_pool.shape[1] != H:
+        raise ValueError("y_pool must be [pool rows, H]")
+    c = plan.c()
+    cfgp = ctypes.byref(cfg) if cfg is not None else None
+    check("moe_expert_ffn", load().moe_expert_ffn(
+        ctypes.byref(c), pool.shape[0], _vp(pool), _vp(pool_s), _vp(w1), _vp(w1_s), _vp(w2),
+        _vp(w2_s), H, twoI // 2, _dtype_code(dtype), epoch, _vp(ws.buf), ws.nbytes, _vp(y_pool),
+        cfgp, _stream(stream)))
+
+
+def moe_combine(y_pool: torch.Tensor, topk_weights: torch.Tensor, plan: Plan, out: torch.Tensor,
+                stream=None) -> None:
+    _need_cuda(y_pool, "y_pool")
+    _need_cuda(topk_weights, "topk_weights", torch.float32)
+    _need_cuda(out, "out", torch.bfloat16)
+    if topk_weights.shape != (plan.T, plan.K) or out.shape[0] != plan.T:
+        raise ValueError("topk_weights [T, K] / out [T, H] shapes do not match the plan")
+    c = plan.c()
+    check("moe_combine", load().moe_combine(_vp(y_pool), y_pool.shape[0], _vp(topk_weights),
+                                            ctypes.byref(c), out.shape[1], _vp(out), _stream(stream)))
+
+
+def moe_get_error(ws: Workspace, stream=None) -> int:
+    return int(load().moe_get_error(_vp(ws.buf), ws.nbytes, _stream(stream)))
+
+
+def make_streams(device=None) -> Tuple[torch.cuda.Stream, torch.cuda.Stream]:
+    """(compute, comm) streams at the default priority."""
+    return torch.cuda.Stream(device=device), torch.cuda.Stream(device=device)
+
+
+class StreamMoE:
+    """Buffers of one layer shape, and the four calls in order.
+
+    The pool, h and y_pool are sized by the sync-free bound
+    (``pool_rows_upper_bound``) unless ``pool_rows`` is given.
+    """
+
+    def __init__(self, T, H, I, K, num_local_experts, *, expert_begin=0, tile=128, dtype="bf16",
+                 device="cuda", pool_rows: Optional[int] = None, cfg: Optional[TileConfig] = None):
+        self.T, self.H, self.I, self.K = T, H, I, K
+        self.E_local, self.expert_begin, self.tile = num_local_experts, expert_begin, tile
+        self.dtype = "fp8" if _dtype_code(dtype) == MOE_FP8_E4M3_G128 else "bf16"
+        self.cfg = cfg
+        self.plan = Plan.allocate(T, K, expert_begin, num_local_experts, tile, device)
+        rows = pool_rows or self.plan.rows_cap
+        self.pool_rows = rows
+        self.ws = Workspace(T, K, num_local_experts, tile, rows, I, self.dtype, device)
+        fp8 = self.dtype == "fp8"
+        self.pool = torch.empty(rows, H, dtype=torch.uint8 if fp8 else torch.bfloat16, device=device)
+        self.pool_s = torch.empty(rows, H // 128, dtype=torch.float32, device=device) if fp8 else None
+        self.y_pool = torch.empty(rows, H, dtype=torch.bfloat16, device=device)
+        self.out = torch.empty(T, H, dtype=torch.bfloat16, device=device)
+        self.epoch = 0
+
+    def next_epoch(self) -> int:
+        self.epoch = (self.epoch % 0xFFFFFFFF) + 1      # 1 .. 2^32-1; 0 is never a valid epoch
+        return self.epoch
+
+    def forward(self, x, topk_idx, topk_weights, w1, w2, w1_scale=None, w2_scale=None,
+                streams=None) -> torch.Tensor:
+        """One layer. ``streams=(compute, comm)`` runs plan/dispatch/combine on comm and the FFN
+        on compute, ordered by events; None runs everything on the current stream."""
+        if topk_idx.dtype != torch.int32:
+            topk_idx = topk_idx.to(torch.int32)
+        epoch = self.next_epoch()
+        if streams is None:
+            s = torch.cuda.current_stream()
+            moe_plan(topk_idx, self.plan, self.ws, s)
+            moe_dispatch(x, self.plan, self.pool, self.pool_s, epoch, self.ws, self.dtype, s)
+            moe_expert_ffn(self.plan, self.pool, self.pool_s, w1, w1_scale, w2, w2_scale, epoch,
+                           self.ws, self.y_pool, self.dtype, self.cfg, s)
+            moe_combine(self.y_pool, topk_weights, self.plan, self.out, s)
+            return self.out
+        compute, comm = streams
+        cur = torch.cuda.current_stream()
+        comm.wait_stream(cur)
+        moe_plan(topk_idx, self.plan, self.ws, comm)
+        planned = torch.cuda.Event()
+        planned.record(comm)
+        moe_dispatch(x, self.plan, self.pool, self.pool_s, epoch, self.ws, self.dtype, comm)
+        compute.wait_event(planned)
+        moe_expert_ffn(self.plan, self.pool, self.pool_s, w1, w1_scale, w2, w2_scale, epoch,
+                       self.ws, self.y_pool, self.dtype, self.cfg, compute)
+        done = torch.cuda.Event()
+        done.record(compute)
+        comm.wait_event(done)
+        moe_combine(self.y_pool, topk_weights, self.plan, self.out, comm)
+        cur.wait_stream(comm)
+        return self.out
+
+    __call__ = forward
+
+
+_LAYERS = {}
+
+
+def stream_moe(x, topk_idx, topk_weights, w1_local, w2_local, *, expert_begin=0, tile=128,
+               w1_scale=None, w2_scale=None, streams=None) -> torch.Tensor:
+    """Functional form: shapes come from the tensors (w1_local [E_local, 2I, H]). Returns a
+    fresh output tensor; buffers are cached per shape and device."""
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    E, twoI, _ = w1_local.shape
+    fp8 = w1_local.dtype == torch.float8_e4m3fn
+    key = (T, H, twoI // 2, K, E, expert_begin, tile, fp8, x.device)
+    layer = _LAYERS.get(key)
+    if layer is None:
+        layer = StreamMoE(T, H, twoI // 2, K, E, expert_begin=expert_begin, tile=tile,
+                          dtype="fp8" if fp8 else "bf16", device=x.device)
+        _LAYERS[key] = layer
+    out = layer.forward(x, topk_idx, topk_weights, w1_local, w2_local, w1_scale, w2_scale, streams)
+    return out.clone()

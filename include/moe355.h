@@ -1,0 +1,201 @@
+/*
+ * moe355.h -- C ABI of the single-GPU MoE dispatch -> expert FFN -> combine path
+ * on MI355X (gfx950).
+ *
+ * The layer is the streaming MoE layer of the StreamEP README ("How it works"):
+ *   - pool-layout dispatch: each routed (token, k) pair lands in an expert-major,
+ *     tile-padded pool, so dispatch's output is the grouped GEMM's input with no
+ *     separate permute;
+ *   - per-tile streaming: dispatch signals each pool tile as it fills and the
+ *     expert GEMMs claim ready tiles;
+ *   - caller-owned streams: the layer runs on a compute stream and a
+ *     communicate stream that the caller supplies; the only host sync is an
+ *     optional poll that sizes the pool;
+ *   - the forward grouped GEMMs "A" (w1, gate|up, then SwiGLU) and "Y" (w2);
+ *   - combine: each token's expert outputs are reduced with its topk_weights.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named as device pointers are caller-owned device memory of the
+ *     current HIP device. The library never allocates or frees memory and never
+ *     synchronises, except moe_query_pool_rows and moe_get_error, which say so.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work is
+ *     enqueued asynchronously on it; the call returns before the GPU runs it.
+ *   - Argument errors are returned synchronously, before anything is enqueued:
+ *     MOE_ERR_INVALID (bad pointer, size or value), MOE_ERR_UNSUPPORTED (valid
+ *     but not built: a shape or dtype outside the kernels' constraints).
+ *     A failed launch returns MOE_ERR_HIP. Errors detected on the device (a
+ *     ready-flag wait that timed out, a pool row past the allocation) are
+ *     recorded in the workspace and returned by moe_get_error.
+ *   - Layouts are row-major and dense: x[T][H], topk_idx[T][K], pool[rows][H],
+ *     w1[E_local][2I][H] (rows 0..I-1 gate, I..2I-1 up), w2[E_local][H][I],
+ *     y_pool[rows][H], out[T][H].
+ *   - Types: bf16 is IEEE binary32's upper half; fp8 is OCP E4M3 ("fn": bias 7,
+ *     max 448, no infinities). fp8 scales are fp32: activations one per 1x128
+ *     group of the contraction dim ([rows][H/128] for the pool), weights one per
+ *     128x128 block (w1_s[E_local][2I/128][H/128], w2_s[E_local][H/128][I/128]).
+ */
+#ifndef MOE355_H
+#define MOE355_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE355_API __attribute__((visibility("default")))
+
+/* Status codes. */
+enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID = 1,     /* bad argument, or a device-side bound check failed */
+  MOE_ERR_UNSUPPORTED = 2, /* valid request outside what the kernels implement */
+  MOE_ERR_HIP = 3,         /* a HIP runtime call or kernel launch failed */
+  MOE_ERR_TIMEOUT = 4      /* a ready-flag wait on the device ran out of time */
+};
+
+/* Storage types of activations and weights. */
+enum {
+  MOE_BF16 = 0,          /* bf16 activations and weights */
+  MOE_FP8_E4M3_G128 = 1  /* e4m3 activations per 1x128 group, e4m3 weights per 128x128 block */
+};
+
+/*
+ * Placement plan: an expert-major, tile-padded pool (StreamEP README, "How it
+ * works", pool-layout dispatch). Shape fields are set by the caller; the arrays
+ * are caller-allocated device memory written by moe_plan.
+ *   counts[e]      pairs routed to local expert e                       [E_local]
+ *   offsets[e]     first pool row of expert e; offsets[E_local] = P      [E_local+1]
+ *   pos[q]         pool row of pair q = t*K+k, -1 if not local           [T*K]
+ *   src[p]         pair id of pool row p; -1 for padding and rows >= P   [rows_cap]
+ *   tile_expert[i] local expert of pool tile i; -1 for i >= num_tiles    [rows_cap/tile]
+ *   num_tiles[0]   P / tile                                              [1]
+ *   tile_ready[i]  epoch of the dispatch call that filled tile i         [rows_cap/tile]
+ * A segment holds its expert's pairs in ascending q and is padded to whole
+ * tiles; an expert with no pairs gets no rows. Ids outside
+ * [expert_begin, expert_begin+E_local), including -1, are not local.
+ */
+typedef struct moe_plan_t {
+  int32_t T, K, expert_begin, E_local, tile;
+  int32_t rows_cap; /* length of src; must be >= moe_pool_rows_upper_bound(T,K,E_local,tile) */
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* pos;
+  int32_t* src;
+  int32_t* tile_expert;
+  int32_t* num_tiles;
+  uint32_t* tile_ready;
+} moe_plan_t;
+
+/*
+ * GEMM tiling and launch overrides ("TileConfig" of the README's usage note:
+ * tiles and CU counts come from the weight shapes; the struct overrides them).
+ * Pass NULL, or zero fields, for the built-in choice.
+ */
+typedef struct moe_tile_config {
+  int32_t block_n;          /* N columns per work unit: 128 or 256 (0 = auto) */
+  int32_t gemm_workgroups;  /* persistent GEMM grid size (0 = one per CU) */
+  uint32_t spin_timeout_us; /* bound on one ready-flag wait (0 = 2 000 000 us) */
+  int32_t reserved;
+} moe_tile_config;
+
+/* Host-only size helpers (no device access). */
+
+/* Pool rows any plan of this shape can need: the padded segments satisfy
+ * ceil(c/tile)*tile <= c + tile - 1, so P <= T*K + E_local*(tile-1); the result
+ * is that bound rounded down to whole tiles. Returns 0 for invalid sizes. */
+MOE355_API size_t moe_pool_rows_upper_bound(int32_t T, int32_t K, int32_t E_local, int32_t tile);
+
+/* Bytes of the device workspace that moe_plan, moe_dispatch, moe_expert_ffn and
+ * moe_get_error share for one layer: plan scratch, per-tile fill counters, the
+ * device error word, and the intermediate h (pool_rows x I, bf16 or e4m3 + fp32
+ * group scales). pool_rows = 0 means moe_pool_rows_upper_bound. Returns 0 for
+ * invalid sizes. The workspace must be zero-filled once before its first use. */
+MOE355_API size_t moe_workspace_bytes(int32_t T, int32_t K, int32_t E_local, int32_t tile,
+                                      int32_t pool_rows, int32_t I, int32_t dtype);
+
+/*
+ * A1. Build the placement plan from topk_idx (device, int32 [T][K]): histogram
+ * of local pairs, padded exclusive scan into offsets, and a stable rank of each
+ * pair inside its expert (the plan's layout is described at moe_plan_t). Also
+ * clears tile_ready and the workspace's fill counters for the dispatch that
+ * follows. Deterministic: no result depends on scheduling.
+ * Errors: MOE_ERR_INVALID for null pointers, T < 1, K not in [1,16],
+ * E_local not in [1,1024], tile not in {16,32,64,128}, rows_cap too small,
+ * expert_begin < 0, or a workspace smaller than moe_workspace_bytes(...,0,0,0).
+ */
+MOE355_API int moe_plan(const int32_t* topk_idx, const moe_plan_t* plan, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/* The one host sync of the layer (README, "Caller-owned streams"): waits for
+ * `stream`, then copies offsets[E_local] (= P, the pool rows in use) to *host_P. */
+MOE355_API int moe_query_pool_rows(const moe_plan_t* plan, int32_t* host_P, void* stream);
+
+/*
+ * A2. Dispatch: pool[pos[t,k]] = x[t] for every local pair (device x bf16 [T][H]).
+ * bf16: pool is bf16 [pool_rows][H] and pool_s must be NULL.
+ * fp8:  pool is e4m3 [pool_rows][H] and pool_s fp32 [pool_rows][H/128]; each
+ *       1x128 group g of x[t] is stored as codes e4m3(x/s) with s = amax/448
+ *       (s = 1 for an all-zero group), rounded to nearest even and saturated.
+ * Padding rows are not written. After a tile's real rows are stored the tile's
+ * tile_ready entry is set to `epoch` with release ordering (device scope).
+ * epoch must be nonzero and should change from one layer call to the next.
+ * A pair whose row is >= pool_rows is not written and records MOE_ERR_INVALID.
+ * Errors: MOE_ERR_INVALID (null pointers, H < 8, epoch 0, bad dtype),
+ * MOE_ERR_UNSUPPORTED (H % 8 != 0; fp8 with H % 128 != 0).
+ */
+MOE355_API int moe_dispatch(const void* x, int32_t H, int32_t act_dtype, const moe_plan_t* plan,
+                            int32_t pool_rows, void* pool, float* pool_s, uint32_t epoch,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * A3 + A4. Expert FFN over the pool, as a persistent grouped GEMM on MFMA:
+ *   GEMM A: g = pool_tile . w1[e]^T (fp32 accumulate), h = silu(g_gate) * g_up,
+ *           silu(z) = z / (1 + exp(-z)); h is stored as bf16 (bf16 mode) or as
+ *           e4m3 + one fp32 scale per 1x128 group (fp8 mode) in the workspace;
+ *   GEMM Y: y_pool_tile = h . w2[e]^T (fp32 accumulate), stored bf16.
+ * fp8 mode applies activation and weight scales per 128-wide K block in fp32.
+ * Each work unit waits until tile_ready of its tile equals `epoch` (acquire);
+ * a wait longer than the timeout records MOE_ERR_TIMEOUT and skips the unit.
+ * Rows of y_pool that are padding are computed from whatever the pool holds and
+ * are never read by moe_combine. Only the first pool_rows/tile tiles are
+ * computed; a plan that needs more records MOE_ERR_INVALID.
+ * Errors: MOE_ERR_INVALID (null pointers, bad dtype, epoch 0, small workspace,
+ * pool_rows not a multiple of tile), MOE_ERR_UNSUPPORTED (bf16: H % 128 or
+ * I % 64 nonzero; fp8: H % 128 or I % 128 nonzero, or tile < 64).
+ */
+MOE355_API int moe_expert_ffn(const moe_plan_t* plan, int32_t pool_rows, const void* pool,
+                              const float* pool_s, const void* w1, const float* w1_s, const void* w2,
+                              const float* w2_s, int32_t H, int32_t I, int32_t dtype, uint32_t epoch,
+                              void* ws, size_t ws_bytes, void* y_pool, const moe_tile_config* cfg,
+                              void* stream);
+
+/*
+ * A5. Combine: out[t] = sum over k with pos[t,k] >= 0, in ascending k, of
+ * topk_weights[t,k] * y_pool[pos[t,k]], accumulated in fp32 and stored bf16
+ * (round to nearest even). Every row of out (bf16 [T][H]) is written; a token
+ * with no local pair gets zeros. Weights are not renormalised.
+ * y_pool: device bf16 [pool_rows][H]; a pair whose row is >= pool_rows is
+ * skipped (dispatch has already reported it). topk_weights: device fp32 [T][K].
+ * The caller orders this after moe_expert_ffn (same stream, or an event).
+ * Errors: MOE_ERR_INVALID (null pointers), MOE_ERR_UNSUPPORTED (H % 8 != 0).
+ */
+MOE355_API int moe_combine(const void* y_pool, int32_t pool_rows, const float* topk_weights,
+                           const moe_plan_t* plan, int32_t H, void* out, void* stream);
+
+/* Waits for `stream`, returns the first error recorded on the device in the
+ * workspace since the last call (MOE_OK if none) and clears it. */
+MOE355_API int moe_get_error(void* ws, size_t ws_bytes, void* stream);
+
+/* Static text for a status code. */
+MOE355_API const char* moe_status_string(int status);
+
+/* Number of compute units of the current device (0 if none is visible). */
+MOE355_API int moe_device_cu_count(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE355_H */

@@ -1,0 +1,155 @@
+"""The C-ABI library loads, exports every symbol its header declares, and rejects bad
+arguments synchronously -- all without a GPU (no call here reaches a launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+from combine_moe_dispatch_02_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe355.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return re.findall(r"MOE355_API\s+[\w\s\*]+?\b(moe_\w+)\s*\(", text)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_abi.LIB_PATH):
+        pytest.fail("libmoe355.so is not built (run __graft_entry__.build())")
+    return _abi.load()
+
+
+def test_header_declares_the_four_calls():
+    names = set(declared_symbols())
+    assert {"moe_plan", "moe_dispatch", "moe_expert_ffn", "moe_combine"} <= names
+    assert len(names) == 10
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    assert {n for n, _, _ in _abi.SIGNATURES} == set(declared_symbols())
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert lib.moe_status_string(code)
+    assert lib.moe_status_string(99) == b"unknown status"
+
+
+@pytest.mark.parametrize("T,K,E,tile", [(64, 2, 8, 16), (128, 8, 128, 64), (8192, 8, 32, 128),
+                                        (16384, 8, 128, 128), (1, 1, 1, 16), (3, 5, 7, 32)])
+def test_pool_bound_matches_oracle(lib, T, K, E, tile):
+    assert lib.moe_pool_rows_upper_bound(T, K, E, tile) == oracle.pool_rows_bound(T, K, E, tile)
+
+
+def test_pool_bound_rejects_bad_sizes(lib):
+    assert lib.moe_pool_rows_upper_bound(0, 2, 8, 16) == 0
+    assert lib.moe_pool_rows_upper_bound(4, 17, 8, 16) == 0
+    assert lib.moe_pool_rows_upper_bound(4, 2, 8, 24) == 0
+    assert lib.moe_pool_rows_upper_bound(4, 2, 0, 16) == 0
+
+
+def test_workspace_bytes(lib):
+    plan_only = lib.moe_workspace_bytes(16384, 8, 128, 128, 0, 0, 0)
+    full_bf16 = lib.moe_workspace_bytes(16384, 8, 128, 128, 0, 1536, 0)
+    full_fp8 = lib.moe_workspace_bytes(16384, 8, 128, 128, 0, 1536, 1)
+    rows = oracle.pool_rows_bound(16384, 8, 128, 128)
+    assert plan_only > 0
+    assert full_bf16 - plan_only >= rows * 1536 * 2
+    assert full_fp8 - plan_only >= rows * 1536 + rows * 12 * 4
+    assert lib.moe_workspace_bytes(16, 2, 4, 16, 0, 100, 1) == 0     # fp8 needs I % 128 == 0
+    assert lib.moe_workspace_bytes(16, 2, 4, 16, 0, 64, 7) == 0      # unknown dtype
+
+
+def _fake_plan(**kw):
+    # addresses are never dereferenced: every case below fails validation first
+    f = dict(T=64, K=2, expert_begin=0, E_local=8, tile=16,
+             rows_cap=oracle.pool_rows_bound(64, 2, 8, 16))
+    f.update(kw)
+    p = _abi.PlanT(f["T"], f["K"], f["expert_begin"], f["E_local"], f["tile"], f["rows_cap"],
+                   0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, 0x7000)
+    return p
+
+
+BAD_PLANS = [dict(T=0), dict(K=0), dict(K=17), dict(E_local=0), dict(E_local=1025), dict(tile=48),
+             dict(expert_begin=-1), dict(rows_cap=16)]
+
+
+@pytest.mark.parametrize("bad", BAD_PLANS)
+def test_plan_validation(lib, bad):
+    p = _fake_plan(**bad)
+    assert lib.moe_plan(ctypes.c_void_p(0x8000), ctypes.byref(p), ctypes.c_void_p(0x9000), 1 << 20,
+                        None) == _abi.MOE_ERR_INVALID
+
+
+def test_plan_null_pointers(lib):
+    p = _fake_plan()
+    assert lib.moe_plan(None, ctypes.byref(p), ctypes.c_void_p(0x9000), 1 << 20, None) == 1
+    assert lib.moe_plan(ctypes.c_void_p(0x8000), None, ctypes.c_void_p(0x9000), 1 << 20, None) == 1
+    p.src = None
+    assert lib.moe_plan(ctypes.c_void_p(0x8000), ctypes.byref(p), ctypes.c_void_p(0x9000), 1 << 20,
+                        None) == 1
+
+
+def test_plan_small_workspace(lib):
+    p = _fake_plan()
+    assert lib.moe_plan(ctypes.c_void_p(0x8000), ctypes.byref(p), ctypes.c_void_p(0x9000), 64,
+                        None) == _abi.MOE_ERR_INVALID
+
+
+def test_dispatch_validation(lib):
+    p = _fake_plan()
+    X, POOL, WS = (ctypes.c_void_p(a) for a in (0x10000, 0x20000, 0x30000))
+    big = 1 << 30
+    # epoch 0 is reserved
+    assert lib.moe_dispatch(X, 128, 0, ctypes.byref(p), 248, POOL, None, 0, WS, big, None) == 1
+    # bf16 takes no scale buffer; fp8 needs one
+    assert lib.moe_dispatch(X, 128, 0, ctypes.byref(p), 248, POOL, ctypes.c_void_p(8), 1, WS, big, None) == 1
+    assert lib.moe_dispatch(X, 128, 1, ctypes.byref(p), 248, POOL, None, 1, WS, big, None) == 1
+    # shapes outside the kernels
+    assert lib.moe_dispatch(X, 100, 0, ctypes.byref(p), 248, POOL, None, 1, WS, big, None) == 2
+    assert lib.moe_dispatch(X, 192, 1, ctypes.byref(p), 248, POOL, ctypes.c_void_p(8), 1, WS, big, None) == 2
+    assert lib.moe_dispatch(X, 128, 5, ctypes.byref(p), 248, POOL, None, 1, WS, big, None) == 1
+
+
+def test_ffn_validation(lib):
+    p = _fake_plan()
+    v = [ctypes.c_void_p(a) for a in range(0x10000, 0x10000 * 9, 0x10000)]
+    POOL, W1, W2, WS, Y = v[:5]
+    big = 1 << 40
+
+    def call(H=128, I=64, dtype=0, epoch=1, rows=256, ws=big, cfg=None, scales=(None, None, None)):
+        ps, w1s, w2s = scales
+        return lib.moe_expert_ffn(ctypes.byref(p), rows, POOL, ps, W1, w1s, W2, w2s, H, I, dtype,
+                                  epoch, WS, ws, Y, cfg, None)
+
+    assert call(epoch=0) == 1
+    assert call(rows=250) == 1                     # not whole tiles
+    assert call(dtype=3) == 1
+    assert call(H=96) == 2                         # H % 128
+    assert call(I=48) == 2                         # I % 64
+    assert call(dtype=1, scales=(v[5], v[6], v[7])) == 2   # fp8 needs tile >= 64
+    assert call(dtype=1) == 1                      # fp8 without scales
+    assert call(scales=(v[5], None, None)) == 1    # bf16 with scales
+    assert call(ws=1024) == 1                      # small workspace
+    cfg = _abi.TileConfig(192, 0, 0, 0)
+    assert call(cfg=ctypes.byref(cfg)) == 1        # block_n must be 128 or 256
+
+
+def test_combine_validation(lib):
+    p = _fake_plan()
+    Y, W, OUT = (ctypes.c_void_p(a) for a in (0x10000, 0x20000, 0x30000))
+    assert lib.moe_combine(None, 248, W, ctypes.byref(p), 128, OUT, None) == 1
+    assert lib.moe_combine(Y, -1, W, ctypes.byref(p), 128, OUT, None) == 1
+    assert lib.moe_combine(Y, 248, W, ctypes.byref(p), 100, OUT, None) == 2
+
+
+def test_get_error_validation(lib):
+    assert lib.moe_get_error(None, 1 << 20, None) == 1
