@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE dispatch -> expert FFN -> combine path on one MI355X.
+
+A step is one pass of the whole path (plan, dispatch, expert FFN, combine) over
+one batch of synthetic input already resident in HBM. Prints ONE JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload zipf_skew]
+
+Default workload: zipf_skew (T=16384, H=4096, I=1536, 128 experts, K=8, tile
+128, Zipf(1.2)-biased routing, bf16), the largest of the five workloads.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense MFMA, bf16
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense MFMA, fp8
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    """Hash of the FFN kernel source: counter readings in profiles/ are valid only for it."""
+    p = os.path.join(ROOT, "combine_moe_dispatch_02_amd", "csrc", "ffn.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic(workload: str, src_hash: str):
+    """HBM bytes per FFN call from the committed counter summary, if it matches this source."""
+    p = os.path.join(ROOT, "profiles", f"ffn_traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except ValueError:
+        return None
+    if d.get("ffn_source_sha256_16") != src_hash:
+        return None
+    return d.get("hbm_bytes_per_ffn_call")
+
+
+def algorithmic_work(cfg, idx_np):
+    """Per-step algorithmic work, real rows only (padding excluded)."""
+    import numpy as np
+
+    local = (idx_np >= cfg.expert_begin) & (idx_np < cfg.expert_begin + cfg.num_local_experts)
+    N = int(local.sum())                        # local pairs
+    T_act = int(local.any(axis=1).sum())        # tokens with at least one local pair
+    H, I, K, T = cfg.H, cfg.I, cfg.K, cfg.T
+    pool_b = 2 if cfg.dtype == "bf16" else 1 + 4 / 128
+    return {
+        "pairs": N,
+        "ffn_flops": 6.0 * N * H * I,
+        "dispatch_bytes": T_act * H * 2 + N * H * pool_b,
+        "combine_bytes": N * H * 2 + T * H * 2 + T * K * 8,
+    }
+
+
+def cpu_baseline(inp, sample_tokens: int):
+    """The oracle as it stands, on tokens [0, sample_tokens) of the same workload."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    toks = np.arange(sample_tokens)
+    t0 = time.perf_counter()
+    oracle.moe_layer(inp, tokens=toks)
+    dt = time.perf_counter() - t0
+    return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"tokens 0..{sample_tokens - 1} of the workload (all their pairs), "
+                      f"float64 NumPy oracle incl. weight dequantisation, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="zipf_skew")
+    ap.add_argument("--streams", action="store_true", help="dispatch/combine and FFN on two streams")
+    ap.add_argument("--block-n", type=int, default=0, help="tile config override: N block (0 = auto)")
+    ap.add_argument("--gemm-wgs", type=int, default=0, help="tile config override: GEMM grid (0 = auto)")
+    ap.add_argument("--unit-order", type=int, default=0, help="tile config override: unit walk (0 = auto)")
+    ap.add_argument("--cpu-sample", type=int, default=512, help="tokens of the oracle CPU baseline (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run three 1 GiB device-to-device copies (a known-size reference for "
+                         "the FETCH_SIZE / WRITE_SIZE counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this single-GPU "
+              f"path (no sharding across GPUs is built).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import combine_moe_dispatch_02_amd as moe
+    from synth import config_by_name, make_inputs
+
+    cfg = config_by_name(args.workload)
+    fp8 = cfg.dtype == "fp8"
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    log(f"[bench] generating {cfg.name} inputs")
+    inp = make_inputs(cfg, pin_memory=True)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = inp.x.to(dev, non_blocking=True)
+    idx = inp.topk_idx.to(dev)
+    w = inp.topk_weights.to(dev)
+    if fp8:
+        w1, w2 = inp.w1.view(torch.uint8).to(dev), inp.w2.view(torch.uint8).to(dev)
+        w1s, w2s = inp.w1_scale.to(dev), inp.w2_scale.to(dev)
+    else:
+        w1, w2, w1s, w2s = inp.w1.to(dev), inp.w2.to(dev), None, None
+    torch.cuda.synchronize()
+    tcfg = None
+    if args.block_n or args.gemm_wgs or args.unit_order:
+        tcfg = moe.TileConfig(args.block_n, args.gemm_wgs, 0, args.unit_order, 0)
+    layer = moe.StreamMoE(cfg.T, cfg.H, cfg.I, cfg.K, cfg.num_local_experts,
+                          expert_begin=cfg.expert_begin, tile=cfg.tile, dtype=cfg.dtype, cfg=tcfg)
+    # weight preprocessing at load time (not part of a step): MFMA fragment order when used
+    w1, w2 = layer.prepare_weights(w1, w2)
+    torch.cuda.synchronize()
+    work = algorithmic_work(cfg, inp.topk_idx.numpy())
+    streams = moe.make_streams() if args.streams else None
+
+    def step():
+        return layer.forward(x, idx, w, w1, w2, w1s, w2s, streams)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    rc = moe.moe_get_error(layer.ws)
+    if rc != 0:
+        raise RuntimeError(f"device error {rc} during warmup")
+
+    # whole-step timing: K steps bracketed by synchronisation
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e_start = torch.cuda.Event(enable_timing=True)
+    e_end = torch.cuda.Event(enable_timing=True)
+    e_start.record()
+    for _ in range(args.steps):
+        step()
+    e_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e_start.elapsed_time(e_end) / args.steps
+
+    # per-stage timing on the stream the kernels run on (single stream here)
+    s = torch.cuda.current_stream()
+    stage_ms = {"plan": 0.0, "dispatch": 0.0, "ffn": 0.0, "combine": 0.0}
+    evs = []
+    for _ in range(args.steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        epoch = layer.next_epoch()
+        ev[0].record(s)
+        moe.moe_plan(idx, layer.plan, layer.ws, s)
+        ev[1].record(s)
+        moe.moe_dispatch(x, layer.plan, layer.pool, layer.pool_s, epoch, layer.ws, cfg.dtype, s)
+        ev[2].record(s)
+        moe.moe_expert_ffn(layer.plan, layer.pool, layer.pool_s, w1, w1s, w2, w2s, epoch, layer.ws,
+                           layer.y_pool, cfg.dtype, layer.cfg, s)
+        ev[3].record(s)
+        moe.moe_combine(layer.y_pool, w, layer.plan, layer.out, s)
+        ev[4].record(s)
+        evs.append(ev)
+    torch.cuda.synchronize()
+    rc = moe.moe_get_error(layer.ws)
+    if rc != 0:
+        raise RuntimeError(f"device error {rc} during timing")
+    for ev in evs:
+        for i, k in enumerate(stage_ms):
+            stage_ms[k] += ev[i].elapsed_time(ev[i + 1]) / len(evs)
+
+    tokens_s = cfg.T / (ms_step * 1e-3)
+    ffn_tflops = work["ffn_flops"] / (stage_ms["ffn"] * 1e-3) / 1e12
+    peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
+    disp_gbs = work["dispatch_bytes"] / (stage_ms["dispatch"] * 1e-3) / 1e9
+    comb_gbs = work["combine_bytes"] / (stage_ms["combine"] * 1e-3) / 1e9
+    src_hash = kernel_source_hash()
+    traffic = read_traffic(cfg.name, src_hash)
+    result = {
+        "metric": "MoE layer tokens/s; grouped-GEMM % MFMA peak; dispatch/combine HBM GB/s",
+        "value": round(tokens_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8" if fp8 else "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "I": cfg.I,
+                   "experts": cfg.num_experts, "local_experts": cfg.num_local_experts, "K": cfg.K,
+                   "tile": cfg.tile, "routing": cfg.routing, "pairs": work["pairs"],
+                   "pool_rows": int(layer.plan.offsets[-1].item()),
+                   "streams": "two (comm + compute)" if args.streams else "one",
+                   "weights": "MFMA-tiled (permuted once at load time)" if layer.tiled else "row-major"},
+        "roofline": {"bound": "mfma", "kernel": "expert FFN (grouped GEMM A + Y)",
+                     "achieved": round(ffn_tflops, 1), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(ffn_tflops / peak, 4), "traffic": traffic},
+        "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "dispatch_GBps": round(disp_gbs, 1),
+        "combine_GBps": round(comb_gbs, 1),
+        "dispatch_combine_frac_hbm": round(
+            (work["dispatch_bytes"] + work["combine_bytes"])
+            / ((stage_ms["dispatch"] + stage_ms["combine"]) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "wall_s_timed": round(wall, 3),
+    }
+    if args.cpu_sample > 0:
+        log(f"[bench] oracle CPU baseline on {args.cpu_sample} tokens")
+        result["cpu_baseline"] = cpu_baseline(inp, min(args.cpu_sample, cfg.T))
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -6,6 +6,8 @@ load it, the first call does, and fails loudly if it has not been built.
 from .layer import (  # noqa: F401
     MOE_BF16,
     MOE_FP8_E4M3_G128,
+    MOE_WEIGHTS_MFMA_TILED,
+    MOE_WEIGHTS_ROW_MAJOR,
     MoeError,
     Plan,
     StreamMoE,
@@ -17,6 +19,7 @@ from .layer import (  # noqa: F401
     moe_dispatch,
     moe_expert_ffn,
     moe_get_error,
+    moe_pack_weights,
     moe_plan,
     moe_query_pool_rows,
     pool_rows_upper_bound,

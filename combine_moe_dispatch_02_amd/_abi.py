@@ -16,6 +16,9 @@ MOE_ERR_TIMEOUT = 4
 MOE_BF16 = 0
 MOE_FP8_E4M3_G128 = 1
 
+MOE_WEIGHTS_ROW_MAJOR = 0
+MOE_WEIGHTS_MFMA_TILED = 1
+
 STATUS_NAMES = {
     MOE_OK: "MOE_OK",
     MOE_ERR_INVALID: "MOE_ERR_INVALID",
@@ -54,7 +57,8 @@ class TileConfig(ctypes.Structure):
         ("block_n", ctypes.c_int32),
         ("gemm_workgroups", ctypes.c_int32),
         ("spin_timeout_us", ctypes.c_uint32),
-        ("reserved", ctypes.c_int32),
+        ("unit_order", ctypes.c_int32),
+        ("weight_layout", ctypes.c_int32),
     ]
 
 
@@ -71,6 +75,7 @@ SIGNATURES = [
      [_PP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _U32, _VP, _SZ, _VP,
       ctypes.POINTER(TileConfig), _VP]),
     ("moe_combine", ctypes.c_int, [_VP, _I32, _VP, _PP, _I32, _VP, _VP]),
+    ("moe_pack_weights", ctypes.c_int, [_VP, _I32, _I32, _I32, _I32, _VP, _VP]),
     ("moe_get_error", ctypes.c_int, [_VP, _SZ, _VP]),
     ("moe_status_string", ctypes.c_char_p, [ctypes.c_int]),
     ("moe_device_cu_count", ctypes.c_int, []),

@@ -110,7 +110,9 @@ MOE355_API int moe_expert_ffn(const moe_plan_t* plan, int32_t pool_rows, const v
   if (fp8 && (!pool_s || !w1_s || !w2_s)) return MOE_ERR_INVALID;
   if (!fp8 && (pool_s || w1_s || w2_s)) return MOE_ERR_INVALID;
   const int32_t block_n = cfg ? cfg->block_n : 0;
-  rc = ffn_supported(H, I, dtype, plan->tile, block_n);
+  const int32_t layout = cfg ? cfg->weight_layout : MOE_WEIGHTS_ROW_MAJOR;
+  if (layout != MOE_WEIGHTS_ROW_MAJOR && layout != MOE_WEIGHTS_MFMA_TILED) return MOE_ERR_INVALID;
+  rc = ffn_supported(H, I, dtype, plan->tile, block_n, layout);
   if (rc != MOE_OK) return rc;
   if ((int64_t)pool_rows * H * 2 > ((int64_t)1 << 40)) return MOE_ERR_UNSUPPORTED;
   const WsLayout L = ws_layout(plan->T, plan->K, plan->E_local, plan->tile, pool_rows, I, dtype);
@@ -132,6 +134,9 @@ MOE355_API int moe_expert_ffn(const moe_plan_t* plan, int32_t pool_rows, const v
   f.y_pool = y_pool;
   f.block_n = block_n;
   f.workgroups = cfg ? cfg->gemm_workgroups : 0;
+  f.unit_order = cfg ? cfg->unit_order : 0;
+  f.weight_layout = layout;
+  if (f.unit_order < 0 || f.unit_order > 2) return MOE_ERR_INVALID;
   const uint64_t us = (cfg && cfg->spin_timeout_us) ? cfg->spin_timeout_us : 2000000u;
   f.timeout_ticks = us * 100u;  // s_memrealtime counts at 100 MHz
   return launch_expert_ffn(f, L, static_cast<char*>(ws), static_cast<hipStream_t>(stream));
@@ -145,6 +150,19 @@ MOE355_API int moe_combine(const void* y_pool, int32_t pool_rows, const float* t
   if (H % 8 != 0) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)H * 2 > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
   return launch_combine(y_pool, pool_rows, topk_weights, *plan, H, out, static_cast<hipStream_t>(stream));
+}
+
+MOE355_API int moe_pack_weights(const void* w, int32_t E, int32_t rows, int32_t K, int32_t dtype, void* out,
+                                void* stream) {
+  if (!w || !out || E < 1 || rows < 1 || K < 1) return MOE_ERR_INVALID;
+  if (dtype != MOE_BF16 && dtype != MOE_FP8_E4M3_G128) return MOE_ERR_INVALID;
+  if (rows % 16 != 0 || K % (dtype == MOE_BF16 ? 32 : 128) != 0) return MOE_ERR_UNSUPPORTED;
+  const int64_t bytes = (int64_t)rows * K * (dtype == MOE_BF16 ? 2 : 1);
+  if (bytes > ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
+  const char* a = static_cast<const char*>(w);
+  const char* b = static_cast<const char*>(out);
+  if (a < b + bytes * E && b < a + bytes * E) return MOE_ERR_INVALID;  // overlap
+  return launch_pack_weights(w, E, rows, K, dtype, out, static_cast<hipStream_t>(stream));
 }
 
 MOE355_API int moe_get_error(void* ws, size_t ws_bytes, void* stream) {

@@ -5,14 +5,15 @@
 // expert-major, tile-padded pool (pool-layout dispatch), and dispatch signals
 // each pool tile as it fills (per-tile streaming).
 //
-// One wave per token: the token's row is read once (16-byte lanes) and stored
-// to each of its local pairs' rows, so x is read T*H*2 bytes once and the pool
-// written once per pair. In fp8 mode each 1x128 group (16 lanes x 8 values) is
-// quantised on the way: scale = amax/448 in fp32 (1 for an all-zero group),
-// code = e4m3(x / scale) with IEEE division, round to nearest even, saturating.
-// After its stores a wave releases them (device scope) and bumps each touched
-// tile's fill counter; the wave that completes a tile's real rows stores the
-// epoch into tile_ready with release ordering.
+// Each token's row is read once (16-byte lanes) and stored to each of its
+// local pairs' rows, so x is read T*H*2 bytes once and the pool written once per
+// pair. In fp8 mode each 1x128 group (16 lanes x 8 values) is quantised on the
+// way: scale = amax/448 in fp32 (1 for an all-zero group), code = e4m3(x /
+// scale) with IEEE division, round to nearest even, saturating. A wave handles
+// a run of 64/K tokens and publishes them with a single device-scope release
+// (an L2 write-back on this chip, so it is paid per run, not per row); each
+// stored pair then bumps its tile's fill counter, and the wave that completes a
+// tile's real rows stores the epoch into tile_ready with release ordering.
 #include "common.h"
 #include "kernels.h"
 
@@ -33,26 +34,16 @@ struct DispatchArgs {
   uint32_t* tile_ready;
   uint32_t epoch;
   uint32_t* err;
+  int32_t tokens_per_wave;  // tokens_per_wave * K <= 64
 };
 
+// One token's row: read once, stored to each of its local pairs' rows.
 template <int CPL, bool FP8>
-__global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs a) {
-  const int lane = lane_id();
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= a.T) return;
-  int p = lane < a.K ? a.pos[(int64_t)t * a.K + lane] : -1;
-  if (p >= a.pool_rows) {
-    record_error(a.err, MOE_ERR_INVALID);
-    p = -1;
-  }
-  const uint64_t dest = ballot(p >= 0);
-  if (dest == 0) return;
-
+__device__ inline void dispatch_token(const DispatchArgs& a, int t, int p, uint64_t dest, int lane) {
   const int H = a.H;
   const int nch = H >> 3;  // 16-byte chunks of 8 bf16 in a row
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x + (int64_t)t * H, (uint32_t)H * 2u);
   const int64_t out_row_bytes = FP8 ? H : (int64_t)H * 2;
-
   for (int c0 = 0; c0 < nch; c0 += kWave * CPL) {
     u32x4 v[CPL];
 #pragma unroll
@@ -99,16 +90,44 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs a) {
       }
     }
   }
+}
+
+// A wave dispatches a run of `tpw` consecutive tokens (tpw * K <= 64), then
+// publishes them at once: one device-scope release for all its stores, one
+// relaxed fill count per stored pair (lane i owns pair i of the run), and the
+// wave whose count completes a tile acquires and stores the epoch (release).
+template <int CPL, bool FP8>
+__global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs a) {
+  const int lane = lane_id();
+  const int tpw = a.tokens_per_wave;
+  const int t0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * tpw;
+  if (t0 >= a.T) return;
+  const int ntok = min(tpw, a.T - t0);
+  for (int i = 0; i < ntok; ++i) {
+    const int t = t0 + i;
+    int p = lane < a.K ? a.pos[(int64_t)t * a.K + lane] : -1;
+    if (p >= a.pool_rows) {
+      record_error(a.err, MOE_ERR_INVALID);
+      p = -1;
+    }
+    const uint64_t dest = ballot(p >= 0);
+    if (dest != 0) dispatch_token<CPL, FP8>(a, t, p, dest, lane);
+  }
 
   // publish: this wave's stores, then one fill count per stored row
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  const int npairs = ntok * a.K;
+  int p = lane < npairs ? a.pos[(int64_t)t0 * a.K + lane] : -1;
+  if (p >= a.pool_rows) p = -1;
   if (p >= 0) {
     const int ti = p >> a.tile_shift;
-    const uint32_t old = __hip_atomic_fetch_add(&a.tile_fill[ti], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t old = __hip_atomic_fetch_add(&a.tile_fill[ti], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int e = a.tile_expert[ti];
     const int real = min(a.tile, a.offsets[e] + a.counts[e] - (ti << a.tile_shift));
-    if ((int)old + 1 == real)
+    if ((int)old + 1 == real) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       __hip_atomic_store(&a.tile_ready[ti], a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
@@ -145,7 +164,9 @@ int launch_dispatch(const void* x, int32_t H, int32_t dtype, const moe_plan_t& p
   a.err = reinterpret_cast<uint32_t*>(ws + L.err);
   const int nch = H / 8;
   const int cpl = nch <= 64 ? 1 : nch <= 128 ? 2 : nch <= 256 ? 4 : 8;
-  const dim3 grid((p.T + 3) / 4);
+  a.tokens_per_wave = 64 / p.K;
+  const int waves = (p.T + a.tokens_per_wave - 1) / a.tokens_per_wave;
+  const dim3 grid((waves + 3) / 4);
   if (dtype == MOE_FP8_E4M3_G128)
     launch_cpl<true>(cpl, grid, stream, a);
   else

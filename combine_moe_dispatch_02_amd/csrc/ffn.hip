@@ -24,6 +24,7 @@
 // fp8: v_mfma_scale_f32_16x16x128_f8f6f4 with unit scales (E8M0 127), one per
 // 128-wide K block, then acc += partial * a_scale[row] * b_scale[block] in fp32.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -52,8 +53,12 @@ struct FfnArgs {
   int32_t bs_ld;             // fp8: B scale row stride (= Kdim / 128)
   int64_t bs_expert;         // fp8: B scale entries per expert
   int32_t out_groups;        // fp8 GEMM A: I / 128
+  int32_t ktiles;            // tiled weights: K tiles per 16-row block (K/32 bf16, K/128 fp8)
   int32_t tile_shift;
   int32_t max_tiles;         // pool_rows / tile: tiles the buffers hold
+  int32_t unit_order;        // 1: tile-major (m, j); 2: expert-major, N block outer
+  int32_t n_experts;
+  const int32_t* offsets;
   const int32_t* num_tiles;
   const int32_t* tile_expert;
   const uint32_t* tile_ready;
@@ -66,6 +71,60 @@ struct FfnArgs {
 __device__ inline uint32_t swz(int row, int chunk) { return (uint32_t)(row * 128 + ((chunk ^ (row & 7)) << 4)); }
 
 __device__ inline float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+// ----------------------------------------------------------------------------
+// Unit schedule shared by the kernels
+// ----------------------------------------------------------------------------
+// Unit u -> (pool tile m, N block j). Order 1 walks tiles, N blocks inside a
+// tile (the pool tile is reused from L2 by its N blocks). Order 2 walks
+// experts, then N blocks, then the expert's tiles, so units that run together
+// stream the same weight panel. Persistent workgroups are dealt to XCDs
+// round-robin by the dispatcher (workgroup g runs on XCD g % 8), so slot(g)
+// gives each XCD a contiguous run of units and its L2 sees the shared panel.
+__device__ inline void unit_coords(const FfnArgs& a, int u, int order, int& m, int& j) {
+  if (order != 2) {
+    m = u / a.n_units;
+    j = u - m * a.n_units;
+    return;
+  }
+  int lo = 0, hi = a.n_experts - 1;
+  while (lo < hi) {  // largest e whose first unit is <= u (empty experts share a start)
+    const int mid = (lo + hi + 1) >> 1;
+    if ((a.offsets[mid] >> a.tile_shift) * a.n_units <= u) lo = mid;
+    else hi = mid - 1;
+  }
+  const int t0 = a.offsets[lo] >> a.tile_shift;
+  const int te = (a.offsets[lo + 1] >> a.tile_shift) - t0;
+  const int local = u - t0 * a.n_units;
+  j = local / te;
+  m = t0 + (local - j * te);
+}
+
+__device__ inline int unit_slot(int g, int G) { return (G & 7) == 0 ? (g & 7) * (G >> 3) + (g >> 3) : g; }
+
+// wait until tile m's ready flag equals the epoch; false when the unit is skipped
+__device__ inline bool wait_tile_ready(const FfnArgs& a, int m, int* s_go) {
+  if (threadIdx.x == 0) {
+    int go = 1;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (__hip_atomic_load(&a.tile_ready[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.epoch) {
+      if (load_error(a.err) != 0) { go = 0; break; }
+      if (__builtin_amdgcn_s_memrealtime() - t0 > a.timeout) {
+        record_error(a.err, MOE_ERR_TIMEOUT);
+        go = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(4);
+    }
+    *s_go = go;
+  }
+  __syncthreads();
+  const int go = *s_go;
+  __syncthreads();  // s_go is rewritten for the next unit only after everyone read it
+  if (go) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return go != 0;
+}
+
 
 template <int BM, int BN, int WM, int WN, bool FP8, bool GEMM_A>
 struct Gemm {
@@ -120,27 +179,7 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(FfnArgs a) {
     const int m0 = m * BM;
     const int e = a.tile_expert[m];
 
-    if (a.wait_ready) {
-      if (tid == 0) {
-        int go = 1;
-        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-        while (__hip_atomic_load(&a.tile_ready[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.epoch) {
-          if (load_error(a.err) != 0) { go = 0; break; }
-          if (__builtin_amdgcn_s_memrealtime() - t0 > a.timeout) {
-            record_error(a.err, MOE_ERR_TIMEOUT);
-            go = 0;
-            break;
-          }
-          __builtin_amdgcn_s_sleep(4);
-        }
-        s_go = go;
-      }
-      __syncthreads();
-      const int go = s_go;
-      __syncthreads();  // s_go is rewritten for the next unit only after everyone read it
-      if (!go) continue;
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    }
+    if (a.wait_ready && !wait_tile_ready(a, m, &s_go)) continue;
 
     // sources of this unit
     const uint8_t* Arow0 = a.A + (int64_t)m0 * a.lda;
@@ -341,10 +380,373 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(FfnArgs a) {
 }
 
 // ----------------------------------------------------------------------------
+// Big-tile kernel: BM x 512 output per workgroup, NW waves of BM x (512/NW).
+//   A (the pool tile or h, shared by all waves) is loaded two K steps ahead
+//   into registers and goes through a two-stage LDS ring; B (weights: each
+//   wave owns 512/NW output columns that no other wave reads) streams from
+//   global memory straight into registers, already in MFMA fragment layout,
+//   one K step ahead of the one being multiplied. (A is the stream that misses
+//   L2 -- a pool tile is used by one unit per N block, far apart in time --
+//   while a weight panel is shared by the units running side by side on an XCD.)
+//   A K step is 128 bytes of a row: 64 bf16 (two 16x16x32 MFMAs per tile) or
+//   128 e4m3 (one 16x16x128 MFMA per tile = one scale block). In fp8 the
+//   accumulator is kept in units of the current block's scale a_s[row] *
+//   b_s[block]: each block first rescales it by old/new scale, then the MFMA
+//   accumulates the block's code product in place; the epilogue applies the
+//   last scale. (No second set of partial-sum registers.) The kernel is
+//   used when the K extents are whole pairs of steps, so every step issues
+//   the same loads and the compiler's load counters stay exact.
+//   The MFMA runs transposed (weight fragment first), so a lane holds one
+//   output row and 4 consecutive output columns: 8-byte stores, one fp8 row
+//   scale per lane.
+// ----------------------------------------------------------------------------
+template <int BM, int NW, bool FP8, bool GEMM_A>
+struct Big {
+  static constexpr int kThreads = 64 * NW;
+  static constexpr int kBN = 512;
+  static constexpr int kWCols = kBN / NW;       // output columns per wave
+  static constexpr int kHalf = kWCols / 2;      // gate (or first-half) columns per wave
+  static constexpr int kTN = kWCols / 16;       // 16-wide tiles per wave
+  static constexpr int kTM = BM / 16;
+  static constexpr int kKB = 128;               // bytes of a row per K step
+  static constexpr int kCH = 8;                 // 16-byte chunks of a row per K step
+  static constexpr int kKS = FP8 ? 1 : 2;       // MFMAs per tile per K step
+  static constexpr int kAStage = BM * kKB;
+  static constexpr int kAChunks = BM * kCH;
+  static constexpr int kALoads = (kAChunks + kThreads - 1) / kThreads;
+};
+
+__device__ inline uint32_t swz_a(int r, int c) {
+  // 8 consecutive rows reading one chunk column hit 8 distinct 16-byte bank groups
+  return (uint32_t)(r * 128 + ((c ^ (r & 7)) << 4));
+}
+
+template <int BM, int NW, bool FP8, bool GEMM_A, bool PACKED>
+__global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
+  using C = Big<BM, NW, FP8, GEMM_A>;
+  constexpr int TN = C::kTN, TM = C::kTM, KS = C::kKS, HALF = C::kHalf;
+  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][C::kAStage];
+  __shared__ float s_as[2][FP8 ? BM : 1];
+  __shared__ float s_red[FP8 && GEMM_A ? NW : 1][FP8 && GEMM_A ? BM : 1];
+  __shared__ int s_go;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wn = tid >> 6;
+  const int l16 = lane & 15;
+  const int lhi = lane >> 4;
+
+  int ntiles = a.num_tiles[0];
+  int order = a.unit_order;
+  if (ntiles > a.max_tiles) {
+    if (blockIdx.x == 0 && tid == 0) record_error(a.err, MOE_ERR_INVALID);
+    ntiles = a.max_tiles;
+    order = 1;
+  }
+  const int total = ntiles * a.n_units;
+  const int slot = unit_slot(blockIdx.x, gridDim.x);
+  const int nk = a.ksteps;  // even
+
+  for (int u = slot; u < total; u += gridDim.x) {
+    int m, j;
+    unit_coords(a, u, order, m, j);
+    const int m0 = m * BM;
+    const int e = a.tile_expert[m];
+    if (a.wait_ready && !wait_tile_ready(a, m, &s_go)) continue;
+
+    // buffer resources: uniform bases, 32-bit lane offsets, uniform per-tile/step offsets
+    const __amdgpu_buffer_rsrc_t ar = make_rsrc(a.A + (int64_t)m0 * a.lda, (uint32_t)(BM * a.lda));
+    const __amdgpu_buffer_rsrc_t br = make_rsrc(a.B + (int64_t)e * a.b_expert, (uint32_t)a.b_expert);
+    // this wave's weight rows: tiles 0..TN/2-1 from rbase0, TN/2..TN-1 from rbase1
+    const int rbase0 = GEMM_A ? j * 256 + wn * HALF : j * 512 + wn * C::kWCols;
+    const int rbase1 = GEMM_A ? a.up_row0 + j * 256 + wn * HALF : rbase0 + HALF;
+    const uint32_t ldb = (uint32_t)a.ldb;
+    const uint32_t lda = (uint32_t)a.lda;
+    // lane's K bytes inside a step: bf16 16 at 16*lhi (+64 for the second MFMA), fp8 32 at 32*lhi
+    const uint32_t lane_k = (uint32_t)lhi * (FP8 ? 32u : 16u);
+    const uint32_t boff0 = (uint32_t)(rbase0 + l16) * ldb + lane_k;
+    const uint32_t boff1 = (uint32_t)(rbase1 + l16) * ldb + lane_k;
+    const uint32_t tstride = 16u * ldb;
+    uint32_t aoff[C::kALoads];
+#pragma unroll
+    for (int i = 0; i < C::kALoads; ++i) {
+      const int c = tid + i * C::kThreads;
+      aoff[i] = (uint32_t)(c >> 3) * lda + (uint32_t)(c & 7) * 16u;
+    }
+    const float* bsx = nullptr;
+    if constexpr (FP8) bsx = a.B_s + (int64_t)e * a.bs_expert;
+
+    // weight fragments [buffer][tile]: bf16 two 16-byte K halves, fp8 one 32-byte tuple
+    u32x4 rb[2][TN][FP8 ? 1 : 2];
+    i32x8_t rb8[2][FP8 ? TN : 1];
+    // A (the pool tile: the stream that misses L2) is loaded two steps ahead into
+    // one of two register sets, and written to LDS one step ahead
+    u32x4 ra[2][C::kALoads];
+    float ras[2] = {0.f, 0.f};
+    float sbn[2][2];
+
+    auto load_a = [&](auto SET, int ks) {
+      constexpr int st = decltype(SET)::value;
+      const uint32_t kofs = (uint32_t)ks * 128u;
+#pragma unroll
+      for (int i = 0; i < C::kALoads; ++i) {
+        const int c = tid + i * C::kThreads;
+        if (C::kAChunks % C::kThreads == 0 || c < C::kAChunks)
+          ra[st][i] = __builtin_amdgcn_raw_buffer_load_b128(ar, aoff[i], kofs, 0);
+      }
+      if constexpr (FP8) {
+        if (tid < BM) ras[st] = a.A_s[(int64_t)(m0 + tid) * a.s_kblocks + ks];
+      }
+    };
+    auto store_a = [&](auto SET, int stage) {
+      constexpr int st = decltype(SET)::value;
+#pragma unroll
+      for (int i = 0; i < C::kALoads; ++i) {
+        const int c = tid + i * C::kThreads;
+        if (C::kAChunks % C::kThreads == 0 || c < C::kAChunks)
+          *reinterpret_cast<u32x4*>(&s_a[stage][0] + swz_a(c >> 3, c & 7)) = ra[st][i];
+      }
+      if constexpr (FP8) {
+        if (tid < BM) s_as[stage][tid] = ras[st];
+      }
+    };
+    auto load_b = [&](auto BUF, int ks) {
+      constexpr int bb = decltype(BUF)::value;
+      const uint32_t kofs = (uint32_t)ks * 128u;
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        if constexpr (PACKED) {
+          // tiled weights: the tile (row block, K tile) is 1 KiB contiguous, lane l at l*16
+          const uint32_t rowblk = (uint32_t)((tn < TN / 2 ? rbase0 : rbase1) + (tn % (TN / 2)) * 16) >> 4;
+          const uint32_t tbase = (rowblk * (uint32_t)a.ktiles + (uint32_t)ks * (FP8 ? 1u : 2u)) * (FP8 ? 2048u : 1024u);
+          if constexpr (FP8) {
+            const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(br, (uint32_t)lane * 16u, tbase, 0);
+            const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(br, (uint32_t)lane * 16u, tbase + 1024u, 0);
+            rb8[bb][tn] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          } else {
+            rb[bb][tn][0] = __builtin_amdgcn_raw_buffer_load_b128(br, (uint32_t)lane * 16u, tbase, 0);
+            rb[bb][tn][1] = __builtin_amdgcn_raw_buffer_load_b128(br, (uint32_t)lane * 16u, tbase + 1024u, 0);
+          }
+          continue;
+        }
+        const uint32_t vo = tn < TN / 2 ? boff0 : boff1;
+        const uint32_t so = (uint32_t)(tn % (TN / 2)) * tstride + kofs;
+        if constexpr (FP8) {
+          const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(br, vo, so, 0);
+          const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(br, vo, so + 16u, 0);
+          rb8[bb][tn] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        } else {
+          rb[bb][tn][0] = __builtin_amdgcn_raw_buffer_load_b128(br, vo, so, 0);
+          rb[bb][tn][1] = __builtin_amdgcn_raw_buffer_load_b128(br, vo, so + 64u, 0);
+        }
+      }
+      if constexpr (FP8) {
+        sbn[bb][0] = bsx[(rbase0 >> 7) * a.bs_ld + ks];
+        sbn[bb][1] = bsx[(rbase1 >> 7) * a.bs_ld + ks];
+      }
+    };
+
+    f32x4_t acc[TM][TN];
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float cur_s[FP8 ? TM : 1][2];  // fp8: scale that acc is currently expressed in
+#pragma unroll
+    for (int tm = 0; tm < (FP8 ? TM : 1); ++tm) cur_s[tm][0] = cur_s[tm][1] = 1.f;
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    load_b(I0{}, 0);
+    load_a(I0{}, 0);
+    load_a(I1{}, nk > 1 ? 1 : 0);
+    store_a(I0{}, 0);
+    __syncthreads();
+
+    auto step = [&](auto BUF, int ks) {
+      constexpr int bb = decltype(BUF)::value;
+      // keep each step's instructions inside the step: hoisting the next step's loads
+      // above these MFMAs would keep two copies of a B buffer alive
+      __builtin_amdgcn_sched_barrier(0);
+      // prefetch step ks+1 unconditionally (the last step reloads itself into the idle
+      // buffer, which nobody reads): a branch here would make the compiler's load
+      // counter waits cover the loads just issued and serialise the pipeline
+      const int kn = ks + 1 < nk ? ks + 1 : ks;
+      const int ka = ks + 2 < nk ? ks + 2 : nk - 1;
+      load_a(std::integral_constant<int, bb>{}, ka);   // the set that held A(ks), already in LDS
+      load_b(std::integral_constant<int, bb ^ 1>{}, kn);
+      // issue the prefetch before this step's MFMAs (into the other buffer), not after them
+      __builtin_amdgcn_sched_barrier(0);
+      const uint8_t* sa = &s_a[bb][0];
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+        const int r = tm * 16 + l16;
+        if constexpr (!FP8) {
+#pragma unroll
+          for (int kk = 0; kk < KS; ++kk) {
+            const bf16x8_t fa = *reinterpret_cast<const bf16x8_t*>(sa + swz_a(r, kk * 4 + lhi));
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn)
+              acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8_t, rb[bb][tn][kk]), fa, acc[tm][tn], 0, 0, 0);
+          }
+        } else {
+          const u32x4 lo = *reinterpret_cast<const u32x4*>(sa + swz_a(r, 2 * lhi));
+          const u32x4 hi = *reinterpret_cast<const u32x4*>(sa + swz_a(r, 2 * lhi + 1));
+          const i32x8_t fa = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          // acc is kept in units of this K block's scale: rescale by old/new, then
+          // accumulate the block's integer-grid product in place
+          const float sar = s_as[bb][r];
+          const float s0 = sar * sbn[bb][0], s1 = sar * sbn[bb][1];
+          const float r0 = cur_s[tm][0] * __builtin_amdgcn_rcpf(s0);
+          const float r1 = cur_s[tm][1] * __builtin_amdgcn_rcpf(s1);
+          cur_s[tm][0] = s0;
+          cur_s[tm][1] = s1;
+#pragma unroll
+          for (int tn = 0; tn < TN; ++tn) {
+            const float rr = tn < TN / 2 ? r0 : r1;
+            acc[tm][tn] *= rr;
+            acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(rb8[bb][tn], fa, acc[tm][tn], 0, 0, 0,
+                                                                           127, 0, 127);
+          }
+        }
+      }
+      store_a(std::integral_constant<int, bb ^ 1>{}, bb ^ 1);  // A(ks+1), loaded last step
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    for (int ks = 0; ks < nk; ks += 2) {
+      step(std::integral_constant<int, 0>{}, ks);
+      step(std::integral_constant<int, 1>{}, ks + 1);
+    }
+
+    // ---------------- epilogue: lane holds row tm*16+l16, columns 4*lhi + (0..3) of each tile
+    if constexpr (FP8) {
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) acc[tm][tn] *= cur_s[tm][tn < TN / 2 ? 0 : 1];
+    }
+    if constexpr (GEMM_A) {
+      const int hcol0 = j * 256 + wn * HALF + 4 * lhi;
+      if constexpr (!FP8) {
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+          const int row = m0 + tm * 16 + l16;
+          uint8_t* orow = a.out + (int64_t)row * a.ldo;
+#pragma unroll
+          for (int tn = 0; tn < TN / 2; ++tn) {
+            u32x2 v;
+            v.x = pack_bf16x2(silu_mul(acc[tm][tn][0], acc[tm][tn + TN / 2][0]),
+                              silu_mul(acc[tm][tn][1], acc[tm][tn + TN / 2][1]));
+            v.y = pack_bf16x2(silu_mul(acc[tm][tn][2], acc[tm][tn + TN / 2][2]),
+                              silu_mul(acc[tm][tn][3], acc[tm][tn + TN / 2][3]));
+            *reinterpret_cast<u32x2*>(orow + (hcol0 + tn * 16) * 2) = v;
+          }
+        }
+      } else {
+        // an h group of 128 columns = the HALF columns of 128/HALF consecutive waves
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+          float mx = 0.f;
+#pragma unroll
+          for (int tn = 0; tn < TN / 2; ++tn)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float h = silu_mul(acc[tm][tn][i], acc[tm][tn + TN / 2][i]);
+              acc[tm][tn][i] = h;
+              mx = fmaxf(mx, fabsf(h));
+            }
+          mx = fmaxf(mx, __shfl_xor(mx, 16));
+          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          if (lhi == 0) s_red[wn][tm * 16 + l16] = mx;
+        }
+        __syncthreads();
+        constexpr int GW = 128 / HALF;  // waves per h group
+        const int w0 = wn / GW * GW;
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+          const int rl = tm * 16 + l16;
+          float mx = s_red[w0][rl];
+#pragma unroll
+          for (int g = 1; g < GW; ++g) mx = fmaxf(mx, s_red[w0 + g][rl]);
+          const float sc = mx > 0.f ? mx / 448.0f : 1.0f;
+          const int row = m0 + rl;
+          uint8_t* orow = a.out + (int64_t)row * a.ldo;
+#pragma unroll
+          for (int tn = 0; tn < TN / 2; ++tn)
+            *reinterpret_cast<uint32_t*>(orow + hcol0 + tn * 16) =
+                pack_e4m3x4(acc[tm][tn][0] / sc, acc[tm][tn][1] / sc, acc[tm][tn][2] / sc, acc[tm][tn][3] / sc);
+          if (wn % GW == 0 && lhi == 0)
+            a.out_s[(int64_t)row * a.out_groups + ((j * 256 + wn * HALF) >> 7)] = sc;
+        }
+        __syncthreads();
+      }
+    } else {
+      const int col0 = j * 512 + wn * C::kWCols + 4 * lhi;
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+        const int row = m0 + tm * 16 + l16;
+        uint8_t* orow = a.out + (int64_t)row * a.ldo;
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          u32x2 v;
+          v.x = pack_bf16x2(acc[tm][tn][0], acc[tm][tn][1]);
+          v.y = pack_bf16x2(acc[tm][tn][2], acc[tm][tn][3]);
+          *reinterpret_cast<u32x2*>(orow + (col0 + tn * 16) * 2) = v;
+        }
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Load-time weight permutation into MFMA fragment order (layout in moe355.h).
+// One thread per 16-byte destination chunk: reads 16 source bytes, writes them
+// to their tile slot, so a whole wave writes 1 KiB contiguously.
+// ----------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void pack_weights_kernel(const uint8_t* w, uint8_t* out, int64_t chunks,
+                                                           int32_t row_bytes, int32_t fp8) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= chunks) return;
+  // destination chunk c -> (tile, half, lane); a tile is 1 KiB (bf16) or 2 KiB (fp8)
+  const int64_t tile = fp8 ? c >> 7 : c >> 6;
+  const int half = fp8 ? (int)((c >> 6) & 1) : 0;
+  const int lane = (int)(c & 63);
+  const int ktiles = fp8 ? row_bytes / 128 : row_bytes / 64;   // K tiles per 16-row block
+  const int64_t rb = tile / ktiles;            // global row block (experts stacked)
+  const int kb = (int)(tile - rb * ktiles);
+  const int64_t row = rb * 16 + (lane & 15);
+  const int64_t col_byte = fp8 ? (int64_t)kb * 128 + 32 * (lane >> 4) + 16 * half
+                               : (int64_t)kb * 64 + 16 * (lane >> 4);
+  const u32x4 v = *reinterpret_cast<const u32x4*>(w + row * row_bytes + col_byte);
+  *reinterpret_cast<u32x4*>(out + c * 16) = v;
+}
+
+int launch_pack_weights(const void* w, int32_t E, int32_t rows, int32_t K, int32_t dtype, void* out,
+                        hipStream_t stream) {
+  const bool fp8 = dtype == MOE_FP8_E4M3_G128;
+  const int32_t row_bytes = K * (fp8 ? 1 : 2);
+  const int64_t chunks = (int64_t)E * rows * row_bytes / 16;
+  const int64_t blocks = (chunks + 255) / 256;
+  hipLaunchKernelGGL(pack_weights_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     static_cast<const uint8_t*>(w), static_cast<uint8_t*>(out), chunks, row_bytes, (int)fp8);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+// ----------------------------------------------------------------------------
 // host side
 // ----------------------------------------------------------------------------
-int ffn_supported(int32_t H, int32_t I, int32_t dtype, int32_t tile, int32_t block_n) {
-  if (block_n != 0 && block_n != 128 && block_n != 256) return MOE_ERR_INVALID;
+int ffn_supported(int32_t H, int32_t I, int32_t dtype, int32_t tile, int32_t block_n, int32_t weight_layout) {
+  if (block_n != 0 && block_n != 128 && block_n != 256 && block_n != 512) return MOE_ERR_INVALID;
+  // the big-tile kernel wants whole 256/512-column units and an even number of 128-byte K steps
+  const bool big_a = dtype == MOE_BF16 && (tile == 64 || tile == 128) && I % 256 == 0 && H % 128 == 0;
+  const bool big_y = dtype == MOE_BF16 && (tile == 64 || tile == 128) && H % 512 == 0 && I % 128 == 0;
+  if (block_n == 512 && !(big_a && big_y)) return MOE_ERR_UNSUPPORTED;
+  // tiled weights are read by the big-tile kernel only, so both GEMMs must take it
+  if (weight_layout == MOE_WEIGHTS_MFMA_TILED && (!(big_a && big_y) || (block_n != 0 && block_n != 512)))
+    return MOE_ERR_UNSUPPORTED;
   if (dtype == MOE_BF16) {
     if (H % 128 != 0 || I % 64 != 0) return MOE_ERR_UNSUPPORTED;
     if (block_n == 256 && (tile < 64 || I % 128 != 0)) return MOE_ERR_UNSUPPORTED;
@@ -357,13 +759,35 @@ int ffn_supported(int32_t H, int32_t I, int32_t dtype, int32_t tile, int32_t blo
   return MOE_ERR_INVALID;
 }
 
+#ifndef MOE_BIG_WAVES
+#define MOE_BIG_WAVES 8
+#endif
+constexpr int kBigWaves = MOE_BIG_WAVES;
+
 template <int BM, int BN, int WM, int WN, bool FP8, bool GEMM_A>
 static void launch_one(const FfnArgs& a, int grid, hipStream_t s) {
   hipLaunchKernelGGL((ffn_gemm_kernel<BM, BN, WM, WN, FP8, GEMM_A>), dim3(grid), dim3(256), 0, s, a);
 }
 
+template <bool FP8, bool GEMM_A, bool PACKED>
+static int launch_big(int tile, const FfnArgs& a, int grid, hipStream_t s) {
+  constexpr int NW = kBigWaves;
+  if (tile == 128) hipLaunchKernelGGL((ffn_big_kernel<128, NW, FP8, GEMM_A, PACKED>), dim3(grid), dim3(64 * NW), 0, s, a);
+  else if (tile == 64) hipLaunchKernelGGL((ffn_big_kernel<64, NW, FP8, GEMM_A, PACKED>), dim3(grid), dim3(64 * NW), 0, s, a);
+  else return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
 template <bool FP8, bool GEMM_A>
-static int launch_shape(int tile, int bn, const FfnArgs& a, int grid, hipStream_t s) {
+static int launch_shape(int tile, int bn, bool packed, const FfnArgs& a, int grid, hipStream_t s) {
+  if (bn == 512) {
+    if constexpr (FP8) {
+      return MOE_ERR_UNSUPPORTED;  // fp8 runs on the general kernel
+    } else {
+      return packed ? launch_big<FP8, GEMM_A, true>(tile, a, grid, s) : launch_big<FP8, GEMM_A, false>(tile, a, grid, s);
+    }
+  }
+  if (packed) return MOE_ERR_UNSUPPORTED;
   if constexpr (FP8) {
     if (tile == 128) launch_one<128, 256, 2, 2, true, GEMM_A>(a, grid, s);
     else if (tile == 64) launch_one<64, 256, 1, 4, true, GEMM_A>(a, grid, s);
@@ -386,23 +810,32 @@ static int launch_shape(int tile, int bn, const FfnArgs& a, int grid, hipStream_
   }
 }
 
+// N block of each GEMM: the big-tile kernel (512) where the shape allows it,
+// else the largest the general kernel takes, unless overridden.
+static void pick_block_n(const FfnLaunch& f, int tile, int& bn_a, int& bn_y) {
+  const bool fp8 = f.dtype == MOE_FP8_E4M3_G128;
+  const bool big_a = !fp8 && (tile == 64 || tile == 128) && f.I % 256 == 0 && f.H % 128 == 0;
+  const bool big_y = !fp8 && (tile == 64 || tile == 128) && f.H % 512 == 0 && f.I % 128 == 0;
+  if (f.block_n == 512) {
+    bn_a = bn_y = 512;
+    return;
+  }
+  if (f.block_n == 128 || f.block_n == 256) {
+    bn_a = bn_y = fp8 ? 256 : f.block_n;
+  } else {
+    bn_a = big_a ? 512 : fp8 ? 256 : (tile >= 64 && f.I % 128 == 0) ? 256 : 128;
+    bn_y = big_y ? 512 : fp8 ? 256 : (tile >= 64 && f.H % 256 == 0) ? 256 : 128;
+  }
+  if (!fp8 && bn_y == 256 && f.H % 256 != 0) bn_y = 128;
+}
+
 int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream_t stream) {
   const moe_plan_t& p = *f.plan;
   const bool fp8 = f.dtype == MOE_FP8_E4M3_G128;
   const int H = f.H, I = f.I, tile = p.tile;
   const int eb = fp8 ? 1 : 2;  // bytes per element
-  // N block per GEMM: the largest the shape allows, unless overridden
   int bn_a, bn_y;
-  if (fp8) {
-    bn_a = 256;
-    bn_y = 256;
-  } else if (f.block_n) {
-    bn_a = bn_y = f.block_n;
-  } else {
-    bn_a = (tile >= 64 && I % 128 == 0) ? 256 : 128;
-    bn_y = (tile >= 64 && H % 256 == 0) ? 256 : 128;
-  }
-  if (!fp8 && bn_y == 256 && H % 256 != 0) bn_y = 128;
+  pick_block_n(f, tile, bn_a, bn_y);
   uint8_t* h = reinterpret_cast<uint8_t*>(ws + L.h);
   float* hs = fp8 ? reinterpret_cast<float*>(ws + L.hs) : nullptr;
   const int ntiles_cap = std::min(p.rows_cap, f.pool_rows) / tile;
@@ -410,6 +843,8 @@ int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream
   FfnArgs a{};
   a.tile_shift = __builtin_ctz((unsigned)tile);
   a.max_tiles = f.pool_rows / tile;
+  a.n_experts = p.E_local;
+  a.offsets = p.offsets;
   a.num_tiles = p.num_tiles;
   a.tile_expert = p.tile_expert;
   a.tile_ready = p.tile_ready;
@@ -436,12 +871,15 @@ int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream
   a.bs_expert = (int64_t)(2 * I / 128) * (H / 128);
   a.out_groups = I / 128;
   a.wait_ready = 1;
+  a.unit_order = bn_a == 512 ? (f.unit_order ? f.unit_order : 2) : 1;
   int grid = f.workgroups > 0 ? f.workgroups : device_cu_count();
   if (grid <= 0) return MOE_ERR_HIP;
   int ga = (int)std::min<int64_t>(grid, (int64_t)ntiles_cap * a.n_units);
   if (ga < 1) ga = 1;
-  int rc = fp8 ? launch_shape<true, true>(tile, bn_a, a, ga, stream)
-               : launch_shape<false, true>(tile, bn_a, a, ga, stream);
+  const bool packed = f.weight_layout == MOE_WEIGHTS_MFMA_TILED;
+  a.ktiles = H / (fp8 ? 128 : 32);
+  int rc = fp8 ? launch_shape<true, true>(tile, bn_a, packed, a, ga, stream)
+               : launch_shape<false, true>(tile, bn_a, packed, a, ga, stream);
   if (rc != MOE_OK) return rc;
   if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
 
@@ -463,10 +901,12 @@ int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream
   a.bs_ld = I / 128;
   a.bs_expert = (int64_t)(H / 128) * (I / 128);
   a.wait_ready = 0;
+  a.unit_order = bn_y == 512 ? (f.unit_order ? f.unit_order : 2) : 1;
   int gy = (int)std::min<int64_t>(grid, (int64_t)ntiles_cap * a.n_units);
   if (gy < 1) gy = 1;
-  rc = fp8 ? launch_shape<true, false>(tile, bn_y, a, gy, stream)
-           : launch_shape<false, false>(tile, bn_y, a, gy, stream);
+  a.ktiles = I / (fp8 ? 128 : 32);
+  rc = fp8 ? launch_shape<true, false>(tile, bn_y, packed, a, gy, stream)
+           : launch_shape<false, false>(tile, bn_y, packed, a, gy, stream);
   if (rc != MOE_OK) return rc;
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

@@ -28,6 +28,8 @@ struct FfnLaunch {
   void* y_pool;
   int32_t block_n;
   int32_t workgroups;
+  int32_t unit_order;
+  int32_t weight_layout;
   uint64_t timeout_ticks;   // s_memrealtime ticks (100 MHz)
 };
 
@@ -37,7 +39,10 @@ int launch_combine(const void* y_pool, int32_t pool_rows, const float* topk_weig
                    int32_t H, void* out, hipStream_t stream);
 
 // what the FFN supports (host-side check shared by validation and launch)
-int ffn_supported(int32_t H, int32_t I, int32_t dtype, int32_t tile, int32_t block_n);
+int ffn_supported(int32_t H, int32_t I, int32_t dtype, int32_t tile, int32_t block_n, int32_t weight_layout);
+
+int launch_pack_weights(const void* w, int32_t E, int32_t rows, int32_t K, int32_t dtype, void* out,
+                        hipStream_t stream);
 
 int device_cu_count();
 

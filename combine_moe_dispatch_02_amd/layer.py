@@ -15,12 +15,14 @@ from typing import Optional, Tuple
 import torch
 
 from . import _abi
-from ._abi import MOE_BF16, MOE_FP8_E4M3_G128, MoeError, PlanT, TileConfig, check, load
+from ._abi import (MOE_BF16, MOE_FP8_E4M3_G128, MOE_WEIGHTS_MFMA_TILED, MOE_WEIGHTS_ROW_MAJOR, MoeError,
+                   PlanT, TileConfig, check, load)
 
 __all__ = [
     "MOE_BF16", "MOE_FP8_E4M3_G128", "MoeError", "Plan", "Workspace", "TileConfig",
     "pool_rows_upper_bound", "workspace_bytes", "moe_plan", "moe_query_pool_rows",
-    "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_get_error", "device_cu_count",
+    "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_get_error", "moe_pack_weights",
+    "device_cu_count", "MOE_WEIGHTS_ROW_MAJOR", "MOE_WEIGHTS_MFMA_TILED",
     "make_streams", "StreamMoE", "stream_moe",
 ]
 
@@ -181,6 +183,16 @@ def moe_combine(y_pool: torch.Tensor, topk_weights: torch.Tensor, plan: Plan, ou
                                             ctypes.byref(c), out.shape[1], _vp(out), _stream(stream)))
 
 
+def moe_pack_weights(w: torch.Tensor, dtype="bf16", stream=None) -> torch.Tensor:
+    """Permute expert weights [E, rows, K] into MFMA fragment order (a new tensor)."""
+    _need_cuda(w, "w")
+    E, rows, K = w.shape
+    out = torch.empty_like(w)
+    check("moe_pack_weights", load().moe_pack_weights(_vp(w), E, rows, K, _dtype_code(dtype), _vp(out),
+                                                      _stream(stream)))
+    return out
+
+
 def moe_get_error(ws: Workspace, stream=None) -> int:
     return int(load().moe_get_error(_vp(ws.buf), ws.nbytes, _stream(stream)))
 
@@ -198,10 +210,19 @@ class StreamMoE:
     """
 
     def __init__(self, T, H, I, K, num_local_experts, *, expert_begin=0, tile=128, dtype="bf16",
-                 device="cuda", pool_rows: Optional[int] = None, cfg: Optional[TileConfig] = None):
+                 device="cuda", pool_rows: Optional[int] = None, cfg: Optional[TileConfig] = None,
+                 weight_layout: str = "auto"):
         self.T, self.H, self.I, self.K = T, H, I, K
         self.E_local, self.expert_begin, self.tile = num_local_experts, expert_begin, tile
         self.dtype = "fp8" if _dtype_code(dtype) == MOE_FP8_E4M3_G128 else "bf16"
+        tiled_ok = (self.dtype == "bf16" and tile in (64, 128) and I % 256 == 0 and H % 512 == 0
+                    and (cfg is None or cfg.block_n in (0, 512)))
+        if weight_layout == "tiled" and not tiled_ok:
+            raise MoeError("StreamMoE", _abi.MOE_ERR_UNSUPPORTED)
+        self.tiled = weight_layout == "tiled" or (weight_layout == "auto" and tiled_ok)
+        if cfg is None:
+            cfg = TileConfig(0, 0, 0, 0, 0)
+        cfg.weight_layout = MOE_WEIGHTS_MFMA_TILED if self.tiled else MOE_WEIGHTS_ROW_MAJOR
         self.cfg = cfg
         self.plan = Plan.allocate(T, K, expert_begin, num_local_experts, tile, device)
         rows = pool_rows or self.plan.rows_cap
@@ -214,14 +235,22 @@ class StreamMoE:
         self.out = torch.empty(T, H, dtype=torch.bfloat16, device=device)
         self.epoch = 0
 
+    def prepare_weights(self, w1, w2):
+        """The weights as forward() wants them: permuted once into MFMA fragment order when the
+        layer uses tiled weights (a load-time step, like any weight preprocessing), else as is."""
+        if not self.tiled:
+            return w1, w2
+        return moe_pack_weights(w1, self.dtype), moe_pack_weights(w2, self.dtype)
+
     def next_epoch(self) -> int:
         self.epoch = (self.epoch % 0xFFFFFFFF) + 1      # 1 .. 2^32-1; 0 is never a valid epoch
         return self.epoch
 
     def forward(self, x, topk_idx, topk_weights, w1, w2, w1_scale=None, w2_scale=None,
                 streams=None) -> torch.Tensor:
-        """One layer. ``streams=(compute, comm)`` runs plan/dispatch/combine on comm and the FFN
-        on compute, ordered by events; None runs everything on the current stream."""
+        """One layer. w1 / w2 come from prepare_weights(). ``streams=(compute, comm)`` runs
+        plan/dispatch/combine on comm and the FFN on compute, ordered by events; None runs
+        everything on the current stream."""
         if topk_idx.dtype != torch.int32:
             topk_idx = topk_idx.to(torch.int32)
         epoch = self.next_epoch()
@@ -270,5 +299,10 @@ def stream_moe(x, topk_idx, topk_weights, w1_local, w2_local, *, expert_begin=0,
         layer = StreamMoE(T, H, twoI // 2, K, E, expert_begin=expert_begin, tile=tile,
                           dtype="fp8" if fp8 else "bf16", device=x.device)
         _LAYERS[key] = layer
-    out = layer.forward(x, topk_idx, topk_weights, w1_local, w2_local, w1_scale, w2_scale, streams)
+    wkey = (w1_local.data_ptr(), w1_local._version, w2_local.data_ptr(), w2_local._version)
+    if getattr(layer, "_wkey", None) != wkey:
+        layer._wkey = wkey
+        layer._w = layer.prepare_weights(w1_local, w2_local)
+    w1p, w2p = layer._w
+    out = layer.forward(x, topk_idx, topk_weights, w1p, w2p, w1_scale, w2_scale, streams)
     return out.clone()

@@ -55,6 +55,12 @@ enum {
   MOE_ERR_TIMEOUT = 4      /* a ready-flag wait on the device ran out of time */
 };
 
+/* Weight layouts (moe_tile_config.weight_layout). */
+enum {
+  MOE_WEIGHTS_ROW_MAJOR = 0,  /* w[E][rows][K] as described above */
+  MOE_WEIGHTS_MFMA_TILED = 1  /* the same values permuted by moe_pack_weights */
+};
+
 /* Storage types of activations and weights. */
 enum {
   MOE_BF16 = 0,          /* bf16 activations and weights */
@@ -94,10 +100,12 @@ typedef struct moe_plan_t {
  * Pass NULL, or zero fields, for the built-in choice.
  */
 typedef struct moe_tile_config {
-  int32_t block_n;          /* N columns per work unit: 128 or 256 (0 = auto) */
+  int32_t block_n;          /* N columns per work unit: 128, 256 or 512 (0 = auto) */
   int32_t gemm_workgroups;  /* persistent GEMM grid size (0 = one per CU) */
   uint32_t spin_timeout_us; /* bound on one ready-flag wait (0 = 2 000 000 us) */
-  int32_t reserved;
+  int32_t unit_order;       /* work-unit walk: 1 = pool tile major, 2 = expert then N block
+                               (0 = auto) */
+  int32_t weight_layout;    /* MOE_WEIGHTS_ROW_MAJOR or MOE_WEIGHTS_MFMA_TILED (w1 and w2) */
 } moe_tile_config;
 
 /* Host-only size helpers (no device access). */
@@ -163,7 +171,8 @@ MOE355_API int moe_dispatch(const void* x, int32_t H, int32_t act_dtype, const m
  * computed; a plan that needs more records MOE_ERR_INVALID.
  * Errors: MOE_ERR_INVALID (null pointers, bad dtype, epoch 0, small workspace,
  * pool_rows not a multiple of tile), MOE_ERR_UNSUPPORTED (bf16: H % 128 or
- * I % 64 nonzero; fp8: H % 128 or I % 128 nonzero, or tile < 64).
+ * I % 64 nonzero; fp8: H % 256 or I % 128 nonzero, or tile < 64; tiled weights:
+ * bf16 with tile 64 or 128, H % 512 == 0 and I % 256 == 0 only).
  */
 MOE355_API int moe_expert_ffn(const moe_plan_t* plan, int32_t pool_rows, const void* pool,
                               const float* pool_s, const void* w1, const float* w1_s, const void* w2,
@@ -183,6 +192,25 @@ MOE355_API int moe_expert_ffn(const moe_plan_t* plan, int32_t pool_rows, const v
  */
 MOE355_API int moe_combine(const void* y_pool, int32_t pool_rows, const float* topk_weights,
                            const moe_plan_t* plan, int32_t H, void* out, void* stream);
+
+/*
+ * Load-time weight permutation for the expert GEMMs (callers that cannot keep a
+ * second copy of the weights use row-major weights instead). Copies w (device,
+ * [E][rows][K] row-major, bf16 or e4m3 per dtype) into out (device, same size,
+ * must not overlap w) in MFMA fragment order, so that every weight-fragment load
+ * of the GEMM reads 1 KiB of contiguous memory:
+ *   bf16: for each expert, 16-row x 32-column tiles (row block rb, K block kb) at
+ *         byte ((rb * K/32) + kb) * 1024; lane l (0..63) of a tile holds the 8
+ *         values w[rb*16 + l%16][kb*32 + 8*(l/16) ..+8] at byte l*16.
+ *   fp8:  16 x 128 tiles at ((rb * K/128) + kb) * 2048; half h (0,1) of lane l at
+ *         byte h*1024 + l*16 holds w[rb*16 + l%16][kb*128 + 32*(l/16) + 16h ..+16].
+ * Values are moved, never changed. Use with moe_tile_config.weight_layout =
+ * MOE_WEIGHTS_MFMA_TILED. Scales (fp8) keep their layout.
+ * Errors: MOE_ERR_INVALID (null pointers, E/rows/K < 1, bad dtype),
+ * MOE_ERR_UNSUPPORTED (rows % 16 != 0, K % 32 != 0 (bf16) or % 128 (fp8)).
+ */
+MOE355_API int moe_pack_weights(const void* w, int32_t E, int32_t rows, int32_t K, int32_t dtype, void* out,
+                                void* stream);
 
 /* Waits for `stream`, returns the first error recorded on the device in the
  * workspace since the last call (MOE_OK if none) and clears it. */

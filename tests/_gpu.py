@@ -41,7 +41,10 @@ def make_layer(shape, **kw):
 
 
 def run_layer(layer, d, streams=None):
-    out = layer.forward(d["x"], d["idx"], d["w"], d["w1"], d["w2"], d["w1s"], d["w2s"], streams)
+    if getattr(layer, "_test_w", None) is None:
+        layer._test_w = layer.prepare_weights(d["w1"], d["w2"])
+    w1, w2 = layer._test_w
+    out = layer.forward(d["x"], d["idx"], d["w"], w1, w2, d["w1s"], d["w2s"], streams)
     torch.cuda.synchronize()
     rc = moe.moe_get_error(layer.ws)
     assert rc == 0, f"device error {rc}"

@@ -28,7 +28,7 @@ def lib():
 def test_header_declares_the_four_calls():
     names = set(declared_symbols())
     assert {"moe_plan", "moe_dispatch", "moe_expert_ffn", "moe_combine"} <= names
-    assert len(names) == 10
+    assert len(names) == 11
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -139,8 +139,12 @@ def test_ffn_validation(lib):
     assert call(dtype=1) == 1                      # fp8 without scales
     assert call(scales=(v[5], None, None)) == 1    # bf16 with scales
     assert call(ws=1024) == 1                      # small workspace
-    cfg = _abi.TileConfig(192, 0, 0, 0)
-    assert call(cfg=ctypes.byref(cfg)) == 1        # block_n must be 128 or 256
+    cfg = _abi.TileConfig(192, 0, 0, 0, 0)
+    assert call(cfg=ctypes.byref(cfg)) == 1        # block_n must be 128, 256 or 512
+    cfg = _abi.TileConfig(0, 0, 0, 0, 3)
+    assert call(cfg=ctypes.byref(cfg)) == 1        # unknown weight layout
+    cfg = _abi.TileConfig(0, 0, 0, 0, 1)
+    assert call(cfg=ctypes.byref(cfg)) == 2        # tiled weights need the big-tile shapes
 
 
 def test_combine_validation(lib):
@@ -149,6 +153,16 @@ def test_combine_validation(lib):
     assert lib.moe_combine(None, 248, W, ctypes.byref(p), 128, OUT, None) == 1
     assert lib.moe_combine(Y, -1, W, ctypes.byref(p), 128, OUT, None) == 1
     assert lib.moe_combine(Y, 248, W, ctypes.byref(p), 100, OUT, None) == 2
+
+
+def test_pack_weights_validation(lib):
+    W, OUT = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x100000000)
+    assert lib.moe_pack_weights(None, 1, 16, 32, 0, OUT, None) == 1
+    assert lib.moe_pack_weights(W, 1, 16, 32, 9, OUT, None) == 1
+    assert lib.moe_pack_weights(W, 1, 24, 32, 0, OUT, None) == 2      # rows % 16
+    assert lib.moe_pack_weights(W, 1, 16, 48, 0, OUT, None) == 2      # bf16 K % 32
+    assert lib.moe_pack_weights(W, 1, 16, 64, 1, OUT, None) == 2      # fp8 K % 128
+    assert lib.moe_pack_weights(W, 4, 64, 256, 0, ctypes.c_void_p(0x10100), None) == 1  # overlap
 
 
 def test_get_error_validation(lib):

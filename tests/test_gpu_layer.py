@@ -22,6 +22,9 @@ FULL_COMPARE = [
     MoEConfig("ragged_t64", 517, 512, 320, 7, 2, 4, 2, 64),         # experts 2..5 local
     MoEConfig("t128_bn128", 1500, 640, 192, 5, 0, 5, 2, 128),       # H % 256 != 0, I % 128 != 0
     MoEConfig("t16_k16", 64, 256, 128, 20, 0, 20, 16, 16),
+    MoEConfig("mix_bigY", 900, 1024, 384, 6, 0, 6, 2, 128),        # GEMM A general, GEMM Y big-tile
+    MoEConfig("mix_bigA", 700, 640, 256, 5, 0, 5, 3, 64),          # GEMM A big-tile, GEMM Y general
+    MoEConfig("big_both", 1200, 1024, 512, 9, 0, 9, 4, 128),
     MoEConfig("fp8_t64", 300, 512, 256, 6, 0, 6, 2, 64, "fp8"),
     MoEConfig("fp8_t128", 700, 1024, 384, 10, 1, 8, 4, 128, "fp8"),
 ]
@@ -104,3 +107,19 @@ def test_layer_polled_pool_size_matches_bound():
     b = run_layer(small, d)
     assert small.pool.shape[0] == P < big.pool.shape[0]
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["decode", "big_both"])
+def test_layer_row_major_weights_on_big_tiles(name):
+    # the big-tile kernel also reads row-major weights; same tolerance as the tiled path
+    cfg = CONFIGS[1] if name == "decode" else next(c for c in FULL_COMPARE if c.name == name)
+    inp = make_inputs(cfg)
+    d = dev_inputs(inp)
+    layer = make_layer(cfg, weight_layout="row_major")
+    assert not layer.tiled
+    say("layer row-major weights", cfg.name)
+    out = run_layer(layer, d)
+    ref = oracle.moe_layer(inp)
+    err = rel_err(out_rows_f64(out), ref.out)
+    print(f"{cfg.name} row-major: max-norm rel err {err:.3e}")
+    assert err <= TOL[cfg.dtype]
