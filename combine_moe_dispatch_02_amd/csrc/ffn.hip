@@ -56,7 +56,7 @@ struct FfnArgs {
   int32_t ktiles;            // tiled weights: K tiles per 16-row block (K/32 bf16, K/128 fp8)
   int32_t tile_shift;
   int32_t max_tiles;         // pool_rows / tile: tiles the buffers hold
-  int32_t unit_order;        // 1: tile-major (m, j); 2: expert-major, N block outer
+  int32_t unit_order;        // 1: tile-major (m, j); 2: expert, N block, tile; 3: expert, N pair, tile
   int32_t n_experts;
   const int32_t* offsets;
   const int32_t* num_tiles;
@@ -78,11 +78,12 @@ __device__ inline float silu_mul(float g, float u) { return g / (1.0f + __expf(-
 // Unit u -> (pool tile m, N block j). Order 1 walks tiles, N blocks inside a
 // tile (the pool tile is reused from L2 by its N blocks). Order 2 walks
 // experts, then N blocks, then the expert's tiles, so units that run together
-// stream the same weight panel. Persistent workgroups are dealt to XCDs
+// stream the same weight panel. Order 3 walks experts, then pairs of N blocks,
+// then the expert's tiles with both blocks of the pair back to back. Persistent workgroups are dealt to XCDs
 // round-robin by the dispatcher (workgroup g runs on XCD g % 8), so slot(g)
 // gives each XCD a contiguous run of units and its L2 sees the shared panel.
 __device__ inline void unit_coords(const FfnArgs& a, int u, int order, int& m, int& j) {
-  if (order != 2) {
+  if (order == 1) {
     m = u / a.n_units;
     j = u - m * a.n_units;
     return;
@@ -96,8 +97,17 @@ __device__ inline void unit_coords(const FfnArgs& a, int u, int order, int& m, i
   const int t0 = a.offsets[lo] >> a.tile_shift;
   const int te = (a.offsets[lo + 1] >> a.tile_shift) - t0;
   const int local = u - t0 * a.n_units;
-  j = local / te;
-  m = t0 + (local - j * te);
+  if (order == 2 || (a.n_units & 1)) {
+    j = local / te;
+    m = t0 + (local - j * te);
+  } else {
+    // order 3: N blocks in pairs, every tile of the expert inside a pair; a run of
+    // 32 units then holds ~16 tiles x 2 weight panels (fewest L2 misses per step)
+    const int jp = local / (2 * te);
+    const int r = local - jp * 2 * te;
+    m = t0 + (r >> 1);
+    j = 2 * jp + (r & 1);
+  }
 }
 
 __device__ inline int unit_slot(int g, int G) { return (G & 7) == 0 ? (g & 7) * (G >> 3) + (g >> 3) : g; }
@@ -398,7 +408,8 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(FfnArgs a) {
 //   the same loads and the compiler's load counters stay exact.
 //   The MFMA runs transposed (weight fragment first), so a lane holds one
 //   output row and 4 consecutive output columns: 8-byte stores, one fp8 row
-//   scale per lane.
+//   scale per lane. (Staging the block through LDS for full-line stores was
+//   measured slower: its barriers cost more than the partial lines.)
 // ----------------------------------------------------------------------------
 template <int BM, int NW, bool FP8, bool GEMM_A>
 struct Big {
@@ -871,7 +882,7 @@ int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream
   a.bs_expert = (int64_t)(2 * I / 128) * (H / 128);
   a.out_groups = I / 128;
   a.wait_ready = 1;
-  a.unit_order = bn_a == 512 ? (f.unit_order ? f.unit_order : 2) : 1;
+  a.unit_order = bn_a == 512 ? (f.unit_order ? f.unit_order : 3) : 1;
   int grid = f.workgroups > 0 ? f.workgroups : device_cu_count();
   if (grid <= 0) return MOE_ERR_HIP;
   int ga = (int)std::min<int64_t>(grid, (int64_t)ntiles_cap * a.n_units);
@@ -901,7 +912,7 @@ int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream
   a.bs_ld = I / 128;
   a.bs_expert = (int64_t)(H / 128) * (I / 128);
   a.wait_ready = 0;
-  a.unit_order = bn_y == 512 ? (f.unit_order ? f.unit_order : 2) : 1;
+  a.unit_order = bn_y == 512 ? (f.unit_order ? f.unit_order : 3) : 1;
   int gy = (int)std::min<int64_t>(grid, (int64_t)ntiles_cap * a.n_units);
   if (gy < 1) gy = 1;
   a.ktiles = I / (fp8 ? 128 : 32);
