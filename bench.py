@@ -86,6 +86,75 @@ def cpu_baseline(inp, sample_tokens: int):
                       f"float64 NumPy oracle incl. weight dequantisation, {dt:.1f} s"}
 
 
+def _read_csv(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _short(name: str) -> str:
+    import re
+    import subprocess
+    try:
+        out = subprocess.run(["c++filt", name], capture_output=True, text=True).stdout.strip()
+        name = out or name
+    except OSError:
+        pass
+    return re.sub(r"moe::|\(moe::\w+\)|void |at::native::", "", name)[:70]
+
+
+def summarize_profiles(workload, trace_dir, fetch_dir, write_dir, out_dir, commands):
+    """rocprofv3 CSV output -> profiles/<kernel>_<workload>.txt and the FFN traffic JSON.
+
+    FETCH_SIZE / WRITE_SIZE (KiB per dispatch) are scaled by what they read for the
+    three 1 GiB device-to-device copies of --copy-calibration."""
+    import collections
+
+    stats = _read_csv(os.path.join(trace_dir, "run_kernel_stats.csv"))
+    per = {}
+    for d, cname in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
+        rows = [r for r in _read_csv(os.path.join(d, "run_counter_collection.csv")) if r["Counter_Name"] == cname]
+        copies = sorted((float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]),
+                        reverse=True)[:3]
+        scale = (1 << 20) / (sum(copies) / len(copies))  # KiB of a 1 GiB copy -> bytes factor
+        agg = collections.defaultdict(list)
+        for r in rows:
+            agg[r["Kernel_Name"]].append(float(r["Counter_Value"]) * 1024 * scale)
+        per[cname] = ({k: sum(v) / len(v) for k, v in agg.items()}, scale)
+    ffn = [r for r in stats if "ffn_" in r["Name"]]
+    ffn_ns = sum(float(r["AverageNs"]) for r in ffn)
+    fetch = sum(v for k, v in per["FETCH_SIZE"][0].items() if "ffn_" in k)
+    write = sum(v for k, v in per["WRITE_SIZE"][0].items() if "ffn_" in k)
+    lines = [f"# rocprofv3 summary: MoE layer, workload {workload}", "",
+             "Commands (from the repository root on one MI355X):"]
+    lines += [f"  {c}" for c in commands]
+    lines += ["", f"{'kernel':70s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} "
+              f"{'fetch_MB':>10s} {'write_MB':>10s}"]
+    for r in stats:
+        n = r["Name"]
+        fv = per["FETCH_SIZE"][0].get(n)
+        wv = per["WRITE_SIZE"][0].get(n)
+        lines.append(f"{_short(n):70s} {r['Calls']:>6s} {float(r['AverageNs'])/1e3:10.1f} "
+                     f"{float(r['MinNs'])/1e3:10.1f} {float(r['MaxNs'])/1e3:10.1f} "
+                     f"{(fv or 0)/1e6:10.1f} {(wv or 0)/1e6:10.1f}")
+    lines += ["", f"FETCH_SIZE scale (1 GiB copy): x{per['FETCH_SIZE'][1]:.3f} of the KiB reading; "
+              f"WRITE_SIZE scale: x{per['WRITE_SIZE'][1]:.3f}",
+              f"expert FFN (all ffn_ kernels of one call): {ffn_ns/1e3:.1f} us, "
+              f"HBM fetch {fetch/1e9:.3f} GB + write {write/1e9:.3f} GB per call"]
+    os.makedirs(out_dir, exist_ok=True)
+    txt = os.path.join(out_dir, f"moe_layer_{workload}.txt")
+    with open(txt, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    js = os.path.join(out_dir, f"ffn_traffic_{workload}.json")
+    with open(js, "w") as f:
+        json.dump({"workload": workload, "ffn_source_sha256_16": kernel_source_hash(),
+                   "hbm_bytes_per_ffn_call": fetch + write, "fetch_bytes": fetch, "write_bytes": write,
+                   "ffn_avg_us": ffn_ns / 1e3, "fetch_scale": per["FETCH_SIZE"][1],
+                   "write_scale": per["WRITE_SIZE"][1], "commands": commands}, f, indent=1)
+    print(txt)
+    print(js)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -100,7 +169,14 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run three 1 GiB device-to-device copies (a known-size reference for "
                          "the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/ summaries from rocprofv3 CSV output and exit (no GPU)")
+    ap.add_argument("--profile-commands", default="", help="';'-separated commands recorded in the summary")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(args.workload, *args.summarize_profiles, os.path.join(ROOT, "profiles"),
+                           [c.strip() for c in args.profile_commands.split(";") if c.strip()])
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this single-GPU "
               f"path (no sharding across GPUs is built).", file=sys.stderr)

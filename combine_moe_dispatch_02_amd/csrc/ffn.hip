@@ -443,7 +443,7 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wn = tid >> 6;
+  const int wn = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps tile offsets scalar
   const int l16 = lane & 15;
   const int lhi = lane >> 4;
 
@@ -557,6 +557,20 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
       }
     };
 
+    // one 16-byte weight fragment load (bf16): tile tn, K half kk of step ks into buffer BUF
+    auto load_b1 = [&](auto BUF, int tn, int kk, int ks) {
+      constexpr int bb = decltype(BUF)::value;
+      if constexpr (PACKED) {
+        const uint32_t rowblk = (uint32_t)((tn < TN / 2 ? rbase0 : rbase1) + (tn % (TN / 2)) * 16) >> 4;
+        const uint32_t tbase = (rowblk * (uint32_t)a.ktiles + (uint32_t)ks * 2u + (uint32_t)kk) * 1024u;
+        rb[bb][tn][kk] = __builtin_amdgcn_raw_buffer_load_b128(br, (uint32_t)lane * 16u, tbase, 0);
+      } else {
+        const uint32_t vo = tn < TN / 2 ? boff0 : boff1;
+        const uint32_t so = (uint32_t)(tn % (TN / 2)) * tstride + (uint32_t)ks * 128u + (uint32_t)kk * 64u;
+        rb[bb][tn][kk] = __builtin_amdgcn_raw_buffer_load_b128(br, vo, so, 0);
+      }
+    };
+
     f32x4_t acc[TM][TN];
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm)
@@ -627,9 +641,51 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     };
 
+    // bf16 step: 16 groups (K half kk, row tile tm) of TN MFMAs. The next step's loads
+    // are spread over the groups instead of issued as one burst (a wave issues in
+    // order, and a burst of vector loads would hold it off its MFMAs until the
+    // texture unit has taken them all): A for step ks+2 and the first K half of B for
+    // step ks+1 early, the second K half mid-step, which is also the order in which
+    // step ks+1 consumes them. LDS fragments are read one group ahead.
+    auto step_bf16 = [&](auto BUF, int ks) {
+      constexpr int bb = decltype(BUF)::value;
+      using NB = std::integral_constant<int, bb ^ 1>;
+      const int kn = ks + 1 < nk ? ks + 1 : ks;
+      const int ka = ks + 2 < nk ? ks + 2 : nk - 1;
+      const uint8_t* sa = &s_a[bb][0];
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8_t fa_cur = *reinterpret_cast<const bf16x8_t*>(sa + swz_a(l16, lhi));
+#pragma unroll
+      for (int g = 0; g < 2 * TM; ++g) {
+        const int kk = g / TM, tm = g % TM;
+        bf16x8_t fa_next = fa_cur;
+        if (g + 1 < 2 * TM) {
+          const int kk1 = (g + 1) / TM, tm1 = (g + 1) % TM;
+          fa_next = *reinterpret_cast<const bf16x8_t*>(sa + swz_a(tm1 * 16 + l16, kk1 * 4 + lhi));
+        }
+        if (g == 0) load_a(std::integral_constant<int, bb>{}, ka);
+        if (g >= 1 && g <= TN) load_b1(NB{}, g - 1, 0, kn);
+        if (g >= TM && g < TM + TN) load_b1(NB{}, g - TM, 1, kn);
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_t, rb[bb][tn][kk]), fa_cur, acc[tm][tn], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        fa_cur = fa_next;
+      }
+      store_a(std::integral_constant<int, bb ^ 1>{}, bb ^ 1);  // A(ks+1), loaded last step
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
     for (int ks = 0; ks < nk; ks += 2) {
-      step(std::integral_constant<int, 0>{}, ks);
-      step(std::integral_constant<int, 1>{}, ks + 1);
+      if constexpr (!FP8 && TM >= TN + 1) {
+        step_bf16(std::integral_constant<int, 0>{}, ks);
+        step_bf16(std::integral_constant<int, 1>{}, ks + 1);
+      } else {
+        step(std::integral_constant<int, 0>{}, ks);
+        step(std::integral_constant<int, 1>{}, ks + 1);
+      }
     }
 
     // ---------------- epilogue: lane holds row tm*16+l16, columns 4*lhi + (0..3) of each tile
