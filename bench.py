@@ -59,9 +59,13 @@ def algorithmic_work(cfg, idx_np):
     T_act = int(local.any(axis=1).sum())        # tokens with at least one local pair
     H, I, K, T = cfg.H, cfg.I, cfg.K, cfg.T
     pool_b = 2 if cfg.dtype == "bf16" else 1 + 4 / 128
+    w_b = 2 if cfg.dtype == "bf16" else 1 + 4 / (128 * 128)
     return {
         "pairs": N,
         "ffn_flops": 6.0 * N * H * I,
+        # least HBM traffic of the FFN: every local weight once, the pool rows read,
+        # h written and read back, y written
+        "ffn_bytes": cfg.num_local_experts * 3 * H * I * w_b + N * H * pool_b + 2 * N * I * pool_b + N * H * 2,
         "dispatch_bytes": T_act * H * 2 + N * H * pool_b,
         "combine_bytes": N * H * 2 + T * H * 2 + T * K * 8,
     }
@@ -274,7 +278,10 @@ def main():
 
     tokens_s = cfg.T / (ms_step * 1e-3)
     ffn_tflops = work["ffn_flops"] / (stage_ms["ffn"] * 1e-3) / 1e12
+    ffn_gbs = work["ffn_bytes"] / (stage_ms["ffn"] * 1e-3) / 1e9
     peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
+    # the FFN's bound: MFMA unless streaming its least traffic takes longer at HBM peak
+    hbm_bound = work["ffn_bytes"] / (PEAK_HBM_GBS * 1e9) > work["ffn_flops"] / (peak * 1e12)
     disp_gbs = work["dispatch_bytes"] / (stage_ms["dispatch"] * 1e-3) / 1e9
     comb_gbs = work["combine_bytes"] / (stage_ms["combine"] * 1e-3) / 1e9
     src_hash = kernel_source_hash()
@@ -298,9 +305,15 @@ def main():
                    "pool_rows": int(layer.plan.offsets[-1].item()),
                    "streams": "two (comm + compute)" if args.streams else "one",
                    "weights": "MFMA-tiled (permuted once at load time)" if layer.tiled else "row-major"},
-        "roofline": {"bound": "mfma", "kernel": "expert FFN (grouped GEMM A + Y)",
-                     "achieved": round(ffn_tflops, 1), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(ffn_tflops / peak, 4), "traffic": traffic},
+        "roofline": ({"bound": "hbm", "kernel": "expert FFN (grouped GEMM A + Y)",
+                      "achieved": round(ffn_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                      "frac": round(ffn_gbs / PEAK_HBM_GBS, 4), "traffic": traffic}
+                     if hbm_bound else
+                     {"bound": "mfma", "kernel": "expert FFN (grouped GEMM A + Y)",
+                      "achieved": round(ffn_tflops, 1), "peak": peak, "unit": "TFLOP/s",
+                      "frac": round(ffn_tflops / peak, 4), "traffic": traffic}),
+        "ffn_TFLOPs": round(ffn_tflops, 1),
+        "ffn_GBps_least_traffic": round(ffn_gbs, 1),
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "dispatch_GBps": round(disp_gbs, 1),
         "combine_GBps": round(comb_gbs, 1),
