@@ -34,6 +34,7 @@ namespace moe {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x8_t __attribute__((ext_vector_type(8)));
 
 struct FfnArgs {
   const uint8_t* A;          // pool (GEMM A) or h (GEMM Y): [rows][Kdim] elements
@@ -427,6 +428,10 @@ struct Big {
   static constexpr int kALoads = (kAChunks + kThreads - 1) / kThreads;
 };
 
+// s_waitcnt vmcnt(0), the other counters left alone (LDS-DMA loads have no
+// register result for the compiler to wait on)
+__device__ inline void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ inline uint32_t swz_a(int r, int c) {
   // 8 consecutive rows reading one chunk column hit 8 distinct 16-byte bank groups
   return (uint32_t)(r * 128 + ((c ^ (r & 7)) << 4));
@@ -486,6 +491,9 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
     }
     const float* bsx = nullptr;
     if constexpr (FP8) bsx = a.B_s + (int64_t)e * a.bs_expert;
+    const __amdgpu_buffer_rsrc_t bsr = make_rsrc(bsx, FP8 ? (uint32_t)(a.bs_expert * 4) : 0u);
+    // fp8 weight tile halves [buffer][tile][half] (16 bytes each: a 32-byte MFMA operand)
+    u32x4 rbh[FP8 ? 2 : 1][FP8 ? TN : 1][2];
 
     // weight fragments [buffer][tile]: bf16 two 16-byte K halves, fp8 one 32-byte tuple
     u32x4 rb[2][TN][FP8 ? 1 : 2];
@@ -571,6 +579,41 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
       }
     };
 
+    auto load_b8h = [&](auto BUF, int tn, int hf, int ks) {
+      constexpr int bb = decltype(BUF)::value;
+      const uint32_t rowblk = (uint32_t)((tn < TN / 2 ? rbase0 : rbase1) + (tn % (TN / 2)) * 16) >> 4;
+      const uint32_t tbase = (rowblk * (uint32_t)a.ktiles + (uint32_t)ks) * 2048u + (uint32_t)hf * 1024u;
+      rbh[bb][tn][hf] = __builtin_amdgcn_raw_buffer_load_b128(br, (uint32_t)lane * 16u, tbase, 0);
+    };
+    // fp8: the A rows of step ks into LDS stage ST by LDS-DMA (row r at r*128, chunk c
+    // at slot c ^ (r & 7): lane i of a 1 KiB load fetches row i/8, chunk (i%8)^(i/8)),
+    // and the rows' activation scales into ras[0] (stored to LDS before the barrier)
+    auto dma_a = [&](auto STAGE, int ks) {
+      constexpr int st = decltype(STAGE)::value;
+#pragma unroll
+      for (int i = 0; i < C::kAStage / 1024 / NW; ++i) {
+        const int q = wn * (C::kAStage / 1024 / NW) + i;
+        const uint32_t off = (uint32_t)(q * 8 + (lane >> 3)) * (uint32_t)a.lda +
+                             (uint32_t)((lane & 7) ^ (lane >> 3)) * 16u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ar, (__attribute__((address_space(3))) void*)(&s_a[st][0] + q * 1024), 16, off, (uint32_t)ks * 128u, 0, 0);
+      }
+      // branch-free (a branch here would split the step into blocks, and the compiler
+      // then hoists every LDS read of the step above its MFMAs): threads past the
+      // tile's rows read, and later store, the last row's scale again
+      ras[0] = a.A_s[(int64_t)(m0 + min(tid, BM - 1)) * a.s_kblocks + ks];
+    };
+    auto load_sb = [&](auto BUF, int ks) {
+      constexpr int bb = decltype(BUF)::value;
+      sbn[bb][0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+          bsr, 0u, (uint32_t)((rbase0 >> 7) * a.bs_ld + ks) * 4u, 0));
+      sbn[bb][1] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+          bsr, 0u, (uint32_t)((rbase1 >> 7) * a.bs_ld + ks) * 4u, 0));
+    };
+    float ap[FP8 ? TM : 1];   // fp8: the activation scale acc is expressed in, per row tile
+    float sbq[2] = {1.f, 1.f};  // fp8: the weight scales acc is expressed in
+#pragma unroll
+    for (int tm = 0; tm < (FP8 ? TM : 1); ++tm) ap[tm] = 1.f;
     f32x4_t acc[TM][TN];
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm)
@@ -582,10 +625,22 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
 
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    load_b(I0{}, 0);
-    load_a(I0{}, 0);
-    load_a(I1{}, nk > 1 ? 1 : 0);
-    store_a(I0{}, 0);
+    if constexpr (FP8 && PACKED) {
+      dma_a(I0{}, 0);
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        load_b8h(I0{}, tn, 0, 0);
+        load_b8h(I0{}, tn, 1, 0);
+      }
+      load_sb(I0{}, 0);
+      wait_vm0();
+      s_as[0][min(tid, BM - 1)] = ras[0];
+    } else {
+      load_b(I0{}, 0);
+      load_a(I0{}, 0);
+      load_a(I1{}, nk > 1 ? 1 : 0);
+      store_a(I0{}, 0);
+    }
     __syncthreads();
 
     auto step = [&](auto BUF, int ks) {
@@ -641,6 +696,64 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     };
 
+    // fp8 step: 8 groups (row tile tm) of TN 16x16x128 MFMAs, one K block per step.
+    // The accumulator is held in units of the current block's scale a_s[row] *
+    // b_s[column block]: each group first rescales its TN tiles by old/new (the old
+    // activation scale kept per lane in ap[], the weight scales per wave), then
+    // accumulates the block's code product in place. The next step's 8 weight loads
+    // and 2 weight-scale loads go out over the first groups (all of them are needed
+    // at the next step's first group); A for step ks+2 in group 0.
+    auto step_fp8 = [&](auto BUF, int ks) {
+      constexpr int bb = decltype(BUF)::value;
+      using NB = std::integral_constant<int, bb ^ 1>;
+      const int kn = ks + 1 < nk ? ks + 1 : ks;
+      const uint8_t* sa = &s_a[bb][0];
+      __builtin_amdgcn_sched_barrier(0);
+      // weight part of old/new, uniform over the wave (acc is zero at step 0)
+      const float sbc0 = sbn[bb][0], sbc1 = sbn[bb][1];
+      const float wr0 = sbq[0] * __builtin_amdgcn_rcpf(sbc0);
+      const float wr1 = sbq[1] * __builtin_amdgcn_rcpf(sbc1);
+      auto rd_a = [&](int tm) {
+        const int r = tm * 16 + l16;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(sa + swz_a(r, 2 * lhi));
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(sa + swz_a(r, 2 * lhi + 1));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+        // the group's A fragment: its LDS latency is covered by the rescale below
+        const u32x8_t fa_cur = rd_a(tm);
+        if (tm == 0) {
+          dma_a(NB{}, kn);
+          load_sb(NB{}, kn);
+        }
+        if (tm < TN) {
+          load_b8h(NB{}, tm, 0, kn);
+          load_b8h(NB{}, tm, 1, kn);
+        }
+        const float sac = s_as[bb][tm * 16 + l16];
+        const float ar = ap[tm] * __builtin_amdgcn_rcpf(sac);
+        ap[tm] = sac;
+        const float r0 = ar * wr0, r1 = ar * wr1;
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          acc[tm][tn] *= tn < TN / 2 ? r0 : r1;
+          const u32x8_t fb = __builtin_shufflevector(rbh[bb][tn][0], rbh[bb][tn][1], 0, 1, 2, 3, 4, 5, 6, 7);
+          acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              __builtin_bit_cast(i32x8_t, fb), __builtin_bit_cast(i32x8_t, fa_cur), acc[tm][tn], 0, 0, 0, 127, 0, 127);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      sbq[0] = sbc0;
+      sbq[1] = sbc1;
+      // every load of this step is in: the next step's A rows (LDS-DMA, which no
+      // register dependency waits for), its weights and scales
+      wait_vm0();
+      s_as[bb ^ 1][min(tid, BM - 1)] = ras[0];
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
     // bf16 step: 16 groups (K half kk, row tile tm) of TN MFMAs. The next step's loads
     // are spread over the groups instead of issued as one burst (a wave issues in
     // order, and a burst of vector loads would hold it off its MFMAs until the
@@ -679,7 +792,10 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
     };
 
     for (int ks = 0; ks < nk; ks += 2) {
-      if constexpr (!FP8 && TM >= TN + 1) {
+      if constexpr (FP8 && PACKED) {
+        step_fp8(std::integral_constant<int, 0>{}, ks);
+        step_fp8(std::integral_constant<int, 1>{}, ks + 1);
+      } else if constexpr (!FP8 && TM >= TN + 1) {
         step_bf16(std::integral_constant<int, 0>{}, ks);
         step_bf16(std::integral_constant<int, 1>{}, ks + 1);
       } else {
@@ -689,7 +805,12 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
     }
 
     // ---------------- epilogue: lane holds row tm*16+l16, columns 4*lhi + (0..3) of each tile
-    if constexpr (FP8) {
+    if constexpr (FP8 && PACKED) {
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) acc[tm][tn] *= ap[tm] * sbq[tn < TN / 2 ? 0 : 1];
+    } else if constexpr (FP8) {
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
@@ -805,11 +926,24 @@ int launch_pack_weights(const void* w, int32_t E, int32_t rows, int32_t K, int32
 // ----------------------------------------------------------------------------
 // host side
 // ----------------------------------------------------------------------------
+// The big-tile kernel wants whole 256 (gate) + 256 (up) and 512-column units and an
+// even number of 128-byte K steps; in fp8 it reads tiled weights only, at tile 128.
+static bool big_a_ok(int32_t H, int32_t I, int32_t dtype, int32_t tile) {
+  if (dtype == MOE_FP8_E4M3_G128) return tile == 128 && I % 256 == 0 && H % 256 == 0;
+  return dtype == MOE_BF16 && (tile == 64 || tile == 128) && I % 256 == 0 && H % 128 == 0;
+}
+static bool big_y_ok(int32_t H, int32_t I, int32_t dtype, int32_t tile) {
+  if (dtype == MOE_FP8_E4M3_G128) return tile == 128 && H % 512 == 0 && I % 256 == 0;
+  return dtype == MOE_BF16 && (tile == 64 || tile == 128) && H % 512 == 0 && I % 128 == 0;
+}
+
 int ffn_supported(int32_t H, int32_t I, int32_t dtype, int32_t tile, int32_t block_n, int32_t weight_layout) {
   if (block_n != 0 && block_n != 128 && block_n != 256 && block_n != 512) return MOE_ERR_INVALID;
-  // the big-tile kernel wants whole 256/512-column units and an even number of 128-byte K steps
-  const bool big_a = dtype == MOE_BF16 && (tile == 64 || tile == 128) && I % 256 == 0 && H % 128 == 0;
-  const bool big_y = dtype == MOE_BF16 && (tile == 64 || tile == 128) && H % 512 == 0 && I % 128 == 0;
+  const bool big_a = big_a_ok(H, I, dtype, tile);
+  const bool big_y = big_y_ok(H, I, dtype, tile);
+  // fp8 on the big-tile kernel needs tiled weights
+  if (dtype == MOE_FP8_E4M3_G128 && block_n == 512 && weight_layout != MOE_WEIGHTS_MFMA_TILED)
+    return MOE_ERR_UNSUPPORTED;
   if (block_n == 512 && !(big_a && big_y)) return MOE_ERR_UNSUPPORTED;
   // tiled weights are read by the big-tile kernel only, so both GEMMs must take it
   if (weight_layout == MOE_WEIGHTS_MFMA_TILED && (!(big_a && big_y) || (block_n != 0 && block_n != 512)))
@@ -849,7 +983,9 @@ template <bool FP8, bool GEMM_A>
 static int launch_shape(int tile, int bn, bool packed, const FfnArgs& a, int grid, hipStream_t s) {
   if (bn == 512) {
     if constexpr (FP8) {
-      return MOE_ERR_UNSUPPORTED;  // fp8 runs on the general kernel
+      if (!packed || tile != 128) return MOE_ERR_UNSUPPORTED;  // fp8 big tiles read tiled weights
+      hipLaunchKernelGGL((ffn_big_kernel<128, kBigWaves, true, GEMM_A, true>), dim3(grid), dim3(64 * kBigWaves), 0, s, a);
+      return MOE_OK;
     } else {
       return packed ? launch_big<FP8, GEMM_A, true>(tile, a, grid, s) : launch_big<FP8, GEMM_A, false>(tile, a, grid, s);
     }
@@ -881,8 +1017,10 @@ static int launch_shape(int tile, int bn, bool packed, const FfnArgs& a, int gri
 // else the largest the general kernel takes, unless overridden.
 static void pick_block_n(const FfnLaunch& f, int tile, int& bn_a, int& bn_y) {
   const bool fp8 = f.dtype == MOE_FP8_E4M3_G128;
-  const bool big_a = !fp8 && (tile == 64 || tile == 128) && f.I % 256 == 0 && f.H % 128 == 0;
-  const bool big_y = !fp8 && (tile == 64 || tile == 128) && f.H % 512 == 0 && f.I % 128 == 0;
+  const bool tiled = f.weight_layout == MOE_WEIGHTS_MFMA_TILED;
+  // fp8 reaches the big-tile kernel only with tiled weights
+  const bool big_a = big_a_ok(f.H, f.I, f.dtype, tile) && (!fp8 || tiled);
+  const bool big_y = big_y_ok(f.H, f.I, f.dtype, tile) && (!fp8 || tiled);
   if (f.block_n == 512) {
     bn_a = bn_y = 512;
     return;

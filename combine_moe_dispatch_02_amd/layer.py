@@ -215,7 +215,10 @@ class StreamMoE:
         self.T, self.H, self.I, self.K = T, H, I, K
         self.E_local, self.expert_begin, self.tile = num_local_experts, expert_begin, tile
         self.dtype = "fp8" if _dtype_code(dtype) == MOE_FP8_E4M3_G128 else "bf16"
-        tiled_ok = (self.dtype == "bf16" and tile in (64, 128) and I % 256 == 0 and H % 512 == 0
+        # tiled weights feed the big-tile kernel, which needs whole 512-column blocks
+        # (bf16: tile 64 or 128; fp8: tile 128)
+        tiles_ok = tile in (64, 128) if self.dtype == "bf16" else tile == 128
+        tiled_ok = (tiles_ok and I % 256 == 0 and H % 512 == 0
                     and (cfg is None or cfg.block_n in (0, 512)))
         if weight_layout == "tiled" and not tiled_ok:
             raise MoeError("StreamMoE", _abi.MOE_ERR_UNSUPPORTED)

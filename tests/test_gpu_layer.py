@@ -27,6 +27,7 @@ FULL_COMPARE = [
     MoEConfig("big_both", 1200, 1024, 512, 9, 0, 9, 4, 128),
     MoEConfig("fp8_t64", 300, 512, 256, 6, 0, 6, 2, 64, "fp8"),
     MoEConfig("fp8_t128", 700, 1024, 384, 10, 1, 8, 4, 128, "fp8"),
+    MoEConfig("fp8_big", 600, 1024, 512, 6, 0, 6, 2, 128, "fp8"),     # fp8 big-tile kernel, tiled weights
 ]
 
 
@@ -109,9 +110,10 @@ def test_layer_polled_pool_size_matches_bound():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-@pytest.mark.parametrize("name", ["decode", "big_both"])
+@pytest.mark.parametrize("name", ["decode", "big_both", "fp8_big"])
 def test_layer_row_major_weights_on_big_tiles(name):
-    # the big-tile kernel also reads row-major weights; same tolerance as the tiled path
+    # the big-tile kernel also reads row-major weights (fp8: row-major weights take the
+    # general kernel); same tolerance as the tiled path
     cfg = CONFIGS[1] if name == "decode" else next(c for c in FULL_COMPARE if c.name == name)
     inp = make_inputs(cfg)
     d = dev_inputs(inp)
