@@ -443,6 +443,7 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
   constexpr int TN = C::kTN, TM = C::kTM, KS = C::kKS, HALF = C::kHalf;
   __shared__ __attribute__((aligned(16))) uint8_t s_a[2][C::kAStage];
   __shared__ float s_as[2][FP8 ? BM : 1];
+  __shared__ float s_rt[2][FP8 && PACKED ? BM : 1];  // fp8: a_s(previous step) / a_s(this step) per row
   __shared__ float s_red[FP8 && GEMM_A ? NW : 1][FP8 && GEMM_A ? BM : 1];
   __shared__ int s_go;
 
@@ -610,10 +611,18 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
       sbn[bb][1] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
           bsr, 0u, (uint32_t)((rbase1 >> 7) * a.bs_ld + ks) * 4u, 0));
     };
-    float ap[FP8 ? TM : 1];   // fp8: the activation scale acc is expressed in, per row tile
     float sbq[2] = {1.f, 1.f};  // fp8: the weight scales acc is expressed in
-#pragma unroll
-    for (int tm = 0; tm < (FP8 ? TM : 1); ++tm) ap[tm] = 1.f;
+    // fp8: thread t stages row min(t, BM-1)'s activation scale of the next step, and
+    // the ratio previous / next that the step multiplies acc by (threads past the
+    // tile's rows write the same values for the last row again)
+    float pa = 1.f;
+    auto stage_scale = [&](auto STAGE) {
+      constexpr int st = decltype(STAGE)::value;
+      const float ns = ras[0];
+      s_as[st][min(tid, BM - 1)] = ns;
+      s_rt[st][min(tid, BM - 1)] = pa / ns;
+      pa = ns;
+    };
     f32x4_t acc[TM][TN];
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm)
@@ -634,7 +643,8 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
       }
       load_sb(I0{}, 0);
       wait_vm0();
-      s_as[0][min(tid, BM - 1)] = ras[0];
+      pa = ras[0];        // ratio 1 at step 0 (acc is zero there anyway)
+      stage_scale(I0{});
     } else {
       load_b(I0{}, 0);
       load_a(I0{}, 0);
@@ -719,10 +729,17 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
         const u32x4 hi = *reinterpret_cast<const u32x4*>(sa + swz_a(r, 2 * lhi + 1));
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       };
+      // fragments and row ratios are read one group ahead
+      u32x8_t fa_cur = rd_a(0);
+      float rt_cur = s_rt[bb][l16];
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
-        // the group's A fragment: its LDS latency is covered by the rescale below
-        const u32x8_t fa_cur = rd_a(tm);
+        u32x8_t fa_next = fa_cur;
+        float rt_next = rt_cur;
+        if (tm + 1 < TM) {
+          fa_next = rd_a(tm + 1);
+          rt_next = s_rt[bb][(tm + 1) * 16 + l16];
+        }
         if (tm == 0) {
           dma_a(NB{}, kn);
           load_sb(NB{}, kn);
@@ -731,10 +748,7 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
           load_b8h(NB{}, tm, 0, kn);
           load_b8h(NB{}, tm, 1, kn);
         }
-        const float sac = s_as[bb][tm * 16 + l16];
-        const float ar = ap[tm] * __builtin_amdgcn_rcpf(sac);
-        ap[tm] = sac;
-        const float r0 = ar * wr0, r1 = ar * wr1;
+        const float r0 = rt_cur * wr0, r1 = rt_cur * wr1;
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
           acc[tm][tn] *= tn < TN / 2 ? r0 : r1;
@@ -743,13 +757,15 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
               __builtin_bit_cast(i32x8_t, fb), __builtin_bit_cast(i32x8_t, fa_cur), acc[tm][tn], 0, 0, 0, 127, 0, 127);
         }
         __builtin_amdgcn_sched_barrier(0);
+        fa_cur = fa_next;
+        rt_cur = rt_next;
       }
       sbq[0] = sbc0;
       sbq[1] = sbc1;
       // every load of this step is in: the next step's A rows (LDS-DMA, which no
       // register dependency waits for), its weights and scales
       wait_vm0();
-      s_as[bb ^ 1][min(tid, BM - 1)] = ras[0];
+      stage_scale(NB{});
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -806,10 +822,13 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
 
     // ---------------- epilogue: lane holds row tm*16+l16, columns 4*lhi + (0..3) of each tile
     if constexpr (FP8 && PACKED) {
+      // the last step's scales (its stage, and the reloaded copy in the other one)
 #pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
+      for (int tm = 0; tm < TM; ++tm) {
+        const float sl = s_as[(nk - 1) & 1][tm * 16 + l16];
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) acc[tm][tn] *= ap[tm] * sbq[tn < TN / 2 ? 0 : 1];
+        for (int tn = 0; tn < TN; ++tn) acc[tm][tn] *= sl * sbq[tn < TN / 2 ? 0 : 1];
+      }
     } else if constexpr (FP8) {
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
