@@ -71,7 +71,8 @@ struct FfnArgs {
 
 __device__ inline uint32_t swz(int row, int chunk) { return (uint32_t)(row * 128 + ((chunk ^ (row & 7)) << 4)); }
 
-__device__ inline float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+// silu(g) * u with the hardware reciprocal (about 1 ulp) in place of a division
+__device__ inline float silu_mul(float g, float u) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u; }
 
 // ----------------------------------------------------------------------------
 // Unit schedule shared by the kernels
@@ -365,11 +366,12 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(FfnArgs a) {
 #pragma unroll
             for (int w2 = 0; w2 < WN; ++w2) mx = fmaxf(mx, s_red[w2][rl]);
             const float sc = mx > 0.f ? mx / 448.0f : 1.0f;
+            const float inv = 1.0f / sc;  // h codes: h * (1/scale), one division per row
             const int row = m0 + rl;
 #pragma unroll
             for (int tn = 0; tn < G::kTN / 2; ++tn) {
               const int col = hcol0 + tn * 16 + l16;
-              a.out[(int64_t)row * a.ldo + col] = (uint8_t)e4m3_from_f32(hv[tm][tn][i] / sc);
+              a.out[(int64_t)row * a.ldo + col] = (uint8_t)e4m3_from_f32(hv[tm][tn][i] * inv);
             }
             if (wn == 0 && l16 == 0) a.out_s[(int64_t)row * a.out_groups + ((j * (BN / 2)) >> 7)] = sc;
           }
@@ -444,6 +446,8 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_a[2][C::kAStage];
   __shared__ float s_as[2][FP8 ? BM : 1];
   __shared__ float s_rt[2][FP8 && PACKED ? BM : 1];  // fp8: a_s(previous step) / a_s(this step) per row
+  // GEMM Y: each wave's 64 rows x 64 columns of bf16 output on their way out
+  __shared__ __attribute__((aligned(16))) uint8_t s_ystage[GEMM_A ? 16 : NW * 8192];
   __shared__ float s_red[FP8 && GEMM_A ? NW : 1][FP8 && GEMM_A ? BM : 1];
   __shared__ int s_go;
 
@@ -879,29 +883,48 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
 #pragma unroll
           for (int g = 1; g < GW; ++g) mx = fmaxf(mx, s_red[w0 + g][rl]);
           const float sc = mx > 0.f ? mx / 448.0f : 1.0f;
+          const float inv = 1.0f / sc;  // h codes: h * (1/scale), one division per row
           const int row = m0 + rl;
           uint8_t* orow = a.out + (int64_t)row * a.ldo;
 #pragma unroll
           for (int tn = 0; tn < TN / 2; ++tn)
             *reinterpret_cast<uint32_t*>(orow + hcol0 + tn * 16) =
-                pack_e4m3x4(acc[tm][tn][0] / sc, acc[tm][tn][1] / sc, acc[tm][tn][2] / sc, acc[tm][tn][3] / sc);
+                pack_e4m3x4(acc[tm][tn][0] * inv, acc[tm][tn][1] * inv, acc[tm][tn][2] * inv, acc[tm][tn][3] * inv);
           if (wn % GW == 0 && lhi == 0)
             a.out_s[(int64_t)row * a.out_groups + ((j * 256 + wn * HALF) >> 7)] = sc;
         }
         __syncthreads();
       }
     } else {
-      const int col0 = j * 512 + wn * C::kWCols + 4 * lhi;
+      // y rows go out in whole 128-byte segments: the wave's 64 columns of 64 rows at
+      // a time are written to its own LDS region (16-byte chunks swizzled by row), then
+      // read back row-contiguous, so each 1 KiB store covers 8 full rows' segments
+      // instead of 32-byte pieces of 16 rows. The region is the wave's alone, and a
+      // wave's LDS accesses complete in order: no barrier.
+      uint8_t* st = &s_ystage[wn * 8192];
+      const int colb = (j * 512 + wn * C::kWCols) * 2;
 #pragma unroll
-      for (int tm = 0; tm < TM; ++tm) {
-        const int row = m0 + tm * 16 + l16;
-        uint8_t* orow = a.out + (int64_t)row * a.ldo;
+      for (int pass = 0; pass < BM / 64; ++pass) {
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-          u32x2 v;
-          v.x = pack_bf16x2(acc[tm][tn][0], acc[tm][tn][1]);
-          v.y = pack_bf16x2(acc[tm][tn][2], acc[tm][tn][3]);
-          *reinterpret_cast<u32x2*>(orow + (col0 + tn * 16) * 2) = v;
+        for (int t = 0; t < 4; ++t) {
+          const int tm = pass * 4 + t;
+          const int r = t * 16 + l16;
+#pragma unroll
+          for (int tn = 0; tn < TN; ++tn) {
+            u32x2 v;
+            v.x = pack_bf16x2(acc[tm][tn][0], acc[tm][tn][1]);
+            v.y = pack_bf16x2(acc[tm][tn][2], acc[tm][tn][3]);
+            const int b = tn * 32 + 8 * lhi;  // byte of the row's 128-byte segment
+            *reinterpret_cast<u32x2*>(st + r * 128 + (((b >> 4) ^ (r & 7)) << 4) + (b & 15)) = v;
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int r = q * 8 + (lane >> 3);
+          const int sl = lane & 7;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(st + r * 128 + sl * 16);
+          const int64_t row = m0 + pass * 64 + r;
+          *reinterpret_cast<u32x4*>(a.out + row * a.ldo + colb + ((sl ^ (r & 7)) << 4)) = v;
         }
       }
     }
