@@ -448,6 +448,8 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
   __shared__ float s_rt[2][FP8 && PACKED ? BM : 1];  // fp8: a_s(previous step) / a_s(this step) per row
   // GEMM Y: each wave's 64 rows x 64 columns of bf16 output on their way out
   __shared__ __attribute__((aligned(16))) uint8_t s_ystage[GEMM_A ? 16 : NW * 8192];
+  // GEMM A: the block's BM x 256 tile of h on its way out
+  __shared__ __attribute__((aligned(16))) uint8_t s_hstage[GEMM_A ? BM * (FP8 ? 256 : 512) : 16];
   __shared__ float s_red[FP8 && GEMM_A ? NW : 1][FP8 && GEMM_A ? BM : 1];
   __shared__ int s_go;
 
@@ -840,12 +842,29 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
         for (int tn = 0; tn < TN; ++tn) acc[tm][tn] *= cur_s[tm][tn < TN / 2 ? 0 : 1];
     }
     if constexpr (GEMM_A) {
-      const int hcol0 = j * 256 + wn * HALF + 4 * lhi;
+      // h leaves through LDS: the block's BM x 256 tile is staged (16-byte chunks
+      // swizzled by row), then stored as whole rows of the tile -- 512 bytes (bf16)
+      // or 256 bytes (e4m3) each -- instead of 32- or 16-byte pieces of 16 rows.
+      // One barrier; the stage is next written after the next unit's K loop.
+      constexpr int HROW = FP8 ? 256 : 512;           // bytes of a tile row of h
+      const int hb0 = (wn * HALF + 4 * lhi) * (FP8 ? 1 : 2);  // this lane's first byte in it
+      auto hst = [&](int r, int b) {                   // staging address of row r, byte b
+        return &s_hstage[r * HROW + ((((b >> 4) ^ (r & 7))) << 4) + (b & 15)];
+      };
+      auto hstore = [&]() {
+        constexpr int LPR = HROW / 16;                 // lanes per row
+#pragma unroll
+        for (int q = 0; q < BM * HROW / 1024 / NW; ++q) {
+          const int r = (wn * (BM * HROW / 1024 / NW) + q) * (64 / LPR) + lane / LPR;
+          const int sl = lane % LPR;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(&s_hstage[r * HROW + sl * 16]);
+          *reinterpret_cast<u32x4*>(a.out + (int64_t)(m0 + r) * a.ldo + j * HROW + ((sl ^ (r & 7)) << 4)) = v;
+        }
+      };
       if constexpr (!FP8) {
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) {
-          const int row = m0 + tm * 16 + l16;
-          uint8_t* orow = a.out + (int64_t)row * a.ldo;
+          const int r = tm * 16 + l16;
 #pragma unroll
           for (int tn = 0; tn < TN / 2; ++tn) {
             u32x2 v;
@@ -853,9 +872,11 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
                               silu_mul(acc[tm][tn][1], acc[tm][tn + TN / 2][1]));
             v.y = pack_bf16x2(silu_mul(acc[tm][tn][2], acc[tm][tn + TN / 2][2]),
                               silu_mul(acc[tm][tn][3], acc[tm][tn + TN / 2][3]));
-            *reinterpret_cast<u32x2*>(orow + (hcol0 + tn * 16) * 2) = v;
+            *reinterpret_cast<u32x2*>(hst(r, hb0 + tn * 32)) = v;
           }
         }
+        __syncthreads();
+        hstore();
       } else {
         // an h group of 128 columns = the HALF columns of 128/HALF consecutive waves
 #pragma unroll
@@ -884,16 +905,15 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
           for (int g = 1; g < GW; ++g) mx = fmaxf(mx, s_red[w0 + g][rl]);
           const float sc = mx > 0.f ? mx / 448.0f : 1.0f;
           const float inv = 1.0f / sc;  // h codes: h * (1/scale), one division per row
-          const int row = m0 + rl;
-          uint8_t* orow = a.out + (int64_t)row * a.ldo;
 #pragma unroll
           for (int tn = 0; tn < TN / 2; ++tn)
-            *reinterpret_cast<uint32_t*>(orow + hcol0 + tn * 16) =
+            *reinterpret_cast<uint32_t*>(hst(rl, hb0 + tn * 16)) =
                 pack_e4m3x4(acc[tm][tn][0] * inv, acc[tm][tn][1] * inv, acc[tm][tn][2] * inv, acc[tm][tn][3] * inv);
           if (wn % GW == 0 && lhi == 0)
-            a.out_s[(int64_t)row * a.out_groups + ((j * 256 + wn * HALF) >> 7)] = sc;
+            a.out_s[(int64_t)(m0 + rl) * a.out_groups + ((j * 256 + wn * HALF) >> 7)] = sc;
         }
-        __syncthreads();
+        __syncthreads();  // (also: every s_red read is done before the next unit writes it)
+        hstore();
       }
     } else {
       // y rows go out in whole 128-byte segments: the wave's 64 columns of 64 rows at
