@@ -10,12 +10,15 @@
 // pair. In fp8 mode each 1x128 group (16 lanes x 8 values) is quantised on the
 // way: scale = amax/448 in fp32 (1 for an all-zero group), code = e4m3(x /
 // scale) with IEEE division, round to nearest even, saturating. A wave handles
-// a run of 64/K tokens and publishes them with a single device-scope release
-// (an L2 write-back on this chip, so it is paid per run, not per row); each
-// stored pair then bumps its tile's fill counter, and the wave that completes a
-// tile's real rows stores the epoch into tile_ready with release ordering.
+// a run of 64/K tokens; a workgroup's runs are published with a single
+// device-scope release (an L2 write-back on this chip, so it is paid per
+// workgroup, not per row or per wave); each stored pair then bumps its tile's
+// fill counter, and the lane that completes a tile's real rows stores the epoch
+// into tile_ready with release ordering.
 #include "common.h"
 #include "kernels.h"
+
+#include <algorithm>
 
 namespace moe {
 
@@ -92,17 +95,23 @@ __device__ inline void dispatch_token(const DispatchArgs& a, int t, int p, uint6
   }
 }
 
-// A wave dispatches a run of `tpw` consecutive tokens (tpw * K <= 64), then
-// publishes them at once: one device-scope release for all its stores, one
-// relaxed fill count per stored pair (lane i owns pair i of the run), and the
-// wave whose count completes a tile acquires and stores the epoch (release).
-template <int CPL, bool FP8>
-__global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs a) {
+// A wave dispatches a run of `tpw` consecutive tokens (tpw * K <= 64). The block's
+// WPB waves then publish together: a barrier (every store of the block has reached
+// L2), one device-scope release by wave 0 (an L2 write-back on this chip, which is
+// what makes the rows visible to the other XCDs -- paid once per block rather than
+// once per wave: a write-back by every wave costs as much as before even when the
+// L2 is mostly clean), then wave 0 bumps the fill count of every stored pair's tile
+// (relaxed), and the lane whose count completes a tile acquires and stores the
+// epoch into tile_ready (release). The host picks the largest WPB (up to 16) that
+// still gives every CU a block.
+template <int CPL, bool FP8, int WPB>
+__global__ __launch_bounds__(64 * WPB) void dispatch_kernel(DispatchArgs a) {
   const int lane = lane_id();
+  const int w = threadIdx.x >> 6;
   const int tpw = a.tokens_per_wave;
-  const int t0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * tpw;
-  if (t0 >= a.T) return;
-  const int ntok = min(tpw, a.T - t0);
+  const int tb = blockIdx.x * WPB * tpw;  // the block's first token
+  const int t0 = tb + w * tpw;
+  const int ntok = t0 < a.T ? min(tpw, a.T - t0) : 0;
   for (int i = 0; i < ntok; ++i) {
     const int t = t0 + i;
     int p = lane < a.K ? a.pos[(int64_t)t * a.K + lane] : -1;
@@ -114,30 +123,45 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs a) {
     if (dest != 0) dispatch_token<CPL, FP8>(a, t, p, dest, lane);
   }
 
-  // publish: this wave's stores, then one fill count per stored row
+  __syncthreads();
+  if (w != 0) return;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  const int npairs = ntok * a.K;
-  int p = lane < npairs ? a.pos[(int64_t)t0 * a.K + lane] : -1;
-  if (p >= a.pool_rows) p = -1;
-  if (p >= 0) {
-    const int ti = p >> a.tile_shift;
-    const uint32_t old = __hip_atomic_fetch_add(&a.tile_fill[ti], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int e = a.tile_expert[ti];
-    const int real = min(a.tile, a.offsets[e] + a.counts[e] - (ti << a.tile_shift));
-    if ((int)old + 1 == real) {
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      __hip_atomic_store(&a.tile_ready[ti], a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  const int npairs = (min(a.T, tb + WPB * tpw) - tb) * a.K;
+  for (int q = lane; q < npairs; q += 64) {
+    int p = a.pos[(int64_t)tb * a.K + q];
+    if (p >= a.pool_rows) p = -1;
+    if (p >= 0) {
+      const int ti = p >> a.tile_shift;
+      const uint32_t old = __hip_atomic_fetch_add(&a.tile_fill[ti], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int e = a.tile_expert[ti];
+      const int real = min(a.tile, a.offsets[e] + a.counts[e] - (ti << a.tile_shift));
+      if ((int)old + 1 == real) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        __hip_atomic_store(&a.tile_ready[ti], a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   }
 }
 
-template <bool FP8>
+template <bool FP8, int WPB>
 static void launch_cpl(int cpl, dim3 grid, hipStream_t s, const DispatchArgs& a) {
   switch (cpl) {
-    case 1: hipLaunchKernelGGL((dispatch_kernel<1, FP8>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((dispatch_kernel<2, FP8>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((dispatch_kernel<4, FP8>), grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((dispatch_kernel<8, FP8>), grid, dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((dispatch_kernel<1, FP8, WPB>), grid, dim3(64 * WPB), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((dispatch_kernel<2, FP8, WPB>), grid, dim3(64 * WPB), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((dispatch_kernel<4, FP8, WPB>), grid, dim3(64 * WPB), 0, s, a); break;
+    default: hipLaunchKernelGGL((dispatch_kernel<8, FP8, WPB>), grid, dim3(64 * WPB), 0, s, a); break;
+  }
+}
+
+template <bool FP8>
+static void launch_wpb(int wpb, int cpl, int waves, hipStream_t s, const DispatchArgs& a) {
+  const dim3 grid((waves + wpb - 1) / wpb);
+  switch (wpb) {
+    case 1: launch_cpl<FP8, 1>(cpl, grid, s, a); break;
+    case 2: launch_cpl<FP8, 2>(cpl, grid, s, a); break;
+    case 4: launch_cpl<FP8, 4>(cpl, grid, s, a); break;
+    case 8: launch_cpl<FP8, 8>(cpl, grid, s, a); break;
+    default: launch_cpl<FP8, 16>(cpl, grid, s, a); break;
   }
 }
 
@@ -166,11 +190,14 @@ int launch_dispatch(const void* x, int32_t H, int32_t dtype, const moe_plan_t& p
   const int cpl = nch <= 64 ? 1 : nch <= 128 ? 2 : nch <= 256 ? 4 : 8;
   a.tokens_per_wave = 64 / p.K;
   const int waves = (p.T + a.tokens_per_wave - 1) / a.tokens_per_wave;
-  const dim3 grid((waves + 3) / 4);
+  // waves per block: the largest power of two up to 16 that leaves a block per CU
+  const int cus = std::max(1, device_cu_count());
+  int wpb = 1;
+  while (wpb < 16 && waves / (2 * wpb) >= cus) wpb *= 2;
   if (dtype == MOE_FP8_E4M3_G128)
-    launch_cpl<true>(cpl, grid, stream, a);
+    launch_wpb<true>(wpb, cpl, waves, stream, a);
   else
-    launch_cpl<false>(cpl, grid, stream, a);
+    launch_wpb<false>(wpb, cpl, waves, stream, a);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
