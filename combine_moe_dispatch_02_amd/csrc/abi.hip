@@ -136,7 +136,7 @@ MOE355_API int moe_expert_ffn(const moe_plan_t* plan, int32_t pool_rows, const v
   f.workgroups = cfg ? cfg->gemm_workgroups : 0;
   f.unit_order = cfg ? cfg->unit_order : 0;
   f.weight_layout = layout;
-  if (f.unit_order < 0 || f.unit_order > 3) return MOE_ERR_INVALID;
+  if (f.unit_order < 0 || f.unit_order > 9) return MOE_ERR_INVALID;
   const uint64_t us = (cfg && cfg->spin_timeout_us) ? cfg->spin_timeout_us : 2000000u;
   f.timeout_ticks = us * 100u;  // s_memrealtime counts at 100 MHz
   return launch_expert_ffn(f, L, static_cast<char*>(ws), static_cast<hipStream_t>(stream));

@@ -80,8 +80,9 @@ __device__ inline float silu_mul(float g, float u) { return g * __builtin_amdgcn
 // Unit u -> (pool tile m, N block j). Order 1 walks tiles, N blocks inside a
 // tile (the pool tile is reused from L2 by its N blocks). Order 2 walks
 // experts, then N blocks, then the expert's tiles, so units that run together
-// stream the same weight panel. Order 3 walks experts, then pairs of N blocks,
-// then the expert's tiles with both blocks of the pair back to back. Persistent workgroups are dealt to XCDs
+// stream the same weight panel. Order k >= 3 walks experts, then groups of k-1 N
+// blocks, then the expert's tiles with the group's blocks back to back (order 3:
+// pairs). Persistent workgroups are dealt to XCDs
 // round-robin by the dispatcher (workgroup g runs on XCD g % 8), so slot(g)
 // gives each XCD a contiguous run of units and its L2 sees the shared panel.
 __device__ inline void unit_coords(const FfnArgs& a, int u, int order, int& m, int& j) {
@@ -99,16 +100,18 @@ __device__ inline void unit_coords(const FfnArgs& a, int u, int order, int& m, i
   const int t0 = a.offsets[lo] >> a.tile_shift;
   const int te = (a.offsets[lo + 1] >> a.tile_shift) - t0;
   const int local = u - t0 * a.n_units;
-  if (order == 2 || (a.n_units & 1)) {
+  const int g = order - 1;  // order >= 3: N blocks in groups of order - 1
+  if (order == 2 || a.n_units % g != 0) {
     j = local / te;
     m = t0 + (local - j * te);
   } else {
-    // order 3: N blocks in pairs, every tile of the expert inside a pair; a run of
-    // 32 units then holds ~16 tiles x 2 weight panels (fewest L2 misses per step)
-    const int jp = local / (2 * te);
-    const int r = local - jp * 2 * te;
-    m = t0 + (r >> 1);
-    j = 2 * jp + (r & 1);
+    // N blocks in groups of g, every tile of the expert inside a group, the group's
+    // blocks back to back; with g = 2 (the default) a run of 32 units holds ~16
+    // tiles x 2 weight panels
+    const int jp = local / (g * te);
+    const int r = local - jp * g * te;
+    m = t0 + r / g;
+    j = g * jp + (r - (r / g) * g);
   }
 }
 

@@ -104,7 +104,7 @@ typedef struct moe_tile_config {
   int32_t gemm_workgroups;  /* persistent GEMM grid size (0 = one per CU) */
   uint32_t spin_timeout_us; /* bound on one ready-flag wait (0 = 2 000 000 us) */
   int32_t unit_order;       /* work-unit walk: 1 = pool tile major, 2 = expert, N block, tile,
-                               3 = expert, pair of N blocks, tile (0 = auto) */
+                               k = 3..9: expert, group of k-1 N blocks, tile (0 = auto) */
   int32_t weight_layout;    /* MOE_WEIGHTS_ROW_MAJOR or MOE_WEIGHTS_MFMA_TILED (w1 and w2) */
 } moe_tile_config;
 

@@ -145,6 +145,10 @@ def test_ffn_validation(lib):
     assert call(cfg=ctypes.byref(cfg)) == 1        # unknown weight layout
     cfg = _abi.TileConfig(0, 0, 0, 0, 1)
     assert call(cfg=ctypes.byref(cfg)) == 2        # tiled weights need the big-tile shapes
+    cfg = _abi.TileConfig(0, 0, 0, 10, 0)
+    assert call(cfg=ctypes.byref(cfg)) == 1        # unit walks are 0..9
+    cfg = _abi.TileConfig(0, -1, 0, 0, 0)
+    assert call(cfg=ctypes.byref(cfg)) == 1        # negative grid
 
 
 def test_combine_validation(lib):

@@ -125,3 +125,16 @@ def test_layer_row_major_weights_on_big_tiles(name):
     err = rel_err(out_rows_f64(out), ref.out)
     print(f"{cfg.name} row-major: max-norm rel err {err:.3e}")
     assert err <= TOL[cfg.dtype]
+
+
+@pytest.mark.parametrize("order", [1, 2, 4, 7])
+def test_layer_unit_walks_agree(order):
+    # every walk of the (tile, N block) units computes the same bits as the default
+    cfg = next(c for c in FULL_COMPARE if c.name == "big_both")
+    inp = make_inputs(cfg)
+    d = dev_inputs(inp)
+    say("unit walk", order)
+    ref = run_layer(make_layer(cfg), d).clone()
+    import combine_moe_dispatch_02_amd as moe
+    got = run_layer(make_layer(cfg, cfg=moe.TileConfig(0, 0, 0, order, 0)), d)
+    assert torch.equal(ref.view(torch.int16), got.view(torch.int16))
