@@ -107,15 +107,31 @@ __device__ inline int block_exclusive_scan4(int v[4], int* scratch) {
 }
 
 // The scan step, run by the last block of pass 1 (all 256 threads).
-__device__ void plan_scan(const PlanArgs& a, int* s_cnt, int* s_off, int* scratch) {
+__device__ void plan_scan(const PlanArgs& a, int* s_cnt, int* s_off, int* s_half, int* scratch) {
   const int tid = threadIdx.x;
   const int E = a.E;
-  // counts: reduce the columns
-  for (int e = tid; e < E; e += 256) {
+  // counts: reduce the columns. With E <= 128 two threads share an expert, each
+  // summing half of the columns (s_half keeps the first half's sum for the bases
+  // below); the loops are unrolled so that 16 column loads are in flight at a time
+  // (one load per iteration would serialise their latency).
+  const bool split = E <= 128;
+  const int half = (a.ncols + 1) >> 1;
+  for (int x = tid; x < (split ? 2 * E : E); x += 256) {
+    const int e = split ? x >> 1 : x;
+    const int c0 = split && (x & 1) ? half : 0;
+    const int c1 = split && !(x & 1) ? half : a.ncols;
     int c = 0;
-    for (int col = 0; col < a.ncols; ++col) c += a.hist[col * E + e];
-    s_cnt[e] = c;
-    a.counts[e] = c;
+#pragma unroll 16
+    for (int col = c0; col < c1; ++col) c += a.hist[col * E + e];
+    if (split) {
+      const int other = __shfl_xor(c, 1);
+      if (!(x & 1)) s_half[e] = c;
+      c += other;
+    }
+    if (!split || !(x & 1)) {
+      s_cnt[e] = c;
+      a.counts[e] = c;
+    }
   }
   __syncthreads();
   // offsets: exclusive scan of the padded counts, 4 consecutive experts per thread
@@ -140,13 +156,19 @@ __device__ void plan_scan(const PlanArgs& a, int* s_cnt, int* s_off, int* scratc
   __syncthreads();
   const int ntiles = P >> a.tile_shift;
   // per-column bases, tile owners, padding rows
-  for (int e = tid; e < E; e += 256) {
-    int run = s_off[e];
-    for (int col = 0; col < a.ncols; ++col) {
+  for (int x = tid; x < (split ? 2 * E : E); x += 256) {
+    const int e = split ? x >> 1 : x;
+    const bool second = split && (x & 1);
+    const int c0 = second ? half : 0;
+    const int c1 = split && !second ? half : a.ncols;
+    int run = s_off[e] + (second ? s_half[e] : 0);
+#pragma unroll 16
+    for (int col = c0; col < c1; ++col) {
       const int c = a.hist[col * E + e];
       a.hist[col * E + e] = run;
       run += c;
     }
+    if (second) continue;
     const int seg_end = s_off[e + 1];
     for (int t = s_off[e] >> a.tile_shift; t < (seg_end >> a.tile_shift); ++t) a.tile_expert[t] = e;
     for (int r = s_off[e] + s_cnt[e]; r < seg_end; ++r) a.src[r] = -1;
@@ -183,8 +205,9 @@ __global__ __launch_bounds__(256) void plan_count_kernel(PlanArgs a) {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   // s_run doubles as the counts array of the scan (the waves' rows are done)
   int* s_cnt = &s_run[0][0];
+  int* s_half = &s_run[1][0];
   __syncthreads();
-  plan_scan(a, s_cnt, s_off, scratch);
+  plan_scan(a, s_cnt, s_off, s_half, scratch);
   if (threadIdx.x == 0) __hip_atomic_store(a.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (gridDim.x != 1) return;
   // single block: place the pairs right away
