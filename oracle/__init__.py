@@ -5,6 +5,16 @@ CPU-baseline leg are its only users. Plain NumPy in float64; it shares no code
 with the GPU library and imports nothing from it.
 """
 from .e4m3 import E4M3_MAX, E4M3_VALUES, e4m3_decode, e4m3_encode  # noqa: F401
+from .mx import (  # noqa: F401
+    MX_BLOCK,
+    dequantize_mx_e4m3,
+    dequantize_mx_fp4,
+    e2m1_decode,
+    e8m0_decode,
+    mx_shared_exponent,
+    quantize_mx_e4m3,
+    unpack_fp4,
+)
 from .moe_oracle import (  # noqa: F401
     GROUP,
     OraclePlan,

@@ -28,6 +28,11 @@ Readings where the page is silent (each is the plainest one the rest supports):
    The quantisation decisions are taken in fp32, the kernels' precision.
 6. combine: out[t] = sum over local k, ascending, of w[t,k] * y(t,k);
    a token with no local pair gets a zero row.
+7. mxfp4 (weights MXFP4, the format the pages tie to MI355X MoE serving):
+   weights are E2M1 codes times an E8M0 scale per 1x32 block along K, as the
+   OCP MX specification defines them (oracle/mx.py); activations (x, and h
+   before GEMM Y) are MXFP8: E4M3 codes with an E8M0 scale per 1x32 block,
+   quantised per that specification in float32.
 
 Arithmetic: float64 on the dequantised values (bf16 -> float is exact), with
 no intermediate rounding except the fp8 activation quantisation of reading 5.
@@ -40,6 +45,7 @@ from typing import Optional, Sequence
 import numpy as np
 
 from .e4m3 import e4m3_decode, e4m3_encode
+from .mx import dequantize_mx_e4m3, dequantize_mx_fp4, quantize_mx_e4m3
 
 GROUP = 128  # fp8 activation group / weight block edge
 
@@ -65,6 +71,15 @@ def bf16_to_f64(t) -> np.ndarray:
     """bf16 tensor -> float64: the 16 bits are the top half of an IEEE binary32."""
     b = bf16_bits(t).astype(np.uint32) << np.uint32(16)
     return b.view(np.float32).astype(np.float64)
+
+
+def _mode(dtype) -> str:
+    """Activation/weight format: "bf16", "fp8" or "mxfp4" (a bool means fp8 or bf16)."""
+    if isinstance(dtype, (bool, np.bool_)):
+        return "fp8" if dtype else "bf16"
+    if dtype not in ("bf16", "fp8", "mxfp4"):
+        raise ValueError(dtype)
+    return dtype
 
 
 def fp8_codes(t) -> np.ndarray:
@@ -173,27 +188,32 @@ def dequantize_blocks(codes, scale) -> np.ndarray:
 # --------------------------------------------------------------------------- #
 # A2: what dispatch must place
 # --------------------------------------------------------------------------- #
-def token_rows(x, fp8: bool, tokens: Optional[np.ndarray] = None):
-    """Activation rows as the expert GEMM consumes them.
+def token_rows(x, fp8, tokens: Optional[np.ndarray] = None):
+    """Activation rows as the expert GEMM consumes them (``fp8``: a format name or bool).
 
-    bf16: float64 copy of x. fp8: (codes, scales) of x per 1x128 group.
+    bf16: float64 copy of x. fp8: (codes, fp32 scales) of x per 1x128 group.
+    mxfp4: (E4M3 codes, E8M0 bytes) of x per 1x32 block (MXFP8).
     """
+    mode = _mode(fp8)
     xs = x if tokens is None else x[np.asarray(tokens)]
     xf = bf16_to_f64(xs)
-    if not fp8:
+    if mode == "bf16":
         return xf
-    return quantize_groups(xf.astype(np.float32))
+    if mode == "fp8":
+        return quantize_groups(xf.astype(np.float32))
+    return quantize_mx_e4m3(xf.astype(np.float32))
 
 
-def dispatch(x, p: OraclePlan, fp8: bool):
+def dispatch(x, p: OraclePlan, fp8):
     """Pool content of the real rows: returns (rows, payload) where ``rows`` are
     pool row indices in ascending order and ``payload`` their values: bf16 bit
-    patterns [n, H], or (e4m3 codes [n, H], scales [n, H/128])."""
+    patterns [n, H], or (e4m3 codes [n, H], scales [n, H/128] fp32 | [n, H/32] E8M0)."""
+    mode = _mode(fp8)
     rows = np.nonzero(p.src >= 0)[0]
     tok = p.src[rows] // p.K
-    if not fp8:
+    if mode == "bf16":
         return rows, bf16_bits(x)[tok]
-    codes, scales = token_rows(x, True)
+    codes, scales = token_rows(x, mode)
     return rows, (codes[tok], scales[tok])
 
 
@@ -205,26 +225,41 @@ def silu(z: np.ndarray) -> np.ndarray:
         return z / (1.0 + np.exp(-z))
 
 
-def expert_weights_f64(w1_e, w1_s_e, w2_e, w2_s_e):
-    """One expert's weights, dequantised to float64: (W1 [2I, H], W2 [H, I])."""
+def expert_weights_f64(w1_e, w1_s_e, w2_e, w2_s_e, dtype=None):
+    """One expert's weights, dequantised to float64: (W1 [2I, H], W2 [H, I]).
+
+    ``dtype`` None infers bf16 / fp8 from whether scales are given; "mxfp4" reads
+    packed E2M1 codes (uint8 [rows, K/2]) with E8M0 bytes [rows, K/32]."""
+    if dtype == "mxfp4":
+        return (dequantize_mx_fp4(_np(w1_e), _np(w1_s_e)),
+                dequantize_mx_fp4(_np(w2_e), _np(w2_s_e)))
     if w1_s_e is None:
         return bf16_to_f64(w1_e), bf16_to_f64(w2_e)
     return (dequantize_blocks(fp8_codes(w1_e), _np(w1_s_e)),
             dequantize_blocks(fp8_codes(w2_e), _np(w2_s_e)))
 
 
-def expert_ffn(xrows, W1: np.ndarray, W2: np.ndarray, fp8: bool) -> np.ndarray:
+def expert_ffn(xrows, W1: np.ndarray, W2: np.ndarray, fp8) -> np.ndarray:
     """y = (silu(X W1_gate^T) * (X W1_up^T)) W2^T for the rows of one expert.
 
-    ``xrows``: float64 [n, H] (bf16), or (codes, scales) of x (fp8). In fp8 mode h is
-    quantised per 1x128 group from its float32 value before GEMM Y.
+    ``xrows``: float64 [n, H] (bf16), or (codes, scales) of x (fp8, mxfp4). In fp8
+    mode h is quantised per 1x128 group from its float32 value before GEMM Y, in
+    mxfp4 mode per 1x32 block (MXFP8).
     """
-    X = dequantize_groups(*xrows) if fp8 else xrows
+    mode = _mode(fp8)
+    if mode == "bf16":
+        X = xrows
+    elif mode == "fp8":
+        X = dequantize_groups(*xrows)
+    else:
+        X = dequantize_mx_e4m3(*xrows)
     I = W1.shape[0] // 2
     G = X @ W1.T                       # GEMM A: [n, 2I]
     h = silu(G[:, :I]) * G[:, I:]      # gate | up
-    if fp8:
+    if mode == "fp8":
         h = dequantize_groups(*quantize_groups(h.astype(np.float32)))
+    elif mode == "mxfp4":
+        h = dequantize_mx_e4m3(*quantize_mx_e4m3(h.astype(np.float32)))
     return h @ W2.T                    # GEMM Y: [n, H]
 
 
@@ -260,7 +295,8 @@ def moe_layer(inp, tokens: Optional[Sequence[int]] = None, p: Optional[OraclePla
     """Run the path for all tokens, or only for ``tokens`` (each expert's weights
     are dequantised once, and only for experts those tokens reach)."""
     cfg = inp.cfg
-    fp8 = cfg.dtype == "fp8"
+    mode = _mode(cfg.dtype)
+    quant = mode != "bf16"
     if p is None:
         p = plan(inp.topk_idx, cfg.expert_begin, cfg.num_local_experts, cfg.tile)
     ids = _np(inp.topk_idx).astype(np.int64)
@@ -268,14 +304,15 @@ def moe_layer(inp, tokens: Optional[Sequence[int]] = None, p: Optional[OraclePla
     toks = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
     sub_ids = ids[toks]
     local = (sub_ids >= cfg.expert_begin) & (sub_ids < cfg.expert_begin + cfg.num_local_experts)
-    xin = token_rows(inp.x, fp8, toks)
+    xin = token_rows(inp.x, mode, toks)
     y_pair = np.zeros((toks.size, K, cfg.H), dtype=np.float64)
     for e in np.unique(sub_ids[local] - cfg.expert_begin):
         W1, W2 = expert_weights_f64(inp.w1[e], None if inp.w1_scale is None else inp.w1_scale[e],
-                                    inp.w2[e], None if inp.w2_scale is None else inp.w2_scale[e])
+                                    inp.w2[e], None if inp.w2_scale is None else inp.w2_scale[e],
+                                    mode if mode == "mxfp4" else None)
         tt, kk = np.nonzero(sub_ids == e + cfg.expert_begin)
-        rows = (xin[0][tt], xin[1][tt]) if fp8 else xin[tt]
-        y_pair[tt, kk] = expert_ffn(rows, W1, W2, fp8)
+        rows = (xin[0][tt], xin[1][tt]) if quant else xin[tt]
+        y_pair[tt, kk] = expert_ffn(rows, W1, W2, mode)
     out = combine(y_pair, _np(inp.topk_weights)[toks], local)
     return OracleResult(p, out, None if tokens is None else toks)
 

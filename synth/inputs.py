@@ -12,6 +12,8 @@ distributions of five workloads:
 * ``zipf_skew``   T=16384, H=4096, I=1536, 128 experts, Zipf(1.2) bias, K=8, tile 128, bf16
 * ``fp8_weights`` T=8192,  H=4096, I=1536, 128 experts, K=8, tile 128,
   weights e4m3 + fp32 scale per 128x128 block
+* ``mxfp4``       T=8192,  H=4096, I=1536, 128 experts, K=8, tile 128,
+  weights MXFP4: e2m1 codes + one E8M0 scale per 32 weights along K
 
 Distributions: x ~ N(0,1) rounded to bf16; w1 (gate|up, [2I, H]) and w2
 ([H, I]) ~ N(0, std 1/sqrt(fan_in)); routing = distinct top-K of per-token
@@ -64,6 +66,7 @@ class MoEConfig:
     K: int                    # top-k
     tile: int                 # pool tile rows
     dtype: str = "bf16"       # "bf16" | "fp8" (weights e4m3 + 128x128 block scales)
+                              # | "mxfp4" (weights e2m1 + E8M0 scale per 1x32 along K)
     routing: str = "uniform"  # "uniform" | "zipf1.2"
 
     @property
@@ -80,6 +83,7 @@ CONFIGS = [
     MoEConfig("ep_share", 8192, 7168, 2048, 256, 0, 32, 8, 128, "bf16", "uniform"),
     MoEConfig("zipf_skew", 16384, 4096, 1536, 128, 0, 128, 8, 128, "bf16", "zipf1.2"),
     MoEConfig("fp8_weights", 8192, 4096, 1536, 128, 0, 128, 8, 128, "fp8", "uniform"),
+    MoEConfig("mxfp4", 8192, 4096, 1536, 128, 0, 128, 8, 128, "mxfp4", "uniform"),
 ]
 
 
@@ -154,6 +158,40 @@ def _block_quant_e4m3(w: torch.Tensor):
     return q.to(torch.float8_e4m3fn), scale.contiguous()
 
 
+# e2m1 magnitudes by code (OCP MX e2m1: 1 sign, 2 exponent bits with bias 1, 1 mantissa bit)
+_E2M1_GRID = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+_E2M1_MIDS = (_E2M1_GRID[1:] + _E2M1_GRID[:-1]) / 2
+
+
+def _mx_quant_e2m1(w: torch.Tensor):
+    """MXFP4-quantise an fp32 master [R, C] along C in blocks of 32.
+
+    Per block: shared exponent = floor(log2(amax)) - 2 (the largest e2m1 power,
+    6 = 1.5 * 2^2), clamped to [-127, 127]; E8M0 byte = exponent + 127 (0 for an
+    all-zero block). Codes = e2m1 of w / 2^exponent, round to nearest, ties to the
+    even code, magnitudes above 6 saturate to 6. Two codes per byte, the even
+    column in the low nibble. This is how the workload's stored weights are
+    defined; the layer only reads them.
+    """
+    R, C = w.shape
+    assert C % 32 == 0, C
+    blk = w.reshape(R, C // 32, 32)
+    amax = blk.abs().amax(dim=2)
+    _, ex = torch.frexp(amax)                       # amax = m * 2^ex, m in [0.5, 1)
+    shared = torch.where(amax > 0, ex - 1 - 2, torch.full_like(ex, -127)).clamp_(-127, 127)
+    v = blk / torch.ldexp(torch.ones_like(amax), shared)[..., None]
+    a = v.abs().clamp_(max=6.0)
+    # nearest grid point: count the midpoints below (lo) and at-or-below (hi);
+    # they differ only on an exact midpoint, where the even code wins
+    lo = torch.bucketize(a, _E2M1_MIDS, right=False)
+    hi = torch.bucketize(a, _E2M1_MIDS, right=True)
+    code = torch.where((lo == hi) | (lo % 2 == 0), lo, hi)
+    code = code | torch.where(v < 0, 8, 0)
+    code = code.reshape(R, C).to(torch.uint8)
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).contiguous()
+    return packed, (shared + 127).to(torch.uint8).contiguous()
+
+
 def expert_weights(cfg: MoEConfig, seed: int, e_local: int):
     """Weights of local expert ``e_local``: (w1 [2I, H], w1_scale, w2 [H, I], w2_scale).
 
@@ -170,6 +208,10 @@ def expert_weights(cfg: MoEConfig, seed: int, e_local: int):
         q1, s1 = _block_quant_e4m3(w1)
         q2, s2 = _block_quant_e4m3(w2)
         return q1, s1, q2, s2
+    if cfg.dtype == "mxfp4":
+        q1, s1 = _mx_quant_e2m1(w1)
+        q2, s2 = _mx_quant_e2m1(w2)
+        return q1, s1, q2, s2
     raise ValueError(cfg.dtype)
 
 
@@ -180,10 +222,10 @@ class MoEInputs:
     x: torch.Tensor                   # bf16 [T, H]
     topk_idx: torch.Tensor            # int32 [T, K], global expert ids
     topk_weights: torch.Tensor        # float32 [T, K]
-    w1: Optional[torch.Tensor]        # bf16 | float8_e4m3fn [E_local, 2I, H]
-    w1_scale: Optional[torch.Tensor]  # float32 [E_local, 2I/128, H/128] (fp8 only)
-    w2: Optional[torch.Tensor]        # bf16 | float8_e4m3fn [E_local, H, I]
-    w2_scale: Optional[torch.Tensor]  # float32 [E_local, H/128, I/128] (fp8 only)
+    w1: Optional[torch.Tensor]        # bf16 | float8_e4m3fn [E_local, 2I, H] | uint8 [E_local, 2I, H/2] (mxfp4)
+    w1_scale: Optional[torch.Tensor]  # float32 [E_local, 2I/128, H/128] (fp8) | uint8 [E_local, 2I, H/32] (mxfp4)
+    w2: Optional[torch.Tensor]        # bf16 | float8_e4m3fn [E_local, H, I] | uint8 [E_local, H, I/2] (mxfp4)
+    w2_scale: Optional[torch.Tensor]  # float32 [E_local, H/128, I/128] (fp8) | uint8 [E_local, H, I/32] (mxfp4)
 
 
 def _threads() -> int:
@@ -209,18 +251,25 @@ def make_inputs(cfg: MoEConfig, seed: Optional[int] = None, *, weights: bool = T
     if not weights:
         return MoEInputs(cfg, s, x, idx, w, None, None, None, None)
     E, H, I = cfg.num_local_experts, cfg.H, cfg.I
-    wdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float8_e4m3fn
-    w1 = torch.empty(E, 2 * I, H, dtype=wdt, pin_memory=pin_memory)
-    w2 = torch.empty(E, H, I, dtype=wdt, pin_memory=pin_memory)
+    mx = cfg.dtype == "mxfp4"
     fp8 = cfg.dtype == "fp8"
-    w1s = torch.empty(E, 2 * I // 128, H // 128, dtype=torch.float32) if fp8 else None
-    w2s = torch.empty(E, H // 128, I // 128, dtype=torch.float32) if fp8 else None
+    if mx:
+        w1 = torch.empty(E, 2 * I, H // 2, dtype=torch.uint8, pin_memory=pin_memory)
+        w2 = torch.empty(E, H, I // 2, dtype=torch.uint8, pin_memory=pin_memory)
+        w1s = torch.empty(E, 2 * I, H // 32, dtype=torch.uint8)
+        w2s = torch.empty(E, H, I // 32, dtype=torch.uint8)
+    else:
+        wdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float8_e4m3fn
+        w1 = torch.empty(E, 2 * I, H, dtype=wdt, pin_memory=pin_memory)
+        w2 = torch.empty(E, H, I, dtype=wdt, pin_memory=pin_memory)
+        w1s = torch.empty(E, 2 * I // 128, H // 128, dtype=torch.float32) if fp8 else None
+        w2s = torch.empty(E, H // 128, I // 128, dtype=torch.float32) if fp8 else None
 
     def one(e):
         a, as_, b, bs = expert_weights(cfg, s, e)
         w1[e].copy_(a)
         w2[e].copy_(b)
-        if fp8:
+        if fp8 or mx:
             w1s[e].copy_(as_)
             w2s[e].copy_(bs)
 

@@ -64,3 +64,29 @@ def test_fp8_weights_layout():
     # every block reaches +-448 in code space
     c = inp.w1.view(torch.uint8).reshape(4, 2, 128, 2, 128)
     assert ((c & 0x7F).amax(dim=(2, 4)) == 0x7E).all()
+
+
+def test_mxfp4_weights_layout_and_rounding():
+    # the stored weights are the MX quantisation of the fp32 masters: every block's
+    # largest code is 6 or (rounded down from) 4..6, and each weight is within the
+    # E2M1 rounding bound of its master (half the step at its magnitude, or the
+    # saturation gap 6..8 for the block maximum)
+    from oracle import dequantize_mx_fp4, unpack_fp4
+    from synth.inputs import _mx_quant_e2m1
+
+    cfg = config_by_name("mxfp4").with_(name="mx_small", T=16, H=256, I=128, num_experts=4,
+                                         num_local_experts=4)
+    inp = make_inputs(cfg, 3)
+    assert inp.w1.dtype == torch.uint8 and inp.w1.shape == (4, 256, 128)
+    assert inp.w1_scale.shape == (4, 256, 8) and inp.w2_scale.shape == (4, 256, 4)
+    rng = np.random.default_rng(0)
+    w = torch.from_numpy((rng.standard_normal((8, 128)) * 0.05).astype(np.float32))
+    q, s = _mx_quant_e2m1(w)
+    deq = dequantize_mx_fp4(q.numpy(), s.numpy())
+    X = np.exp2(s.numpy().astype(np.float64) - 127).repeat(32, axis=1)
+    a = np.abs(w.numpy().astype(np.float64)) / X
+    step = np.where(a < 2, 0.5, np.where(a < 4, 1.0, 2.0))
+    bound = np.where(a > 6, a - 6, step / 2) * X
+    assert (np.abs(deq - w.numpy()) <= bound + 1e-30).all()
+    codes = unpack_fp4(q.numpy()).reshape(8, 4, 32) & 7
+    assert (codes.max(axis=2) >= 6).all()
