@@ -58,8 +58,10 @@ def algorithmic_work(cfg, idx_np):
     N = int(local.sum())                        # local pairs
     T_act = int(local.any(axis=1).sum())        # tokens with at least one local pair
     H, I, K, T = cfg.H, cfg.I, cfg.K, cfg.T
-    pool_b = 2 if cfg.dtype == "bf16" else 1 + 4 / 128
-    w_b = 2 if cfg.dtype == "bf16" else 1 + 4 / (128 * 128)
+    # bytes per element with scales: bf16 2; fp8 e4m3 + fp32 per 1x128 group (activations) or
+    # per 128x128 block (weights); mxfp4 e4m3 + E8M0 per 1x32 (activations), e2m1 + E8M0 per 1x32
+    pool_b = {"bf16": 2, "fp8": 1 + 4 / 128, "mxfp4": 1 + 1 / 32}[cfg.dtype]
+    w_b = {"bf16": 2, "fp8": 1 + 4 / (128 * 128), "mxfp4": 0.5 + 1 / 32}[cfg.dtype]
     return {
         "pairs": N,
         "ffn_flops": 6.0 * N * H * I,
@@ -208,7 +210,7 @@ def main():
     x = inp.x.to(dev, non_blocking=True)
     idx = inp.topk_idx.to(dev)
     w = inp.topk_weights.to(dev)
-    if fp8:
+    if fp8 or cfg.dtype == "mxfp4":
         w1, w2 = inp.w1.view(torch.uint8).to(dev), inp.w2.view(torch.uint8).to(dev)
         w1s, w2s = inp.w1_scale.to(dev), inp.w2_scale.to(dev)
     else:
@@ -220,7 +222,7 @@ def main():
     layer = moe.StreamMoE(cfg.T, cfg.H, cfg.I, cfg.K, cfg.num_local_experts,
                           expert_begin=cfg.expert_begin, tile=cfg.tile, dtype=cfg.dtype, cfg=tcfg)
     # weight preprocessing at load time (not part of a step): MFMA fragment order when used
-    w1, w2 = layer.prepare_weights(w1, w2)
+    w1, w2, w1s, w2s = layer.prepare_weights(w1, w2, w1s, w2s)
     torch.cuda.synchronize()
     work = algorithmic_work(cfg, inp.topk_idx.numpy())
     streams = moe.make_streams() if args.streams else None
@@ -279,7 +281,9 @@ def main():
     tokens_s = cfg.T / (ms_step * 1e-3)
     ffn_tflops = work["ffn_flops"] / (stage_ms["ffn"] * 1e-3) / 1e12
     ffn_gbs = work["ffn_bytes"] / (stage_ms["ffn"] * 1e-3) / 1e9
-    peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
+    # mxfp4 multiplies e2m1 weights by e4m3 activations: the scaled MFMA runs at the
+    # rate of its wider operand, fp8
+    peak = PEAK_FP8_TFLOPS if cfg.dtype in ("fp8", "mxfp4") else PEAK_BF16_TFLOPS
     # the FFN's bound: MFMA unless streaming its least traffic takes longer at HBM peak
     hbm_bound = work["ffn_bytes"] / (PEAK_HBM_GBS * 1e9) > work["ffn_flops"] / (peak * 1e12)
     disp_gbs = work["dispatch_bytes"] / (stage_ms["dispatch"] * 1e-3) / 1e9
@@ -297,7 +301,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8" if fp8 else "bf16",
+        "dtype": {"bf16": "bf16", "fp8": "fp8", "mxfp4": "mxfp4 (e2m1 x e4m3)"}[cfg.dtype],
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "I": cfg.I,
                    "experts": cfg.num_experts, "local_experts": cfg.num_local_experts, "K": cfg.K,

@@ -6,6 +6,7 @@ load it, the first call does, and fails loudly if it has not been built.
 from .layer import (  # noqa: F401
     MOE_BF16,
     MOE_FP8_E4M3_G128,
+    MOE_MXFP4,
     MOE_WEIGHTS_MFMA_TILED,
     MOE_WEIGHTS_ROW_MAJOR,
     MoeError,
@@ -19,6 +20,7 @@ from .layer import (  # noqa: F401
     moe_dispatch,
     moe_expert_ffn,
     moe_get_error,
+    moe_pack_mx_scales,
     moe_pack_weights,
     moe_plan,
     moe_query_pool_rows,

@@ -15,6 +15,7 @@ MOE_ERR_TIMEOUT = 4
 
 MOE_BF16 = 0
 MOE_FP8_E4M3_G128 = 1
+MOE_MXFP4 = 2
 
 MOE_WEIGHTS_ROW_MAJOR = 0
 MOE_WEIGHTS_MFMA_TILED = 1
@@ -76,6 +77,7 @@ SIGNATURES = [
       ctypes.POINTER(TileConfig), _VP]),
     ("moe_combine", ctypes.c_int, [_VP, _I32, _VP, _PP, _I32, _VP, _VP]),
     ("moe_pack_weights", ctypes.c_int, [_VP, _I32, _I32, _I32, _I32, _VP, _VP]),
+    ("moe_pack_mx_scales", ctypes.c_int, [_VP, _I32, _I32, _I32, _VP, _VP]),
     ("moe_get_error", ctypes.c_int, [_VP, _SZ, _VP]),
     ("moe_status_string", ctypes.c_char_p, [ctypes.c_int]),
     ("moe_device_cu_count", ctypes.c_int, []),

@@ -49,8 +49,9 @@ MOE355_API size_t moe_pool_rows_upper_bound(int32_t T, int32_t K, int32_t E_loca
 MOE355_API size_t moe_workspace_bytes(int32_t T, int32_t K, int32_t E_local, int32_t tile, int32_t pool_rows,
                                       int32_t I, int32_t dtype) {
   if (T < 1 || K < 1 || K > 16 || E_local < 1 || E_local > 1024 || !valid_tile(tile)) return 0;
-  if (pool_rows < 0 || I < 0 || (dtype != MOE_BF16 && dtype != MOE_FP8_E4M3_G128)) return 0;
+  if (pool_rows < 0 || I < 0 || (dtype != MOE_BF16 && dtype != MOE_FP8_E4M3_G128 && dtype != MOE_MXFP4)) return 0;
   if (dtype == MOE_FP8_E4M3_G128 && I % 128 != 0) return 0;
+  if (dtype == MOE_MXFP4 && I % 32 != 0) return 0;
   return ws_layout(T, K, E_local, tile, pool_rows, I, dtype).total;
 }
 
@@ -76,7 +77,7 @@ MOE355_API int moe_query_pool_rows(const moe_plan_t* plan, int32_t* host_P, void
 }
 
 MOE355_API int moe_dispatch(const void* x, int32_t H, int32_t act_dtype, const moe_plan_t* plan,
-                            int32_t pool_rows, void* pool, float* pool_s, uint32_t epoch, void* ws,
+                            int32_t pool_rows, void* pool, void* pool_s, uint32_t epoch, void* ws,
                             size_t ws_bytes, void* stream) {
   int rc = check_plan(plan);
   if (rc != MOE_OK) return rc;
@@ -86,6 +87,9 @@ MOE355_API int moe_dispatch(const void* x, int32_t H, int32_t act_dtype, const m
   } else if (act_dtype == MOE_FP8_E4M3_G128) {
     if (!pool_s) return MOE_ERR_INVALID;
     if (H % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  } else if (act_dtype == MOE_MXFP4) {
+    if (!pool_s) return MOE_ERR_INVALID;
+    if (H % 32 != 0) return MOE_ERR_UNSUPPORTED;
   } else {
     return MOE_ERR_INVALID;
   }
@@ -97,18 +101,18 @@ MOE355_API int moe_dispatch(const void* x, int32_t H, int32_t act_dtype, const m
                          static_cast<hipStream_t>(stream));
 }
 
-MOE355_API int moe_expert_ffn(const moe_plan_t* plan, int32_t pool_rows, const void* pool, const float* pool_s,
-                              const void* w1, const float* w1_s, const void* w2, const float* w2_s, int32_t H,
+MOE355_API int moe_expert_ffn(const moe_plan_t* plan, int32_t pool_rows, const void* pool, const void* pool_s,
+                              const void* w1, const void* w1_s, const void* w2, const void* w2_s, int32_t H,
                               int32_t I, int32_t dtype, uint32_t epoch, void* ws, size_t ws_bytes, void* y_pool,
                               const moe_tile_config* cfg, void* stream) {
   int rc = check_plan(plan);
   if (rc != MOE_OK) return rc;
   if (!pool || !w1 || !w2 || !ws || !y_pool || epoch == 0 || H < 1 || I < 1) return MOE_ERR_INVALID;
   if (pool_rows < 1 || pool_rows % plan->tile != 0) return MOE_ERR_INVALID;
-  const bool fp8 = dtype == MOE_FP8_E4M3_G128;
-  if (dtype != MOE_BF16 && !fp8) return MOE_ERR_INVALID;
-  if (fp8 && (!pool_s || !w1_s || !w2_s)) return MOE_ERR_INVALID;
-  if (!fp8 && (pool_s || w1_s || w2_s)) return MOE_ERR_INVALID;
+  const bool scaled = dtype == MOE_FP8_E4M3_G128 || dtype == MOE_MXFP4;
+  if (dtype != MOE_BF16 && !scaled) return MOE_ERR_INVALID;
+  if (scaled && (!pool_s || !w1_s || !w2_s)) return MOE_ERR_INVALID;
+  if (!scaled && (pool_s || w1_s || w2_s)) return MOE_ERR_INVALID;
   const int32_t block_n = cfg ? cfg->block_n : 0;
   const int32_t layout = cfg ? cfg->weight_layout : MOE_WEIGHTS_ROW_MAJOR;
   if (layout != MOE_WEIGHTS_ROW_MAJOR && layout != MOE_WEIGHTS_MFMA_TILED) return MOE_ERR_INVALID;
@@ -155,14 +159,25 @@ MOE355_API int moe_combine(const void* y_pool, int32_t pool_rows, const float* t
 MOE355_API int moe_pack_weights(const void* w, int32_t E, int32_t rows, int32_t K, int32_t dtype, void* out,
                                 void* stream) {
   if (!w || !out || E < 1 || rows < 1 || K < 1) return MOE_ERR_INVALID;
-  if (dtype != MOE_BF16 && dtype != MOE_FP8_E4M3_G128) return MOE_ERR_INVALID;
+  if (dtype != MOE_BF16 && dtype != MOE_FP8_E4M3_G128 && dtype != MOE_MXFP4) return MOE_ERR_INVALID;
   if (rows % 16 != 0 || K % (dtype == MOE_BF16 ? 32 : 128) != 0) return MOE_ERR_UNSUPPORTED;
-  const int64_t bytes = (int64_t)rows * K * (dtype == MOE_BF16 ? 2 : 1);
+  const int64_t bytes = dtype == MOE_MXFP4 ? (int64_t)rows * K / 2 : (int64_t)rows * K * (dtype == MOE_BF16 ? 2 : 1);
   if (bytes > ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
   const char* a = static_cast<const char*>(w);
   const char* b = static_cast<const char*>(out);
   if (a < b + bytes * E && b < a + bytes * E) return MOE_ERR_INVALID;  // overlap
   return launch_pack_weights(w, E, rows, K, dtype, out, static_cast<hipStream_t>(stream));
+}
+
+MOE355_API int moe_pack_mx_scales(const void* s, int32_t E, int32_t rows, int32_t K, void* out, void* stream) {
+  if (!s || !out || E < 1 || rows < 1 || K < 1) return MOE_ERR_INVALID;
+  if (rows % 16 != 0 || K % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  const int64_t bytes = (int64_t)rows * (K / 32);
+  if (bytes * E > ((int64_t)1 << 40)) return MOE_ERR_UNSUPPORTED;
+  const char* a = static_cast<const char*>(s);
+  const char* b = static_cast<const char*>(out);
+  if (a < b + bytes * E && b < a + bytes * E) return MOE_ERR_INVALID;  // overlap
+  return launch_pack_mx_scales(s, E, rows, K, out, static_cast<hipStream_t>(stream));
 }
 
 MOE355_API int moe_get_error(void* ws, size_t ws_bytes, void* stream) {

@@ -23,7 +23,7 @@ struct WsLayout {
   size_t hist = 256;     // int32 [ncols][E_local]: per-wave expert counts, then bases
   size_t fill = 0;       // uint32 [ntiles_cap]: rows stored per tile by dispatch
   size_t h = 0;          // h [pool_rows][I]: bf16, or e4m3 codes
-  size_t hs = 0;         // float [pool_rows][I/128] (fp8 only)
+  size_t hs = 0;         // fp8: float [pool_rows][I/128]; mxfp4: E8M0 bytes [pool_rows][I/32]
   size_t plan_end = 0;   // end of what plan/dispatch need
   size_t total = 0;
   int32_t ncols = 0;
@@ -48,12 +48,15 @@ inline WsLayout ws_layout(int32_t T, int32_t K, int32_t E, int32_t tile, int64_t
   if (pool_rows <= 0) pool_rows = cap;
   size_t off = L.plan_end;
   if (I > 0) {
-    const size_t elem = dtype == MOE_FP8_E4M3_G128 ? 1 : 2;
+    const size_t elem = dtype == MOE_BF16 ? 2 : 1;
     L.h = off;
     off = align_up(off + (size_t)pool_rows * I * elem, 256);
     if (dtype == MOE_FP8_E4M3_G128) {
       L.hs = off;
       off = align_up(off + (size_t)pool_rows * (I / 128) * 4, 256);
+    } else if (dtype == MOE_MXFP4) {
+      L.hs = off;
+      off = align_up(off + (size_t)pool_rows * (I / 32), 256);
     }
   }
   L.total = off;
@@ -161,6 +164,17 @@ __device__ inline uint32_t pack_e4m3x4(float a, float b, float c, float d) {
 __device__ inline uint32_t e4m3_from_f32(float v) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(v, -448.0f, 448.0f), 0.0f, 0, false) & 0xffu;
 }
+
+// MXFP8 block scale (OCP MX): shared exponent floor(log2(amax)) - 8 (8 = exponent
+// of e4m3's largest normal), clamped to [-127, 127], -127 for amax = 0 (NaN-free
+// input assumed). frexp's exponent is exact for subnormal amax too.
+__device__ inline int mx_e4m3_shared_exp(float amax) {
+  const int e = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) - 1 - 8 : -127;
+  return max(-127, min(127, e));
+}
+// 2^-e for a shared exponent of mx_e4m3_shared_exp (-e <= 127, and e <= 119 keeps it
+// normal): multiplying by it is exact, so the codes equal those of x / 2^e
+__device__ inline float mx_inv_scale(int e) { return __builtin_amdgcn_ldexpf(1.0f, -e); }
 
 // --------------------------------------------------------------------------
 // buffer resources: hardware range checks (out-of-range loads read 0, stores drop)

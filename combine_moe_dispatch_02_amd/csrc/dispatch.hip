@@ -9,7 +9,10 @@
 // local pairs' rows, so x is read T*H*2 bytes once and the pool written once per
 // pair. In fp8 mode each 1x128 group (16 lanes x 8 values) is quantised on the
 // way: scale = amax/448 in fp32 (1 for an all-zero group), code = e4m3(x /
-// scale) with IEEE division, round to nearest even, saturating. A wave handles
+// scale) with IEEE division, round to nearest even, saturating. In mxfp4 mode
+// the activations become MXFP8 (OCP MX): each 1x32 block (4 lanes x 8 values)
+// gets the E8M0 scale 2^e, e = floor(log2(amax)) - 8, and codes e4m3(x * 2^-e),
+// exact scaling then the same rounding. A wave handles
 // a run of 64/K tokens; a workgroup's runs are published with a single
 // device-scope release (an L2 write-back on this chip, so it is paid per
 // workgroup, not per row or per wave); each stored pair then bumps its tile's
@@ -31,7 +34,7 @@ struct DispatchArgs {
   const int32_t* offsets;
   const int32_t* counts;
   uint8_t* pool;
-  float* pool_s;
+  void* pool_s;                // fp8: float [rows][H/128]; mxfp4: E8M0 bytes [rows][H/32]
   int32_t pool_rows;
   uint32_t* tile_fill;
   uint32_t* tile_ready;
@@ -40,9 +43,18 @@ struct DispatchArgs {
   int32_t tokens_per_wave;  // tokens_per_wave * K <= 64
 };
 
+// max over the 4 lanes of a DPP quad (quad_perm [1,0,3,2] then [2,3,0,1])
+__device__ inline float quad_max(float v) {
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xf, 0xf, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xf, 0xf, false)));
+  return v;
+}
+
 // One token's row: read once, stored to each of its local pairs' rows.
-template <int CPL, bool FP8>
+// FMT: 0 bf16 copy, 1 fp8 1x128 groups, 2 MXFP8 1x32 blocks.
+template <int CPL, int FMT>
 __device__ inline void dispatch_token(const DispatchArgs& a, int t, int p, uint64_t dest, int lane) {
+  constexpr bool FP8 = FMT != 0;
   const int H = a.H;
   const int nch = H >> 3;  // 16-byte chunks of 8 bf16 in a row
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x + (int64_t)t * H, (uint32_t)H * 2u);
@@ -51,13 +63,48 @@ __device__ inline void dispatch_token(const DispatchArgs& a, int t, int p, uint6
     u32x4 v[CPL];
 #pragma unroll
     for (int i = 0; i < CPL; ++i) v[i] = buf_load16(xr, (uint32_t)(c0 + i * kWave + lane) * 16u);
-    if constexpr (!FP8) {
+    if constexpr (FMT == 0) {
       for (int k = 0; k < a.K; ++k) {
         if (!((dest >> k) & 1ull)) continue;
         const int pk = readlane(p, k);
         const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.pool + (int64_t)pk * out_row_bytes, (uint32_t)out_row_bytes);
 #pragma unroll
         for (int i = 0; i < CPL; ++i) buf_store16(v[i], pr, (uint32_t)(c0 + i * kWave + lane) * 16u);
+      }
+    } else if constexpr (FMT == 2) {
+      u32x2 q[CPL];
+      uint32_t sb[CPL];
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        float f[8];
+        f[0] = bf16_lo(v[i].x); f[1] = bf16_hi(v[i].x);
+        f[2] = bf16_lo(v[i].y); f[3] = bf16_hi(v[i].y);
+        f[4] = bf16_lo(v[i].z); f[5] = bf16_hi(v[i].z);
+        f[6] = bf16_lo(v[i].w); f[7] = bf16_hi(v[i].w);
+        float m = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(f[j]));
+        m = quad_max(m);                       // the 4 lanes of a DPP quad hold one block
+        const int e = mx_e4m3_shared_exp(m);
+        const float inv = mx_inv_scale(e);
+        sb[i] = (uint32_t)(e + 127);
+        q[i].x = pack_e4m3x4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
+        q[i].y = pack_e4m3x4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
+      }
+      const int blocks = H >> 5;
+      for (int k = 0; k < a.K; ++k) {
+        if (!((dest >> k) & 1ull)) continue;
+        const int pk = readlane(p, k);
+        const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.pool + (int64_t)pk * out_row_bytes, (uint32_t)out_row_bytes);
+        const __amdgpu_buffer_rsrc_t sr =
+            make_rsrc(static_cast<uint8_t*>(a.pool_s) + (int64_t)pk * blocks, (uint32_t)blocks);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+          const int c = c0 + i * kWave + lane;
+          buf_store8(q[i], pr, (uint32_t)c * 8u);
+          if ((lane & 3) == 0)   // chunks past the row end fall outside the buffer: dropped
+            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sb[i], sr, (uint32_t)(c >> 2), 0, 0);
+        }
       }
     } else {
       u32x2 q[CPL];
@@ -83,7 +130,7 @@ __device__ inline void dispatch_token(const DispatchArgs& a, int t, int p, uint6
         if (!((dest >> k) & 1ull)) continue;
         const int pk = readlane(p, k);
         const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.pool + (int64_t)pk * out_row_bytes, (uint32_t)out_row_bytes);
-        float* srow = a.pool_s + (int64_t)pk * groups;
+        float* srow = static_cast<float*>(a.pool_s) + (int64_t)pk * groups;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
           const int c = c0 + i * kWave + lane;
@@ -104,7 +151,7 @@ __device__ inline void dispatch_token(const DispatchArgs& a, int t, int p, uint6
 // (relaxed), and the lane whose count completes a tile acquires and stores the
 // epoch into tile_ready (release). The host picks the largest WPB (up to 16) that
 // still gives every CU a block.
-template <int CPL, bool FP8, int WPB>
+template <int CPL, int FMT, int WPB>
 __global__ __launch_bounds__(64 * WPB) void dispatch_kernel(DispatchArgs a) {
   const int lane = lane_id();
   const int w = threadIdx.x >> 6;
@@ -120,7 +167,7 @@ __global__ __launch_bounds__(64 * WPB) void dispatch_kernel(DispatchArgs a) {
       p = -1;
     }
     const uint64_t dest = ballot(p >= 0);
-    if (dest != 0) dispatch_token<CPL, FP8>(a, t, p, dest, lane);
+    if (dest != 0) dispatch_token<CPL, FMT>(a, t, p, dest, lane);
   }
 
   __syncthreads();
@@ -143,30 +190,30 @@ __global__ __launch_bounds__(64 * WPB) void dispatch_kernel(DispatchArgs a) {
   }
 }
 
-template <bool FP8, int WPB>
+template <int FMT, int WPB>
 static void launch_cpl(int cpl, dim3 grid, hipStream_t s, const DispatchArgs& a) {
   switch (cpl) {
-    case 1: hipLaunchKernelGGL((dispatch_kernel<1, FP8, WPB>), grid, dim3(64 * WPB), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((dispatch_kernel<2, FP8, WPB>), grid, dim3(64 * WPB), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((dispatch_kernel<4, FP8, WPB>), grid, dim3(64 * WPB), 0, s, a); break;
-    default: hipLaunchKernelGGL((dispatch_kernel<8, FP8, WPB>), grid, dim3(64 * WPB), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((dispatch_kernel<1, FMT, WPB>), grid, dim3(64 * WPB), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((dispatch_kernel<2, FMT, WPB>), grid, dim3(64 * WPB), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((dispatch_kernel<4, FMT, WPB>), grid, dim3(64 * WPB), 0, s, a); break;
+    default: hipLaunchKernelGGL((dispatch_kernel<8, FMT, WPB>), grid, dim3(64 * WPB), 0, s, a); break;
   }
 }
 
-template <bool FP8>
+template <int FMT>
 static void launch_wpb(int wpb, int cpl, int waves, hipStream_t s, const DispatchArgs& a) {
   const dim3 grid((waves + wpb - 1) / wpb);
   switch (wpb) {
-    case 1: launch_cpl<FP8, 1>(cpl, grid, s, a); break;
-    case 2: launch_cpl<FP8, 2>(cpl, grid, s, a); break;
-    case 4: launch_cpl<FP8, 4>(cpl, grid, s, a); break;
-    case 8: launch_cpl<FP8, 8>(cpl, grid, s, a); break;
-    default: launch_cpl<FP8, 16>(cpl, grid, s, a); break;
+    case 1: launch_cpl<FMT, 1>(cpl, grid, s, a); break;
+    case 2: launch_cpl<FMT, 2>(cpl, grid, s, a); break;
+    case 4: launch_cpl<FMT, 4>(cpl, grid, s, a); break;
+    case 8: launch_cpl<FMT, 8>(cpl, grid, s, a); break;
+    default: launch_cpl<FMT, 16>(cpl, grid, s, a); break;
   }
 }
 
 int launch_dispatch(const void* x, int32_t H, int32_t dtype, const moe_plan_t& p, int32_t pool_rows,
-                    void* pool, float* pool_s, uint32_t epoch, const WsLayout& L, char* ws,
+                    void* pool, void* pool_s, uint32_t epoch, const WsLayout& L, char* ws,
                     hipStream_t stream) {
   DispatchArgs a;
   a.x = static_cast<const uint16_t*>(x);
@@ -195,9 +242,11 @@ int launch_dispatch(const void* x, int32_t H, int32_t dtype, const moe_plan_t& p
   int wpb = 1;
   while (wpb < 16 && waves / (2 * wpb) >= cus) wpb *= 2;
   if (dtype == MOE_FP8_E4M3_G128)
-    launch_wpb<true>(wpb, cpl, waves, stream, a);
+    launch_wpb<1>(wpb, cpl, waves, stream, a);
+  else if (dtype == MOE_MXFP4)
+    launch_wpb<2>(wpb, cpl, waves, stream, a);
   else
-    launch_wpb<false>(wpb, cpl, waves, stream, a);
+    launch_wpb<0>(wpb, cpl, waves, stream, a);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

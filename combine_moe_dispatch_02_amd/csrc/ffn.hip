@@ -23,6 +23,8 @@
 // row per lane (lane l: row l%16, K chunk l/16).
 // fp8: v_mfma_scale_f32_16x16x128_f8f6f4 with unit scales (E8M0 127), one per
 // 128-wide K block, then acc += partial * a_scale[row] * b_scale[block] in fp32.
+// mxfp4: the same instruction with e2m1 weights (format 4) and e4m3 activations,
+// its per-lane E8M0 operands carrying the 1x32 block scales of both sides.
 #include <algorithm>
 #include <type_traits>
 
@@ -67,6 +69,12 @@ struct FfnArgs {
   uint32_t* err;
   uint64_t timeout;
   int32_t wait_ready;
+  const uint8_t* A_e8;       // mxfp4: activation E8M0 scales [rows][Kdim/32]
+  const uint8_t* B_e8;       // mxfp4: weight E8M0 scales in tile order, expert-major
+  uint8_t* out_e8;           // mxfp4 GEMM A: h E8M0 scales [rows][I/32]
+  int32_t e8_lda;            // mxfp4: bytes per row of A_e8 (Kdim/32)
+  int64_t b_e8_expert;       // mxfp4: bytes per expert of B_e8
+  int32_t e8_ldo;            // mxfp4 GEMM A: bytes per row of out_e8 (I/32)
 };
 
 __device__ inline uint32_t swz(int row, int chunk) { return (uint32_t)(row * 128 + ((chunk ^ (row & 7)) << 4)); }
@@ -442,18 +450,28 @@ __device__ inline uint32_t swz_a(int r, int c) {
   return (uint32_t)(r * 128 + ((c ^ (r & 7)) << 4));
 }
 
-template <int BM, int NW, bool FP8, bool GEMM_A, bool PACKED>
+// MX (mxfp4): A is MXFP8 (e4m3 rows as in fp8, plus one E8M0 byte per 32 K), B is
+// tiled MXFP4 (a 16 x 128 tile = 1 KiB, lane l's 16 bytes = 32 consecutive K of
+// row l%16) with its E8M0 bytes in tile order (64 per tile, byte l = lane l's).
+// The scaled MFMA takes, per lane, the scale of its row and of K block l/16 of the
+// step, and pairs K [16b, 16b+16) + [64+16b, 64+16b+16) of an e4m3 operand lane
+// block b with K [32b, 32b+32) of an e2m1 one: A fragments are therefore 16-byte
+// chunks b and b+4 of the row's 128-byte step.
+template <int BM, int NW, bool FP8, bool GEMM_A, bool PACKED, bool MX = false>
 __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
+  static_assert(!MX || (FP8 && PACKED), "mxfp4 runs on the tiled e4m3 path");
   using C = Big<BM, NW, FP8, GEMM_A>;
   constexpr int TN = C::kTN, TM = C::kTM, KS = C::kKS, HALF = C::kHalf;
+  static_assert(!MX || (TM >= TN && HALF % 32 == 0), "mxfp4 step and h block layout");
   __shared__ __attribute__((aligned(16))) uint8_t s_a[2][C::kAStage];
-  __shared__ float s_as[2][FP8 ? BM : 1];
-  __shared__ float s_rt[2][FP8 && PACKED ? BM : 1];  // fp8: a_s(previous step) / a_s(this step) per row
+  __shared__ float s_as[2][FP8 && !MX ? BM : 1];
+  __shared__ uint32_t s_ax[2][MX ? BM : 1];          // mxfp4: a row's 4 E8M0 bytes of a step
+  __shared__ float s_rt[2][FP8 && PACKED && !MX ? BM : 1];  // fp8: a_s(previous step) / a_s(this step) per row
   // GEMM Y: each wave's 64 rows x 64 columns of bf16 output on their way out
   __shared__ __attribute__((aligned(16))) uint8_t s_ystage[GEMM_A ? 16 : NW * 8192];
   // GEMM A: the block's BM x 256 tile of h on its way out
   __shared__ __attribute__((aligned(16))) uint8_t s_hstage[GEMM_A ? BM * (FP8 ? 256 : 512) : 16];
-  __shared__ float s_red[FP8 && GEMM_A ? NW : 1][FP8 && GEMM_A ? BM : 1];
+  __shared__ float s_red[FP8 && GEMM_A && !MX ? NW : 1][FP8 && GEMM_A && !MX ? BM : 1];
   __shared__ int s_go;
 
   const int tid = threadIdx.x;
@@ -500,8 +518,14 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
       aoff[i] = (uint32_t)(c >> 3) * lda + (uint32_t)(c & 7) * 16u;
     }
     const float* bsx = nullptr;
-    if constexpr (FP8) bsx = a.B_s + (int64_t)e * a.bs_expert;
-    const __amdgpu_buffer_rsrc_t bsr = make_rsrc(bsx, FP8 ? (uint32_t)(a.bs_expert * 4) : 0u);
+    if constexpr (FP8 && !MX) bsx = a.B_s + (int64_t)e * a.bs_expert;
+    const __amdgpu_buffer_rsrc_t bsr =
+        MX ? make_rsrc(a.B_e8 + (int64_t)e * a.b_e8_expert, (uint32_t)a.b_e8_expert)
+           : make_rsrc(bsx, FP8 ? (uint32_t)(a.bs_expert * 4) : 0u);
+    // mxfp4 weight fragments [buffer][tile] (16 bytes: 32 e2m1 codes) and scale bytes
+    u32x4 rbf[MX ? 2 : 1][MX ? TN : 1];
+    uint32_t rsb[MX ? 2 : 1][MX ? TN : 1];
+    uint32_t rax = 0;   // mxfp4: this thread's row's 4 A scale bytes of the step in flight
     // fp8 weight tile halves [buffer][tile][half] (16 bytes each: a 32-byte MFMA operand)
     u32x4 rbh[FP8 ? 2 : 1][FP8 ? TN : 1][2];
 
@@ -611,7 +635,22 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
       // branch-free (a branch here would split the step into blocks, and the compiler
       // then hoists every LDS read of the step above its MFMAs): threads past the
       // tile's rows read, and later store, the last row's scale again
-      ras[0] = a.A_s[(int64_t)(m0 + min(tid, BM - 1)) * a.s_kblocks + ks];
+      if constexpr (MX)
+        rax = *reinterpret_cast<const uint32_t*>(a.A_e8 + (int64_t)(m0 + min(tid, BM - 1)) * a.e8_lda + 4 * ks);
+      else
+        ras[0] = a.A_s[(int64_t)(m0 + min(tid, BM - 1)) * a.s_kblocks + ks];
+    };
+    // mxfp4: tile tn's fragment and scale byte of step ks into buffer BUF
+    auto load_bmx = [&](auto BUF, int tn, int ks) {
+      constexpr int bb = decltype(BUF)::value;
+      const uint32_t rowblk = (uint32_t)((tn < TN / 2 ? rbase0 : rbase1) + (tn % (TN / 2)) * 16) >> 4;
+      const uint32_t tix = rowblk * (uint32_t)a.ktiles + (uint32_t)ks;
+      rbf[bb][tn] = __builtin_amdgcn_raw_buffer_load_b128(br, (uint32_t)lane * 16u, tix * 1024u, 0);
+      rsb[bb][tn] = __builtin_amdgcn_raw_buffer_load_b8(bsr, (uint32_t)lane, tix * 64u, 0);
+    };
+    auto stage_mx = [&](auto STAGE) {
+      constexpr int st = decltype(STAGE)::value;
+      s_ax[st][min(tid, BM - 1)] = rax;
     };
     auto load_sb = [&](auto BUF, int ks) {
       constexpr int bb = decltype(BUF)::value;
@@ -643,7 +682,13 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
 
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    if constexpr (FP8 && PACKED) {
+    if constexpr (MX) {
+      dma_a(I0{}, 0);
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) load_bmx(I0{}, tn, 0);
+      wait_vm0();
+      stage_mx(I0{});
+    } else if constexpr (FP8 && PACKED) {
       dma_a(I0{}, 0);
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) {
@@ -779,6 +824,52 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     };
 
+    // mxfp4 step: 8 groups (row tile tm) of TN scaled MFMAs, no fp32 rescaling. The
+    // next step's weight fragments and scale bytes go out over the first TN groups,
+    // its A rows (LDS-DMA) and A scales in group 0; fragments and the lane's A scale
+    // byte are read from LDS one group ahead.
+    auto step_mx = [&](auto BUF, int ks) {
+      constexpr int bb = decltype(BUF)::value;
+      using NB = std::integral_constant<int, bb ^ 1>;
+      const int kn = ks + 1 < nk ? ks + 1 : ks;
+      const uint8_t* sa = &s_a[bb][0];
+      const uint8_t* sx = reinterpret_cast<const uint8_t*>(&s_ax[bb][0]);
+      __builtin_amdgcn_sched_barrier(0);
+      auto rd_a = [&](int tm) {
+        const int r = tm * 16 + l16;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(sa + swz_a(r, lhi));
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(sa + swz_a(r, lhi + 4));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      u32x8_t fa_cur = rd_a(0);
+      uint32_t xs_cur = sx[l16 * 4 + lhi];
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+        u32x8_t fa_next = fa_cur;
+        uint32_t xs_next = xs_cur;
+        if (tm + 1 < TM) {
+          fa_next = rd_a(tm + 1);
+          xs_next = sx[((tm + 1) * 16 + l16) * 4 + lhi];
+        }
+        if (tm == 0) dma_a(NB{}, kn);
+        if (tm < TN) load_bmx(NB{}, tm, kn);
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const u32x8_t fb = __builtin_shufflevector(rbf[bb][tn], rbf[bb][tn], 0, 1, 2, 3, -1, -1, -1, -1);
+          acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              __builtin_bit_cast(i32x8_t, fb), __builtin_bit_cast(i32x8_t, fa_cur), acc[tm][tn], 4, 0, 0,
+              (int)rsb[bb][tn], 0, (int)xs_cur);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        fa_cur = fa_next;
+        xs_cur = xs_next;
+      }
+      wait_vm0();
+      stage_mx(NB{});
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
     // bf16 step: 16 groups (K half kk, row tile tm) of TN MFMAs. The next step's loads
     // are spread over the groups instead of issued as one burst (a wave issues in
     // order, and a burst of vector loads would hold it off its MFMAs until the
@@ -817,7 +908,10 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
     };
 
     for (int ks = 0; ks < nk; ks += 2) {
-      if constexpr (FP8 && PACKED) {
+      if constexpr (MX) {
+        step_mx(std::integral_constant<int, 0>{}, ks);
+        step_mx(std::integral_constant<int, 1>{}, ks + 1);
+      } else if constexpr (FP8 && PACKED) {
         step_fp8(std::integral_constant<int, 0>{}, ks);
         step_fp8(std::integral_constant<int, 1>{}, ks + 1);
       } else if constexpr (!FP8 && TM >= TN + 1) {
@@ -830,7 +924,9 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
     }
 
     // ---------------- epilogue: lane holds row tm*16+l16, columns 4*lhi + (0..3) of each tile
-    if constexpr (FP8 && PACKED) {
+    if constexpr (MX) {
+      // block scales were applied by the MFMAs
+    } else if constexpr (FP8 && PACKED) {
       // the last step's scales (its stage, and the reloaded copy in the other one)
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
@@ -876,6 +972,37 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
             v.y = pack_bf16x2(silu_mul(acc[tm][tn][2], acc[tm][tn + TN / 2][2]),
                               silu_mul(acc[tm][tn][3], acc[tm][tn + TN / 2][3]));
             *reinterpret_cast<u32x2*>(hst(r, hb0 + tn * 32)) = v;
+          }
+        }
+        __syncthreads();
+        hstore();
+      } else if constexpr (MX) {
+        // MXFP8 h: a 1x32 block of a row = gate tiles 2b, 2b+1 of one wave, spread
+        // over the row's 4 lanes (lhi): amax by two cross-lane steps, no LDS
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+          const int rl = tm * 16 + l16;
+#pragma unroll
+          for (int bi = 0; bi < HALF / 32; ++bi) {
+            float am = 0.f;
+#pragma unroll
+            for (int tn = 2 * bi; tn < 2 * bi + 2; ++tn)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float h = silu_mul(acc[tm][tn][i], acc[tm][tn + TN / 2][i]);
+                acc[tm][tn][i] = h;
+                am = fmaxf(am, fabsf(h));
+              }
+            am = fmaxf(am, __shfl_xor(am, 16));
+            am = fmaxf(am, __shfl_xor(am, 32));
+            const int ex = mx_e4m3_shared_exp(am);
+            const float inv = mx_inv_scale(ex);
+#pragma unroll
+            for (int tn = 2 * bi; tn < 2 * bi + 2; ++tn)
+              *reinterpret_cast<uint32_t*>(hst(rl, hb0 + tn * 16)) =
+                  pack_e4m3x4(acc[tm][tn][0] * inv, acc[tm][tn][1] * inv, acc[tm][tn][2] * inv, acc[tm][tn][3] * inv);
+            if (lhi == 0)
+              a.out_e8[(int64_t)(m0 + rl) * a.e8_ldo + ((j * 256 + wn * HALF) >> 5) + bi] = (uint8_t)(ex + 127);
           }
         }
         __syncthreads();
@@ -979,12 +1106,34 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const uint8_t* w, uin
 
 int launch_pack_weights(const void* w, int32_t E, int32_t rows, int32_t K, int32_t dtype, void* out,
                         hipStream_t stream) {
+  // an MXFP4 tile (16 rows x 64 bytes, lane l = row l%16, bytes 16*(l/16)..+16) has
+  // the byte layout of a bf16 one
   const bool fp8 = dtype == MOE_FP8_E4M3_G128;
-  const int32_t row_bytes = K * (fp8 ? 1 : 2);
+  const int32_t row_bytes = dtype == MOE_MXFP4 ? K / 2 : K * (fp8 ? 1 : 2);
   const int64_t chunks = (int64_t)E * rows * row_bytes / 16;
   const int64_t blocks = (chunks + 255) / 256;
   hipLaunchKernelGGL(pack_weights_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                      static_cast<const uint8_t*>(w), static_cast<uint8_t*>(out), chunks, row_bytes, (int)fp8);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+// MXFP4 scale permutation (layout in moe355.h): one thread per destination byte.
+__global__ __launch_bounds__(256) void pack_mx_scales_kernel(const uint8_t* s, uint8_t* out, int64_t n,
+                                                             int32_t kblocks) {
+  const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (o >= n) return;
+  const int l = (int)(o & 63);
+  const int64_t tile = o >> 6;
+  const int ktiles = kblocks / 4;
+  const int64_t rb = tile / ktiles;            // global row block (experts stacked)
+  const int kb = (int)(tile - rb * ktiles);
+  out[o] = s[(rb * 16 + (l & 15)) * kblocks + kb * 4 + (l >> 4)];
+}
+
+int launch_pack_mx_scales(const void* s, int32_t E, int32_t rows, int32_t K, void* out, hipStream_t stream) {
+  const int64_t n = (int64_t)E * rows * (K / 32);
+  hipLaunchKernelGGL(pack_mx_scales_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                     static_cast<const uint8_t*>(s), static_cast<uint8_t*>(out), n, K / 32);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -994,11 +1143,11 @@ int launch_pack_weights(const void* w, int32_t E, int32_t rows, int32_t K, int32
 // The big-tile kernel wants whole 256 (gate) + 256 (up) and 512-column units and an
 // even number of 128-byte K steps; in fp8 it reads tiled weights only, at tile 128.
 static bool big_a_ok(int32_t H, int32_t I, int32_t dtype, int32_t tile) {
-  if (dtype == MOE_FP8_E4M3_G128) return tile == 128 && I % 256 == 0 && H % 256 == 0;
+  if (dtype == MOE_FP8_E4M3_G128 || dtype == MOE_MXFP4) return tile == 128 && I % 256 == 0 && H % 256 == 0;
   return dtype == MOE_BF16 && (tile == 64 || tile == 128) && I % 256 == 0 && H % 128 == 0;
 }
 static bool big_y_ok(int32_t H, int32_t I, int32_t dtype, int32_t tile) {
-  if (dtype == MOE_FP8_E4M3_G128) return tile == 128 && H % 512 == 0 && I % 256 == 0;
+  if (dtype == MOE_FP8_E4M3_G128 || dtype == MOE_MXFP4) return tile == 128 && H % 512 == 0 && I % 256 == 0;
   return dtype == MOE_BF16 && (tile == 64 || tile == 128) && H % 512 == 0 && I % 128 == 0;
 }
 
@@ -1022,6 +1171,12 @@ int ffn_supported(int32_t H, int32_t I, int32_t dtype, int32_t tile, int32_t blo
     if (H % 256 != 0 || I % 128 != 0 || tile < 64) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
   }
+  if (dtype == MOE_MXFP4) {
+    // the big-tile kernel with tiled weights is the only mxfp4 path
+    if (weight_layout != MOE_WEIGHTS_MFMA_TILED || !(big_a && big_y) || (block_n != 0 && block_n != 512))
+      return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+  }
   return MOE_ERR_INVALID;
 }
 
@@ -1041,6 +1196,14 @@ static int launch_big(int tile, const FfnArgs& a, int grid, hipStream_t s) {
   if (tile == 128) hipLaunchKernelGGL((ffn_big_kernel<128, NW, FP8, GEMM_A, PACKED>), dim3(grid), dim3(64 * NW), 0, s, a);
   else if (tile == 64) hipLaunchKernelGGL((ffn_big_kernel<64, NW, FP8, GEMM_A, PACKED>), dim3(grid), dim3(64 * NW), 0, s, a);
   else return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+template <bool GEMM_A>
+static int launch_mx(int tile, int bn, bool packed, const FfnArgs& a, int grid, hipStream_t s) {
+  if (bn != 512 || !packed || tile != 128) return MOE_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL((ffn_big_kernel<128, kBigWaves, true, GEMM_A, true, true>), dim3(grid), dim3(64 * kBigWaves), 0,
+                     s, a);
   return MOE_OK;
 }
 
@@ -1081,6 +1244,10 @@ static int launch_shape(int tile, int bn, bool packed, const FfnArgs& a, int gri
 // N block of each GEMM: the big-tile kernel (512) where the shape allows it,
 // else the largest the general kernel takes, unless overridden.
 static void pick_block_n(const FfnLaunch& f, int tile, int& bn_a, int& bn_y) {
+  if (f.dtype == MOE_MXFP4) {
+    bn_a = bn_y = 512;
+    return;
+  }
   const bool fp8 = f.dtype == MOE_FP8_E4M3_G128;
   const bool tiled = f.weight_layout == MOE_WEIGHTS_MFMA_TILED;
   // fp8 reaches the big-tile kernel only with tiled weights
@@ -1102,12 +1269,14 @@ static void pick_block_n(const FfnLaunch& f, int tile, int& bn_a, int& bn_y) {
 int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream_t stream) {
   const moe_plan_t& p = *f.plan;
   const bool fp8 = f.dtype == MOE_FP8_E4M3_G128;
+  const bool mx = f.dtype == MOE_MXFP4;
   const int H = f.H, I = f.I, tile = p.tile;
-  const int eb = fp8 ? 1 : 2;  // bytes per element
+  const int eb = fp8 || mx ? 1 : 2;  // bytes per activation element
   int bn_a, bn_y;
   pick_block_n(f, tile, bn_a, bn_y);
   uint8_t* h = reinterpret_cast<uint8_t*>(ws + L.h);
   float* hs = fp8 ? reinterpret_cast<float*>(ws + L.hs) : nullptr;
+  uint8_t* hs8 = mx ? reinterpret_cast<uint8_t*>(ws + L.hs) : nullptr;
   const int ntiles_cap = std::min(p.rows_cap, f.pool_rows) / tile;
 
   FfnArgs a{};
@@ -1124,14 +1293,20 @@ int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream
 
   // GEMM A: pool x w1^T -> SwiGLU -> h
   a.A = static_cast<const uint8_t*>(f.pool);
-  a.A_s = f.pool_s;
+  a.A_s = fp8 ? static_cast<const float*>(f.pool_s) : nullptr;
   a.B = static_cast<const uint8_t*>(f.w1);
-  a.B_s = f.w1_s;
+  a.B_s = fp8 ? static_cast<const float*>(f.w1_s) : nullptr;
   a.out = h;
   a.out_s = hs;
+  a.A_e8 = mx ? static_cast<const uint8_t*>(f.pool_s) : nullptr;
+  a.B_e8 = mx ? static_cast<const uint8_t*>(f.w1_s) : nullptr;
+  a.out_e8 = hs8;
+  a.e8_lda = H / 32;
+  a.b_e8_expert = (int64_t)2 * I * (H / 32);
+  a.e8_ldo = I / 32;
   a.ksteps = H * eb / 128;
   a.lda = (int64_t)H * eb;
-  a.b_expert = (int64_t)2 * I * H * eb;
+  a.b_expert = mx ? (int64_t)2 * I * (H / 2) : (int64_t)2 * I * H * eb;
   a.ldb = (int64_t)H * eb;
   a.up_row0 = I;
   a.ldo = (int64_t)I * eb;
@@ -1147,9 +1322,10 @@ int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream
   int ga = (int)std::min<int64_t>(grid, (int64_t)ntiles_cap * a.n_units);
   if (ga < 1) ga = 1;
   const bool packed = f.weight_layout == MOE_WEIGHTS_MFMA_TILED;
-  a.ktiles = H / (fp8 ? 128 : 32);
-  int rc = fp8 ? launch_shape<true, true>(tile, bn_a, packed, a, ga, stream)
-               : launch_shape<false, true>(tile, bn_a, packed, a, ga, stream);
+  a.ktiles = H / (fp8 || mx ? 128 : 32);
+  int rc = mx    ? launch_mx<true>(tile, bn_a, packed, a, ga, stream)
+           : fp8 ? launch_shape<true, true>(tile, bn_a, packed, a, ga, stream)
+                 : launch_shape<false, true>(tile, bn_a, packed, a, ga, stream);
   if (rc != MOE_OK) return rc;
   if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
 
@@ -1157,12 +1333,17 @@ int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream
   a.A = h;
   a.A_s = hs;
   a.B = static_cast<const uint8_t*>(f.w2);
-  a.B_s = f.w2_s;
+  a.B_s = fp8 ? static_cast<const float*>(f.w2_s) : nullptr;
   a.out = static_cast<uint8_t*>(f.y_pool);
   a.out_s = nullptr;
+  a.A_e8 = hs8;
+  a.B_e8 = mx ? static_cast<const uint8_t*>(f.w2_s) : nullptr;
+  a.out_e8 = nullptr;
+  a.e8_lda = I / 32;
+  a.b_e8_expert = (int64_t)H * (I / 32);
   a.ksteps = I * eb / 128;
   a.lda = (int64_t)I * eb;
-  a.b_expert = (int64_t)H * I * eb;
+  a.b_expert = mx ? (int64_t)H * (I / 2) : (int64_t)H * I * eb;
   a.ldb = (int64_t)I * eb;
   a.up_row0 = 0;
   a.ldo = (int64_t)H * 2;
@@ -1174,9 +1355,10 @@ int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream
   a.unit_order = bn_y == 512 ? (f.unit_order ? f.unit_order : 3) : 1;
   int gy = (int)std::min<int64_t>(grid, (int64_t)ntiles_cap * a.n_units);
   if (gy < 1) gy = 1;
-  a.ktiles = I / (fp8 ? 128 : 32);
-  rc = fp8 ? launch_shape<true, false>(tile, bn_y, packed, a, gy, stream)
-           : launch_shape<false, false>(tile, bn_y, packed, a, gy, stream);
+  a.ktiles = I / (fp8 || mx ? 128 : 32);
+  rc = mx    ? launch_mx<false>(tile, bn_y, packed, a, gy, stream)
+       : fp8 ? launch_shape<true, false>(tile, bn_y, packed, a, gy, stream)
+             : launch_shape<false, false>(tile, bn_y, packed, a, gy, stream);
   if (rc != MOE_OK) return rc;
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

@@ -11,18 +11,18 @@ int launch_plan(const int32_t* topk_idx, const moe_plan_t& p, const WsLayout& L,
                 hipStream_t stream);
 
 int launch_dispatch(const void* x, int32_t H, int32_t dtype, const moe_plan_t& p, int32_t pool_rows,
-                    void* pool, float* pool_s, uint32_t epoch, const WsLayout& L, char* ws,
+                    void* pool, void* pool_s, uint32_t epoch, const WsLayout& L, char* ws,
                     hipStream_t stream);
 
 struct FfnLaunch {
   const moe_plan_t* plan;
   int32_t pool_rows;
   const void* pool;
-  const float* pool_s;
+  const void* pool_s;   // fp8: float group scales; mxfp4: E8M0 bytes
   const void* w1;
-  const float* w1_s;
+  const void* w1_s;     // fp8: float block scales; mxfp4: packed E8M0 bytes
   const void* w2;
-  const float* w2_s;
+  const void* w2_s;
   int32_t H, I, dtype;
   uint32_t epoch;
   void* y_pool;
@@ -43,6 +43,8 @@ int ffn_supported(int32_t H, int32_t I, int32_t dtype, int32_t tile, int32_t blo
 
 int launch_pack_weights(const void* w, int32_t E, int32_t rows, int32_t K, int32_t dtype, void* out,
                         hipStream_t stream);
+
+int launch_pack_mx_scales(const void* s, int32_t E, int32_t rows, int32_t K, void* out, hipStream_t stream);
 
 int device_cu_count();
 

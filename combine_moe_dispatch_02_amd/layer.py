@@ -15,13 +15,14 @@ from typing import Optional, Tuple
 import torch
 
 from . import _abi
-from ._abi import (MOE_BF16, MOE_FP8_E4M3_G128, MOE_WEIGHTS_MFMA_TILED, MOE_WEIGHTS_ROW_MAJOR, MoeError,
-                   PlanT, TileConfig, check, load)
+from ._abi import (MOE_BF16, MOE_FP8_E4M3_G128, MOE_MXFP4, MOE_WEIGHTS_MFMA_TILED, MOE_WEIGHTS_ROW_MAJOR,
+                   MoeError, PlanT, TileConfig, check, load)
 
 __all__ = [
-    "MOE_BF16", "MOE_FP8_E4M3_G128", "MoeError", "Plan", "Workspace", "TileConfig",
+    "MOE_BF16", "MOE_FP8_E4M3_G128", "MOE_MXFP4", "MoeError", "Plan", "Workspace", "TileConfig",
     "pool_rows_upper_bound", "workspace_bytes", "moe_plan", "moe_query_pool_rows",
     "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_get_error", "moe_pack_weights",
+    "moe_pack_mx_scales",
     "device_cu_count", "MOE_WEIGHTS_ROW_MAJOR", "MOE_WEIGHTS_MFMA_TILED",
     "make_streams", "StreamMoE", "stream_moe",
 ]
@@ -44,7 +45,12 @@ def _dtype_code(dtype) -> int:
         return MOE_BF16
     if dtype in ("fp8", MOE_FP8_E4M3_G128):
         return MOE_FP8_E4M3_G128
+    if dtype in ("mxfp4", MOE_MXFP4):
+        return MOE_MXFP4
     raise ValueError(f"dtype {dtype!r}")
+
+
+_DTYPE_NAMES = {MOE_BF16: "bf16", MOE_FP8_E4M3_G128: "fp8", MOE_MXFP4: "mxfp4"}
 
 
 def _need_cuda(t: torch.Tensor, name: str, dtype=None):
@@ -158,8 +164,13 @@ def moe_expert_ffn(plan: Plan, pool: torch.Tensor, pool_s: Optional[torch.Tensor
                    dtype="bf16", cfg: Optional[TileConfig] = None, stream=None) -> None:
     for t, n in ((pool, "pool"), (w1, "w1"), (w2, "w2"), (y_pool, "y_pool")):
         _need_cuda(t, n)
+    code = _dtype_code(dtype)
     E, twoI, H = w1.shape
-    if E != plan.E_local or w2.shape != (E, H, twoI // 2):
+    if code == MOE_MXFP4:          # packed e2m1: two codes per byte along K
+        H *= 2
+        if E != plan.E_local or w2.shape != (E, H, twoI // 4):
+            raise ValueError("mxfp4 w1 [E_local, 2I, H/2] / w2 [E_local, H, I/2] shapes do not match")
+    elif E != plan.E_local or w2.shape != (E, H, twoI // 2):
         raise ValueError("w1 [E_local, 2I, H] / w2 [E_local, H, I] shapes do not match")
     if y_pool.shape[0] != pool.shape[0] or y_pool.shape[1] != H:
         raise ValueError("y_pool must be [pool rows, H]")
@@ -167,7 +178,7 @@ def moe_expert_ffn(plan: Plan, pool: torch.Tensor, pool_s: Optional[torch.Tensor
     cfgp = ctypes.byref(cfg) if cfg is not None else None
     check("moe_expert_ffn", load().moe_expert_ffn(
         ctypes.byref(c), pool.shape[0], _vp(pool), _vp(pool_s), _vp(w1), _vp(w1_s), _vp(w2),
-        _vp(w2_s), H, twoI // 2, _dtype_code(dtype), epoch, _vp(ws.buf), ws.nbytes, _vp(y_pool),
+        _vp(w2_s), H, twoI // 2, code, epoch, _vp(ws.buf), ws.nbytes, _vp(y_pool),
         cfgp, _stream(stream)))
 
 
@@ -184,12 +195,25 @@ def moe_combine(y_pool: torch.Tensor, topk_weights: torch.Tensor, plan: Plan, ou
 
 
 def moe_pack_weights(w: torch.Tensor, dtype="bf16", stream=None) -> torch.Tensor:
-    """Permute expert weights [E, rows, K] into MFMA fragment order (a new tensor)."""
+    """Permute expert weights [E, rows, K] (mxfp4: packed codes [E, rows, K/2]) into MFMA
+    fragment order (a new tensor)."""
     _need_cuda(w, "w")
     E, rows, K = w.shape
+    if _dtype_code(dtype) == MOE_MXFP4:
+        K *= 2
     out = torch.empty_like(w)
     check("moe_pack_weights", load().moe_pack_weights(_vp(w), E, rows, K, _dtype_code(dtype), _vp(out),
                                                       _stream(stream)))
+    return out
+
+
+def moe_pack_mx_scales(s: torch.Tensor, stream=None) -> torch.Tensor:
+    """Permute MXFP4 weight scales [E, rows, K/32] (E8M0 bytes) into the scaled MFMA's
+    operand order (a new tensor)."""
+    _need_cuda(s, "s", torch.uint8)
+    E, rows, kb = s.shape
+    out = torch.empty_like(s)
+    check("moe_pack_mx_scales", load().moe_pack_mx_scales(_vp(s), E, rows, kb * 32, _vp(out), _stream(stream)))
     return out
 
 
@@ -214,13 +238,15 @@ class StreamMoE:
                  weight_layout: str = "auto"):
         self.T, self.H, self.I, self.K = T, H, I, K
         self.E_local, self.expert_begin, self.tile = num_local_experts, expert_begin, tile
-        self.dtype = "fp8" if _dtype_code(dtype) == MOE_FP8_E4M3_G128 else "bf16"
+        self.dtype = _DTYPE_NAMES[_dtype_code(dtype)]
         # tiled weights feed the big-tile kernel, which needs whole 512-column blocks
-        # (bf16: tile 64 or 128; fp8: tile 128)
+        # (bf16: tile 64 or 128; fp8, mxfp4: tile 128); mxfp4 runs there only
         tiles_ok = tile in (64, 128) if self.dtype == "bf16" else tile == 128
         tiled_ok = (tiles_ok and I % 256 == 0 and H % 512 == 0
                     and (cfg is None or cfg.block_n in (0, 512)))
-        if weight_layout == "tiled" and not tiled_ok:
+        if (weight_layout == "tiled" or self.dtype == "mxfp4") and not tiled_ok:
+            raise MoeError("StreamMoE", _abi.MOE_ERR_UNSUPPORTED)
+        if self.dtype == "mxfp4" and weight_layout == "row_major":
             raise MoeError("StreamMoE", _abi.MOE_ERR_UNSUPPORTED)
         self.tiled = weight_layout == "tiled" or (weight_layout == "auto" and tiled_ok)
         if cfg is None:
@@ -231,19 +257,28 @@ class StreamMoE:
         rows = pool_rows or self.plan.rows_cap
         self.pool_rows = rows
         self.ws = Workspace(T, K, num_local_experts, tile, rows, I, self.dtype, device)
-        fp8 = self.dtype == "fp8"
-        self.pool = torch.empty(rows, H, dtype=torch.uint8 if fp8 else torch.bfloat16, device=device)
-        self.pool_s = torch.empty(rows, H // 128, dtype=torch.float32, device=device) if fp8 else None
+        if self.dtype == "bf16":
+            self.pool = torch.empty(rows, H, dtype=torch.bfloat16, device=device)
+            self.pool_s = None
+        elif self.dtype == "fp8":
+            self.pool = torch.empty(rows, H, dtype=torch.uint8, device=device)
+            self.pool_s = torch.empty(rows, H // 128, dtype=torch.float32, device=device)
+        else:
+            self.pool = torch.empty(rows, H, dtype=torch.uint8, device=device)
+            self.pool_s = torch.empty(rows, H // 32, dtype=torch.uint8, device=device)
         self.y_pool = torch.empty(rows, H, dtype=torch.bfloat16, device=device)
         self.out = torch.empty(T, H, dtype=torch.bfloat16, device=device)
         self.epoch = 0
 
-    def prepare_weights(self, w1, w2):
-        """The weights as forward() wants them: permuted once into MFMA fragment order when the
-        layer uses tiled weights (a load-time step, like any weight preprocessing), else as is."""
+    def prepare_weights(self, w1, w2, w1_scale=None, w2_scale=None):
+        """(w1, w2, w1_scale, w2_scale) as forward() wants them: permuted once into MFMA fragment
+        order when the layer uses tiled weights (a load-time step, like any weight
+        preprocessing), MXFP4 scales into operand order, else as is."""
         if not self.tiled:
-            return w1, w2
-        return moe_pack_weights(w1, self.dtype), moe_pack_weights(w2, self.dtype)
+            return w1, w2, w1_scale, w2_scale
+        if self.dtype == "mxfp4":
+            w1_scale, w2_scale = moe_pack_mx_scales(w1_scale), moe_pack_mx_scales(w2_scale)
+        return moe_pack_weights(w1, self.dtype), moe_pack_weights(w2, self.dtype), w1_scale, w2_scale
 
     def next_epoch(self) -> int:
         self.epoch = (self.epoch % 0xFFFFFFFF) + 1      # 1 .. 2^32-1; 0 is never a valid epoch
@@ -251,7 +286,7 @@ class StreamMoE:
 
     def forward(self, x, topk_idx, topk_weights, w1, w2, w1_scale=None, w2_scale=None,
                 streams=None) -> torch.Tensor:
-        """One layer. w1 / w2 come from prepare_weights(). ``streams=(compute, comm)`` runs
+        """One layer. Weights and scales come from prepare_weights(). ``streams=(compute, comm)`` runs
         plan/dispatch/combine on comm and the FFN on compute, ordered by events; None runs
         everything on the current stream."""
         if topk_idx.dtype != torch.int32:
@@ -290,22 +325,25 @@ _LAYERS = {}
 
 def stream_moe(x, topk_idx, topk_weights, w1_local, w2_local, *, expert_begin=0, tile=128,
                w1_scale=None, w2_scale=None, streams=None) -> torch.Tensor:
-    """Functional form: shapes come from the tensors (w1_local [E_local, 2I, H]). Returns a
-    fresh output tensor; buffers are cached per shape and device."""
+    """Functional form: shapes come from the tensors (w1_local [E_local, 2I, H]; uint8
+    w1_local [E_local, 2I, H/2] means MXFP4). Returns a fresh output tensor; buffers are
+    cached per shape and device."""
     T, H = x.shape
     K = topk_idx.shape[1]
     E, twoI, _ = w1_local.shape
-    fp8 = w1_local.dtype == torch.float8_e4m3fn
-    key = (T, H, twoI // 2, K, E, expert_begin, tile, fp8, x.device)
+    dtype = ("fp8" if w1_local.dtype == torch.float8_e4m3fn
+             else "mxfp4" if w1_local.dtype == torch.uint8 else "bf16")
+    key = (T, H, twoI // 2, K, E, expert_begin, tile, dtype, x.device)
     layer = _LAYERS.get(key)
     if layer is None:
         layer = StreamMoE(T, H, twoI // 2, K, E, expert_begin=expert_begin, tile=tile,
-                          dtype="fp8" if fp8 else "bf16", device=x.device)
+                          dtype=dtype, device=x.device)
         _LAYERS[key] = layer
-    wkey = (w1_local.data_ptr(), w1_local._version, w2_local.data_ptr(), w2_local._version)
+    wkey = tuple((t.data_ptr(), t._version) if t is not None else None
+                 for t in (w1_local, w2_local, w1_scale, w2_scale))
     if getattr(layer, "_wkey", None) != wkey:
         layer._wkey = wkey
-        layer._w = layer.prepare_weights(w1_local, w2_local)
-    w1p, w2p = layer._w
-    out = layer.forward(x, topk_idx, topk_weights, w1p, w2p, w1_scale, w2_scale, streams)
+        layer._w = layer.prepare_weights(w1_local, w2_local, w1_scale, w2_scale)
+    w1p, w2p, s1p, s2p = layer._w
+    out = layer.forward(x, topk_idx, topk_weights, w1p, w2p, s1p, s2p, streams)
     return out.clone()

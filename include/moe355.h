@@ -64,7 +64,10 @@ enum {
 /* Storage types of activations and weights. */
 enum {
   MOE_BF16 = 0,          /* bf16 activations and weights */
-  MOE_FP8_E4M3_G128 = 1  /* e4m3 activations per 1x128 group, e4m3 weights per 128x128 block */
+  MOE_FP8_E4M3_G128 = 1, /* e4m3 activations per 1x128 group, e4m3 weights per 128x128 block */
+  MOE_MXFP4 = 2          /* MXFP8 activations (e4m3 + E8M0 scale per 1x32 block along K) and
+                            MXFP4 weights (e2m1 codes, two per byte with the even K in the low
+                            nibble, + E8M0 scale per 1x32 block along K); the OCP MX formats */
 };
 
 /*
@@ -117,9 +120,10 @@ MOE355_API size_t moe_pool_rows_upper_bound(int32_t T, int32_t K, int32_t E_loca
 
 /* Bytes of the device workspace that moe_plan, moe_dispatch, moe_expert_ffn and
  * moe_get_error share for one layer: plan scratch, per-tile fill counters, the
- * device error word, and the intermediate h (pool_rows x I, bf16 or e4m3 + fp32
- * group scales). pool_rows = 0 means moe_pool_rows_upper_bound. Returns 0 for
- * invalid sizes. The workspace must be zero-filled once before its first use. */
+ * device error word, and the intermediate h (pool_rows x I: bf16, e4m3 + fp32
+ * 1x128 group scales, or e4m3 + E8M0 1x32 block scales). pool_rows = 0 means
+ * moe_pool_rows_upper_bound. Returns 0 for invalid sizes. The workspace must be
+ * zero-filled once before its first use. */
 MOE355_API size_t moe_workspace_bytes(int32_t T, int32_t K, int32_t E_local, int32_t tile,
                                       int32_t pool_rows, int32_t I, int32_t dtype);
 
@@ -146,24 +150,34 @@ MOE355_API int moe_query_pool_rows(const moe_plan_t* plan, int32_t* host_P, void
  * fp8:  pool is e4m3 [pool_rows][H] and pool_s fp32 [pool_rows][H/128]; each
  *       1x128 group g of x[t] is stored as codes e4m3(x/s) with s = amax/448
  *       (s = 1 for an all-zero group), rounded to nearest even and saturated.
+ * mxfp4: pool is e4m3 [pool_rows][H] and pool_s E8M0 bytes [pool_rows][H/32]
+ *       (MXFP8, OCP MX specification): per 1x32 block, e = floor(log2(amax)) - 8
+ *       clamped to [-127, 127] (-127 for an all-zero block), pool_s = e + 127,
+ *       codes e4m3(x * 2^-e) rounded to nearest even and saturated. The scaling is
+ *       exact, so the codes depend on x alone.
  * Padding rows are not written. After a tile's real rows are stored the tile's
  * tile_ready entry is set to `epoch` with release ordering (device scope).
  * epoch must be nonzero and should change from one layer call to the next.
  * A pair whose row is >= pool_rows is not written and records MOE_ERR_INVALID.
  * Errors: MOE_ERR_INVALID (null pointers, H < 8, epoch 0, bad dtype),
- * MOE_ERR_UNSUPPORTED (H % 8 != 0; fp8 with H % 128 != 0).
+ * MOE_ERR_UNSUPPORTED (H % 8 != 0; fp8 with H % 128 != 0; mxfp4 with H % 32 != 0).
  */
 MOE355_API int moe_dispatch(const void* x, int32_t H, int32_t act_dtype, const moe_plan_t* plan,
-                            int32_t pool_rows, void* pool, float* pool_s, uint32_t epoch,
+                            int32_t pool_rows, void* pool, void* pool_s, uint32_t epoch,
                             void* ws, size_t ws_bytes, void* stream);
 
 /*
  * A3 + A4. Expert FFN over the pool, as a persistent grouped GEMM on MFMA:
  *   GEMM A: g = pool_tile . w1[e]^T (fp32 accumulate), h = silu(g_gate) * g_up,
- *           silu(z) = z / (1 + exp(-z)); h is stored as bf16 (bf16 mode) or as
- *           e4m3 + one fp32 scale per 1x128 group (fp8 mode) in the workspace;
+ *           silu(z) = z / (1 + exp(-z)); h is stored as bf16 (bf16 mode), as
+ *           e4m3 + one fp32 scale per 1x128 group (fp8 mode), or as MXFP8 like
+ *           the pool (mxfp4 mode) in the workspace;
  *   GEMM Y: y_pool_tile = h . w2[e]^T (fp32 accumulate), stored bf16.
  * fp8 mode applies activation and weight scales per 128-wide K block in fp32.
+ * mxfp4 mode: pool_s is E8M0 [pool_rows][H/32]; w1 / w2 are MXFP4 codes in the
+ * tiled layout of moe_pack_weights and w1_s / w2_s their E8M0 scales in the
+ * layout of moe_pack_mx_scales; the scales are applied per 32-wide K block by
+ * the matrix cores (scaled MFMA), so no rescaling happens in fp32.
  * Each work unit waits until tile_ready of its tile equals `epoch` (acquire);
  * a wait longer than the timeout records MOE_ERR_TIMEOUT and skips the unit.
  * Rows of y_pool that are padding are computed from whatever the pool holds and
@@ -172,11 +186,12 @@ MOE355_API int moe_dispatch(const void* x, int32_t H, int32_t act_dtype, const m
  * Errors: MOE_ERR_INVALID (null pointers, bad dtype, epoch 0, small workspace,
  * pool_rows not a multiple of tile), MOE_ERR_UNSUPPORTED (bf16: H % 128 or
  * I % 64 nonzero; fp8: H % 256 or I % 128 nonzero, or tile < 64; tiled weights:
- * bf16 with tile 64 or 128, H % 512 == 0 and I % 256 == 0 only).
+ * bf16 with tile 64 or 128, H % 512 == 0 and I % 256 == 0 only; mxfp4: tiled
+ * weights, tile 128, H % 512 == 0 and I % 256 == 0 only).
  */
 MOE355_API int moe_expert_ffn(const moe_plan_t* plan, int32_t pool_rows, const void* pool,
-                              const float* pool_s, const void* w1, const float* w1_s, const void* w2,
-                              const float* w2_s, int32_t H, int32_t I, int32_t dtype, uint32_t epoch,
+                              const void* pool_s, const void* w1, const void* w1_s, const void* w2,
+                              const void* w2_s, int32_t H, int32_t I, int32_t dtype, uint32_t epoch,
                               void* ws, size_t ws_bytes, void* y_pool, const moe_tile_config* cfg,
                               void* stream);
 
@@ -196,21 +211,36 @@ MOE355_API int moe_combine(const void* y_pool, int32_t pool_rows, const float* t
 /*
  * Load-time weight permutation for the expert GEMMs (callers that cannot keep a
  * second copy of the weights use row-major weights instead). Copies w (device,
- * [E][rows][K] row-major, bf16 or e4m3 per dtype) into out (device, same size,
- * must not overlap w) in MFMA fragment order, so that every weight-fragment load
- * of the GEMM reads 1 KiB of contiguous memory:
+ * [E][rows][K] row-major: bf16, e4m3, or packed e2m1 [E][rows][K/2] per dtype)
+ * into out (device, same size, must not overlap w) in MFMA fragment order, so
+ * that every weight-fragment load of the GEMM reads 1 KiB of contiguous memory:
  *   bf16: for each expert, 16-row x 32-column tiles (row block rb, K block kb) at
  *         byte ((rb * K/32) + kb) * 1024; lane l (0..63) of a tile holds the 8
  *         values w[rb*16 + l%16][kb*32 + 8*(l/16) ..+8] at byte l*16.
  *   fp8:  16 x 128 tiles at ((rb * K/128) + kb) * 2048; half h (0,1) of lane l at
  *         byte h*1024 + l*16 holds w[rb*16 + l%16][kb*128 + 32*(l/16) + 16h ..+16].
+ *   mxfp4: 16 x 128 tiles at ((rb * K/128) + kb) * 1024; lane l at byte l*16 holds
+ *         the 32 codes w[rb*16 + l%16][kb*128 + 32*(l/16) ..+32] (16 bytes as
+ *         stored, low nibble first).
  * Values are moved, never changed. Use with moe_tile_config.weight_layout =
- * MOE_WEIGHTS_MFMA_TILED. Scales (fp8) keep their layout.
+ * MOE_WEIGHTS_MFMA_TILED. Scales keep their layout (fp8) or are permuted by
+ * moe_pack_mx_scales (mxfp4).
  * Errors: MOE_ERR_INVALID (null pointers, E/rows/K < 1, bad dtype),
- * MOE_ERR_UNSUPPORTED (rows % 16 != 0, K % 32 != 0 (bf16) or % 128 (fp8)).
+ * MOE_ERR_UNSUPPORTED (rows % 16 != 0, K % 32 != 0 (bf16) or % 128 (fp8, mxfp4)).
  */
 MOE355_API int moe_pack_weights(const void* w, int32_t E, int32_t rows, int32_t K, int32_t dtype, void* out,
                                 void* stream);
+
+/*
+ * Load-time permutation of MXFP4 weight scales (E8M0 bytes, device, [E][rows][K/32]
+ * row-major, one per 1x32 block along K) into the order the scaled MFMA takes them:
+ * for each expert, the 16-row x 128-K tile (rb, kb) owns 64 bytes at
+ * ((rb * K/128) + kb) * 64, and byte l holds s[rb*16 + l%16][kb*4 + l/16] (lane l's
+ * operand scale). out has the size of s and must not overlap it.
+ * Errors: MOE_ERR_INVALID (null pointers, E/rows/K < 1),
+ * MOE_ERR_UNSUPPORTED (rows % 16 != 0 or K % 128 != 0).
+ */
+MOE355_API int moe_pack_mx_scales(const void* s, int32_t E, int32_t rows, int32_t K, void* out, void* stream);
 
 /* Waits for `stream`, returns the first error recorded on the device in the
  * workspace since the last call (MOE_OK if none) and clears it. */

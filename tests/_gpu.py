@@ -7,7 +7,7 @@ import torch
 import combine_moe_dispatch_02_amd as moe
 import oracle
 
-TOL = {"bf16": 1e-2, "fp8": 3e-2}
+TOL = {"bf16": 1e-2, "fp8": 3e-2, "mxfp4": 3e-2}
 
 
 def say(*a):
@@ -23,7 +23,7 @@ def dev_inputs(inp):
         "w": inp.topk_weights.cuda(),
     }
     if inp.w1 is not None:
-        if inp.cfg.dtype == "fp8":
+        if inp.cfg.dtype in ("fp8", "mxfp4"):
             d["w1"] = inp.w1.view(torch.uint8).cuda()
             d["w2"] = inp.w2.view(torch.uint8).cuda()
             d["w1s"] = inp.w1_scale.cuda()
@@ -42,9 +42,9 @@ def make_layer(shape, **kw):
 
 def run_layer(layer, d, streams=None):
     if getattr(layer, "_test_w", None) is None:
-        layer._test_w = layer.prepare_weights(d["w1"], d["w2"])
-    w1, w2 = layer._test_w
-    out = layer.forward(d["x"], d["idx"], d["w"], w1, w2, d["w1s"], d["w2s"], streams)
+        layer._test_w = layer.prepare_weights(d["w1"], d["w2"], d["w1s"], d["w2s"])
+    w1, w2, w1s, w2s = layer._test_w
+    out = layer.forward(d["x"], d["idx"], d["w"], w1, w2, w1s, w2s, streams)
     torch.cuda.synchronize()
     rc = moe.moe_get_error(layer.ws)
     assert rc == 0, f"device error {rc}"

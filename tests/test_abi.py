@@ -28,7 +28,7 @@ def lib():
 def test_header_declares_the_four_calls():
     names = set(declared_symbols())
     assert {"moe_plan", "moe_dispatch", "moe_expert_ffn", "moe_combine"} <= names
-    assert len(names) == 11
+    assert len(names) == 12
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -64,7 +64,10 @@ def test_workspace_bytes(lib):
     assert plan_only > 0
     assert full_bf16 - plan_only >= rows * 1536 * 2
     assert full_fp8 - plan_only >= rows * 1536 + rows * 12 * 4
+    full_mx = lib.moe_workspace_bytes(16384, 8, 128, 128, 0, 1536, 2)
+    assert full_mx - plan_only >= rows * 1536 + rows * 48
     assert lib.moe_workspace_bytes(16, 2, 4, 16, 0, 100, 1) == 0     # fp8 needs I % 128 == 0
+    assert lib.moe_workspace_bytes(16, 2, 4, 16, 0, 48, 2) == 0      # mxfp4 needs I % 32 == 0
     assert lib.moe_workspace_bytes(16, 2, 4, 16, 0, 64, 7) == 0      # unknown dtype
 
 
@@ -117,6 +120,9 @@ def test_dispatch_validation(lib):
     assert lib.moe_dispatch(X, 100, 0, ctypes.byref(p), 248, POOL, None, 1, WS, big, None) == 2
     assert lib.moe_dispatch(X, 192, 1, ctypes.byref(p), 248, POOL, ctypes.c_void_p(8), 1, WS, big, None) == 2
     assert lib.moe_dispatch(X, 128, 5, ctypes.byref(p), 248, POOL, None, 1, WS, big, None) == 1
+    # mxfp4: needs its E8M0 buffer and whole 32-wide blocks
+    assert lib.moe_dispatch(X, 128, 2, ctypes.byref(p), 248, POOL, None, 1, WS, big, None) == 1
+    assert lib.moe_dispatch(X, 136, 2, ctypes.byref(p), 248, POOL, ctypes.c_void_p(8), 1, WS, big, None) == 2
 
 
 def test_ffn_validation(lib):
@@ -149,6 +155,11 @@ def test_ffn_validation(lib):
     assert call(cfg=ctypes.byref(cfg)) == 1        # unit walks are 0..9
     cfg = _abi.TileConfig(0, -1, 0, 0, 0)
     assert call(cfg=ctypes.byref(cfg)) == 1        # negative grid
+    mx = (v[5], v[6], v[7])
+    assert call(dtype=2) == 1                      # mxfp4 without scales
+    assert call(dtype=2, scales=mx) == 2           # mxfp4 runs on tiled weights only
+    tiled = _abi.TileConfig(0, 0, 0, 0, 1)
+    assert call(H=512, I=256, dtype=2, scales=mx, cfg=ctypes.byref(tiled)) == 2   # tile 128 only
 
 
 def test_combine_validation(lib):
@@ -167,6 +178,16 @@ def test_pack_weights_validation(lib):
     assert lib.moe_pack_weights(W, 1, 16, 48, 0, OUT, None) == 2      # bf16 K % 32
     assert lib.moe_pack_weights(W, 1, 16, 64, 1, OUT, None) == 2      # fp8 K % 128
     assert lib.moe_pack_weights(W, 4, 64, 256, 0, ctypes.c_void_p(0x10100), None) == 1  # overlap
+    assert lib.moe_pack_weights(W, 1, 16, 64, 2, OUT, None) == 2      # mxfp4 K % 128
+
+
+def test_pack_mx_scales_validation(lib):
+    S, OUT = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x100000000)
+    assert lib.moe_pack_mx_scales(None, 1, 16, 128, OUT, None) == 1
+    assert lib.moe_pack_mx_scales(S, 0, 16, 128, OUT, None) == 1
+    assert lib.moe_pack_mx_scales(S, 1, 24, 128, OUT, None) == 2     # rows % 16
+    assert lib.moe_pack_mx_scales(S, 1, 16, 96, OUT, None) == 2      # K % 128
+    assert lib.moe_pack_mx_scales(S, 2, 16, 256, ctypes.c_void_p(0x10040), None) == 1  # overlap
 
 
 def test_get_error_validation(lib):

@@ -1,5 +1,6 @@
 """A2 and A5 on the GPU, without the FFN:
-* dispatch writes exactly the oracle's pool rows (bf16 bits; e4m3 codes and scales),
+* dispatch writes exactly the oracle's pool rows (bf16 bits; e4m3 codes and fp32 group
+  scales; MXFP8 e4m3 codes and E8M0 block scales),
   leaves poisoned padding rows alone, and raises every tile's ready flag;
 * with identity experts (y_pool = pool) combine returns sum_k w_k x_t, and with
   K = 1, w = 1 the dispatch -> combine round trip is bit-exact."""
@@ -18,20 +19,24 @@ pytestmark = pytest.mark.gpu
 POISON = 0x7FC1  # a bf16 NaN pattern
 
 
-def plan_and_dispatch(inp, epoch=5, fp8=False):
+def plan_and_dispatch(inp, epoch=5, fp8=False, dtype=None):
     c = inp.cfg
+    dtype = dtype or ("fp8" if fp8 else "bf16")
     plan = moe.Plan.allocate(c.T, c.K, c.expert_begin, c.num_local_experts, c.tile)
     ws = moe.Workspace(c.T, c.K, c.num_local_experts, c.tile)
     rows = plan.rows_cap
-    if fp8:
+    if dtype == "fp8":
         pool = torch.full((rows, c.H), 0x7F, dtype=torch.uint8, device="cuda")
         pool_s = torch.full((rows, c.H // 128), -1.0, dtype=torch.float32, device="cuda")
+    elif dtype == "mxfp4":
+        pool = torch.full((rows, c.H), 0x7F, dtype=torch.uint8, device="cuda")
+        pool_s = torch.full((rows, c.H // 32), 0xFF, dtype=torch.uint8, device="cuda")
     else:
         pool = torch.full((rows, c.H), POISON, dtype=torch.int16, device="cuda").view(torch.bfloat16)
         pool_s = None
     x = inp.x.cuda()
     moe.moe_plan(inp.topk_idx.cuda(), plan, ws)
-    moe.moe_dispatch(x, plan, pool, pool_s, epoch, ws, "fp8" if fp8 else "bf16")
+    moe.moe_dispatch(x, plan, pool, pool_s, epoch, ws, dtype)
     torch.cuda.synchronize()
     assert moe.moe_get_error(ws) == 0
     return plan, ws, pool, pool_s
@@ -107,6 +112,44 @@ def test_dispatch_fp8_full_size_sampled_rows():
     rng = np.random.default_rng(0)
     rows = np.sort(rng.choice(np.nonzero(src >= 0)[0], 256, replace=False))
     codes, scales = oracle.token_rows(inp.x, True, src[rows] // cfg.K)
+    assert np.array_equal(pool.cpu().numpy()[rows], codes)
+    assert np.array_equal(pool_s.cpu().numpy()[rows], scales)
+
+
+MX = [
+    MoEConfig("mx_small", 300, 512, 128, 10, 0, 10, 4, 64, "mxfp4"),
+    MoEConfig("mx_ragged", 129, 1184, 128, 7, 2, 4, 3, 128, "mxfp4"),    # 37 blocks: a partial lane sweep
+]
+
+
+@pytest.mark.parametrize("cfg", MX, ids=[c.name for c in MX])
+def test_dispatch_mxfp8_codes_and_scales_exact(cfg):
+    inp = make_inputs(cfg, weights=False)
+    inp.x[3, 32:64] = 0                                       # an all-zero block
+    inp.x[5, 7] = -2.5e30                                     # a huge value
+    inp.x[5, 40] = 256.0                                      # amax exactly a power of two
+    inp.x[5, 41:64] = 0
+    inp.x[6, 64:96] = torch.linspace(-1e-39, 1e-39, 32)      # bf16 subnormals only: clamped scale
+    inp.x[7, :32] = 3.0e-38
+    say("dispatch mxfp8", cfg.name)
+    plan, ws, pool, pool_s = plan_and_dispatch(inp, dtype="mxfp4")
+    op = oracle.plan(inp.topk_idx, cfg.expert_begin, cfg.num_local_experts, cfg.tile)
+    rows, (codes, scales) = oracle.dispatch(inp.x, op, "mxfp4")
+    assert np.array_equal(pool.cpu().numpy()[rows], codes)
+    assert np.array_equal(pool_s.cpu().numpy()[rows], scales)
+    pad = np.setdiff1d(np.arange(op.P_cap), rows)
+    assert (pool_s.cpu().numpy()[pad] == 0xFF).all()
+
+
+def test_dispatch_mxfp8_full_size_sampled_rows():
+    cfg = config_by_name("mxfp4")
+    inp = make_inputs(cfg, weights=False)
+    say("dispatch mxfp8 full size", cfg.name)
+    plan, ws, pool, pool_s = plan_and_dispatch(inp, dtype="mxfp4")
+    src = plan.src.cpu().numpy()
+    rng = np.random.default_rng(0)
+    rows = np.sort(rng.choice(np.nonzero(src >= 0)[0], 256, replace=False))
+    codes, scales = oracle.token_rows(inp.x, "mxfp4", src[rows] // cfg.K)
     assert np.array_equal(pool.cpu().numpy()[rows], codes)
     assert np.array_equal(pool_s.cpu().numpy()[rows], scales)
 

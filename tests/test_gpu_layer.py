@@ -1,5 +1,5 @@
 """The whole path on the GPU (plan -> dispatch -> expert FFN -> combine) against the
-oracle: max-normwise relative error <= 1e-2 (bf16) / 3e-2 (fp8), plan bit-exact,
+oracle: max-normwise relative error <= 1e-2 (bf16) / 3e-2 (fp8, mxfp4), plan bit-exact,
 tokens with no local pair exactly zero, repeated runs bitwise identical.
 
 Small shapes are compared on every output element; the full-size workloads on a
@@ -28,6 +28,8 @@ FULL_COMPARE = [
     MoEConfig("fp8_t64", 300, 512, 256, 6, 0, 6, 2, 64, "fp8"),
     MoEConfig("fp8_t128", 700, 1024, 384, 10, 1, 8, 4, 128, "fp8"),
     MoEConfig("fp8_big", 600, 1024, 512, 6, 0, 6, 2, 128, "fp8"),     # fp8 big-tile kernel, tiled weights
+    MoEConfig("mx_small", 300, 512, 256, 4, 0, 4, 2, 128, "mxfp4"),   # mxfp4: one N block, 2 K steps
+    MoEConfig("mx_big", 700, 1024, 768, 10, 1, 8, 4, 128, "mxfp4"),   # 3 A units, ragged tiles, EP slice
 ]
 
 
@@ -61,7 +63,7 @@ def _sample_tokens(cfg, inp, n=24, seed=0):
     return np.array(sorted(pick))
 
 
-@pytest.mark.parametrize("name", ["ep_share", "zipf_skew", "fp8_weights"])
+@pytest.mark.parametrize("name", ["ep_share", "zipf_skew", "fp8_weights", "mxfp4"])
 def test_layer_full_size_sampled(name):
     cfg = config_by_name(name)
     inp = make_inputs(cfg, pin_memory=True)
