@@ -19,6 +19,7 @@ from .layer import (  # noqa: F401
     moe_combine,
     moe_dispatch,
     moe_expert_ffn,
+    moe_expert_ffn_combine,
     moe_get_error,
     moe_pack_mx_scales,
     moe_pack_weights,

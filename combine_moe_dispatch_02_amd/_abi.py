@@ -75,6 +75,9 @@ SIGNATURES = [
     ("moe_expert_ffn", ctypes.c_int,
      [_PP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _U32, _VP, _SZ, _VP,
       ctypes.POINTER(TileConfig), _VP]),
+    ("moe_expert_ffn_combine", ctypes.c_int,
+     [_PP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _U32, _VP, _SZ, _VP, _VP, _VP,
+      ctypes.POINTER(TileConfig), _VP]),
     ("moe_combine", ctypes.c_int, [_VP, _I32, _VP, _PP, _I32, _VP, _VP]),
     ("moe_pack_weights", ctypes.c_int, [_VP, _I32, _I32, _I32, _I32, _VP, _VP]),
     ("moe_pack_mx_scales", ctypes.c_int, [_VP, _I32, _I32, _I32, _VP, _VP]),

@@ -101,10 +101,14 @@ MOE355_API int moe_dispatch(const void* x, int32_t H, int32_t act_dtype, const m
                          static_cast<hipStream_t>(stream));
 }
 
-MOE355_API int moe_expert_ffn(const moe_plan_t* plan, int32_t pool_rows, const void* pool, const void* pool_s,
-                              const void* w1, const void* w1_s, const void* w2, const void* w2_s, int32_t H,
-                              int32_t I, int32_t dtype, uint32_t epoch, void* ws, size_t ws_bytes, void* y_pool,
-                              const moe_tile_config* cfg, void* stream) {
+}  // extern "C"
+
+// moe_expert_ffn and moe_expert_ffn_combine: the same validation and launch; the
+// second also takes topk_weights and out (non-null) for combine on completion
+static int expert_ffn(const moe_plan_t* plan, int32_t pool_rows, const void* pool, const void* pool_s,
+                      const void* w1, const void* w1_s, const void* w2, const void* w2_s, int32_t H, int32_t I,
+                      int32_t dtype, uint32_t epoch, void* ws, size_t ws_bytes, void* y_pool,
+                      const float* topk_weights, void* out, const moe_tile_config* cfg, void* stream) {
   int rc = check_plan(plan);
   if (rc != MOE_OK) return rc;
   if (!pool || !w1 || !w2 || !ws || !y_pool || epoch == 0 || H < 1 || I < 1) return MOE_ERR_INVALID;
@@ -122,7 +126,9 @@ MOE355_API int moe_expert_ffn(const moe_plan_t* plan, int32_t pool_rows, const v
   const WsLayout L = ws_layout(plan->T, plan->K, plan->E_local, plan->tile, pool_rows, I, dtype);
   if (ws_bytes < L.total) return MOE_ERR_INVALID;
   if (cfg && cfg->gemm_workgroups < 0) return MOE_ERR_INVALID;
-  FfnLaunch f;
+  FfnLaunch f{};
+  f.topk_w = topk_weights;
+  f.comb_out = out;
   f.plan = plan;
   f.pool_rows = pool_rows;
   f.pool = pool;
@@ -144,6 +150,27 @@ MOE355_API int moe_expert_ffn(const moe_plan_t* plan, int32_t pool_rows, const v
   const uint64_t us = (cfg && cfg->spin_timeout_us) ? cfg->spin_timeout_us : 2000000u;
   f.timeout_ticks = us * 100u;  // s_memrealtime counts at 100 MHz
   return launch_expert_ffn(f, L, static_cast<char*>(ws), static_cast<hipStream_t>(stream));
+}
+
+extern "C" {
+
+MOE355_API int moe_expert_ffn(const moe_plan_t* plan, int32_t pool_rows, const void* pool, const void* pool_s,
+                              const void* w1, const void* w1_s, const void* w2, const void* w2_s, int32_t H,
+                              int32_t I, int32_t dtype, uint32_t epoch, void* ws, size_t ws_bytes, void* y_pool,
+                              const moe_tile_config* cfg, void* stream) {
+  return expert_ffn(plan, pool_rows, pool, pool_s, w1, w1_s, w2, w2_s, H, I, dtype, epoch, ws, ws_bytes, y_pool,
+                    nullptr, nullptr, cfg, stream);
+}
+
+MOE355_API int moe_expert_ffn_combine(const moe_plan_t* plan, int32_t pool_rows, const void* pool,
+                                      const void* pool_s, const void* w1, const void* w1_s, const void* w2,
+                                      const void* w2_s, int32_t H, int32_t I, int32_t dtype, uint32_t epoch,
+                                      void* ws, size_t ws_bytes, void* y_pool, const float* topk_weights, void* out,
+                                      const moe_tile_config* cfg, void* stream) {
+  if (!topk_weights || !out) return MOE_ERR_INVALID;
+  if (H % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  return expert_ffn(plan, pool_rows, pool, pool_s, w1, w1_s, w2, w2_s, H, I, dtype, epoch, ws, ws_bytes, y_pool,
+                    topk_weights, out, cfg, stream);
 }
 
 MOE355_API int moe_combine(const void* y_pool, int32_t pool_rows, const float* topk_weights,

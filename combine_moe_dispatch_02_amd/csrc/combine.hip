@@ -9,6 +9,7 @@
 // One wave per token, 16-byte lanes; each pair's row is read through a
 // hardware-bounded buffer resource, and non-local pairs (pos = -1) are skipped
 // on a wave-uniform mask.
+#include "combine.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -33,47 +34,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   if (p >= a.pool_rows) p = -1;  // past the allocation: dispatch has reported it
   const float wt = lane < a.K ? a.w[pair0 + lane] : 0.f;
   const uint64_t have = ballot(p >= 0);
-  const int H = a.H;
-  const uint32_t row_bytes = (uint32_t)H * 2u;
-  const int nch = H >> 3;
-  const __amdgpu_buffer_rsrc_t orow = make_rsrc(a.out + (int64_t)t * row_bytes, row_bytes);
-
-  for (int c0 = 0; c0 < nch; c0 += kWave * CPL) {
-    float acc[CPL][8];
-#pragma unroll
-    for (int i = 0; i < CPL; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
-    for (int k = 0; k < a.K; ++k) {
-      if (!((have >> k) & 1ull)) continue;
-      const int pk = readlane(p, k);
-      const float wk = __builtin_bit_cast(float, readlane(__builtin_bit_cast(int, wt), k));
-      const __amdgpu_buffer_rsrc_t r = make_rsrc(a.y + (int64_t)pk * row_bytes, row_bytes);
-      u32x4 v[CPL];
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) v[i] = buf_load16(r, (uint32_t)(c0 + i * kWave + lane) * 16u);
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        acc[i][0] += wk * bf16_lo(v[i].x);
-        acc[i][1] += wk * bf16_hi(v[i].x);
-        acc[i][2] += wk * bf16_lo(v[i].y);
-        acc[i][3] += wk * bf16_hi(v[i].y);
-        acc[i][4] += wk * bf16_lo(v[i].z);
-        acc[i][5] += wk * bf16_hi(v[i].z);
-        acc[i][6] += wk * bf16_lo(v[i].w);
-        acc[i][7] += wk * bf16_hi(v[i].w);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      u32x4 o;
-      o.x = pack_bf16x2(acc[i][0], acc[i][1]);
-      o.y = pack_bf16x2(acc[i][2], acc[i][3]);
-      o.z = pack_bf16x2(acc[i][4], acc[i][5]);
-      o.w = pack_bf16x2(acc[i][6], acc[i][7]);
-      buf_store16(o, orow, (uint32_t)(c0 + i * kWave + lane) * 16u);
-    }
-  }
+  combine_token<CPL>(a.y, p, wt, have, a.K, a.H, a.out + (int64_t)t * a.H * 2, lane);
 }
 
 int launch_combine(const void* y_pool, int32_t pool_rows, const float* topk_weights, const moe_plan_t& p,

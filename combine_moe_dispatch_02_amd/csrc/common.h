@@ -22,6 +22,8 @@ struct WsLayout {
   size_t done = 64;      // uint32: plan blocks finished (reset by the last one)
   size_t hist = 256;     // int32 [ncols][E_local]: per-wave expert counts, then bases
   size_t fill = 0;       // uint32 [ntiles_cap]: rows stored per tile by dispatch
+  size_t ydone = 0;      // uint32 [ntiles_cap]: GEMM Y units finished per tile (combine on completion)
+  size_t cq = 0;         // uint32: combine items claimed (combine on completion)
   size_t h = 0;          // h [pool_rows][I]: bf16, or e4m3 codes
   size_t hs = 0;         // fp8: float [pool_rows][I/128]; mxfp4: E8M0 bytes [pool_rows][I/32]
   size_t plan_end = 0;   // end of what plan/dispatch need
@@ -44,7 +46,9 @@ inline WsLayout ws_layout(int32_t T, int32_t K, int32_t E, int32_t tile, int64_t
   L.ncols = (int32_t)((pairs + kPairsPerWave - 1) / kPairsPerWave);
   L.ntiles_cap = (int32_t)(cap / tile);
   L.fill = align_up(L.hist + (size_t)L.ncols * E * 4, 256);
-  L.plan_end = align_up(L.fill + (size_t)L.ntiles_cap * 4, 256);
+  L.ydone = align_up(L.fill + (size_t)L.ntiles_cap * 4, 256);
+  L.cq = align_up(L.ydone + (size_t)L.ntiles_cap * 4, 256);
+  L.plan_end = L.cq + 256;
   if (pool_rows <= 0) pool_rows = cap;
   size_t off = L.plan_end;
   if (I > 0) {

@@ -28,6 +28,7 @@
 #include <algorithm>
 #include <type_traits>
 
+#include "combine.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -75,6 +76,14 @@ struct FfnArgs {
   int32_t e8_lda;            // mxfp4: bytes per row of A_e8 (Kdim/32)
   int64_t b_e8_expert;       // mxfp4: bytes per expert of B_e8
   int32_t e8_ldo;            // mxfp4 GEMM A: bytes per row of out_e8 (I/32)
+  // combine on completion (GEMM Y on the big-tile kernel; null ydone = off)
+  uint32_t* ydone;           // per tile: GEMM Y units finished (GEMM A zeroes them)
+  uint32_t* cq;              // next combine item to claim (GEMM A zeroes it)
+  const int32_t* pos;        // plan: pool row of pair t*K+k
+  const float* topk_w;       // [T][K]
+  uint8_t* comb_out;         // out [T][H] bf16
+  int32_t T, K;
+  int32_t pool_rows;
 };
 
 __device__ inline uint32_t swz(int row, int chunk) { return (uint32_t)(row * 128 + ((chunk ^ (row & 7)) << 4)); }
@@ -196,6 +205,7 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(FfnArgs a) {
     ntiles = a.max_tiles;
   }
   const int total = ntiles * a.n_units;
+  if (GEMM_A && a.cq != nullptr && blockIdx.x == 0 && tid == 0) *a.cq = 0u;
   for (int u = blockIdx.x; u < total; u += gridDim.x) {
     const int m = u / a.n_units;
     const int j = u - m * a.n_units;
@@ -203,6 +213,7 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(FfnArgs a) {
     const int e = a.tile_expert[m];
 
     if (a.wait_ready && !wait_tile_ready(a, m, &s_go)) continue;
+    if (GEMM_A && a.ydone != nullptr && j == 0 && tid == 0) a.ydone[m] = 0u;  // for GEMM Y's combine
 
     // sources of this unit
     const uint8_t* Arow0 = a.A + (int64_t)m0 * a.lda;
@@ -441,6 +452,54 @@ struct Big {
   static constexpr int kALoads = (kAChunks + kThreads - 1) / kThreads;
 };
 
+// Combine on completion (StreamEP README, "How it works": combine starts on a token
+// as soon as its compute is done). After its last GEMM Y unit, a workgroup claims
+// items of one token per wave from a device-wide counter. A wave waits until every
+// pool tile holding one of its token's pairs has all its GEMM Y units counted (an
+// acquire after the counts), then does the token's weighted gather-sum exactly as
+// the combine kernel does. Items are claimed only after the claimer's own units,
+// and a unit never waits, so the waits end whenever the grid's workgroups can all be
+// resident at once (the launch keeps the grid at or below the CU count). A wait that
+// outlasts the timeout records MOE_ERR_TIMEOUT and writes the token's row as zeros.
+__device__ inline void combine_tail(const FfnArgs& a, int* s_item) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int nw = blockDim.x >> 6;
+  const int items = (a.T + nw - 1) / nw;
+  const int H = (int)(a.ldo >> 1);
+  const uint32_t target = (uint32_t)a.n_units;
+  for (;;) {
+    __syncthreads();
+    if (tid == 0) *s_item = (int)__hip_atomic_fetch_add(a.cq, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int item = *s_item;
+    if (item >= items) break;
+    const int t = item * nw + (tid >> 6);
+    if (t >= a.T) continue;
+    const int64_t pair0 = (int64_t)t * a.K;
+    int p = lane < a.K ? a.pos[pair0 + lane] : -1;
+    if (p >= a.pool_rows) p = -1;  // past the allocation: dispatch has reported it
+    const float wt = lane < a.K ? a.topk_w[pair0 + lane] : 0.f;
+    uint64_t have = ballot(p >= 0);
+    if (have != 0) {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      for (;;) {
+        const bool done =
+            p < 0 || __hip_atomic_load(&a.ydone[p >> a.tile_shift], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target;
+        if (ballot(!done) == 0) break;
+        if (__builtin_amdgcn_s_memrealtime() - t0 > a.timeout) {
+          if (lane == 0) record_error(a.err, MOE_ERR_TIMEOUT);
+          have = 0;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    combine_token<4>(a.out, p, wt, have, a.K, H, a.comb_out + (int64_t)t * H * 2, lane);
+  }
+}
+
 // s_waitcnt vmcnt(0), the other counters left alone (LDS-DMA loads have no
 // register result for the compiler to wait on)
 __device__ inline void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -490,6 +549,7 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
   const int total = ntiles * a.n_units;
   const int slot = unit_slot(blockIdx.x, gridDim.x);
   const int nk = a.ksteps;  // even
+  if (GEMM_A && a.cq != nullptr && blockIdx.x == 0 && tid == 0) *a.cq = 0u;
 
   for (int u = slot; u < total; u += gridDim.x) {
     int m, j;
@@ -497,6 +557,7 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
     const int m0 = m * BM;
     const int e = a.tile_expert[m];
     if (a.wait_ready && !wait_tile_ready(a, m, &s_go)) continue;
+    if (GEMM_A && a.ydone != nullptr && j == 0 && tid == 0) a.ydone[m] = 0u;  // for GEMM Y's combine
 
     // buffer resources: uniform bases, 32-bit lane offsets, uniform per-tile/step offsets
     const __amdgpu_buffer_rsrc_t ar = make_rsrc(a.A + (int64_t)m0 * a.lda, (uint32_t)(BM * a.lda));
@@ -1077,7 +1138,19 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
           *reinterpret_cast<u32x4*>(a.out + row * a.ldo + colb + ((sl ^ (r & 7)) << 4)) = v;
         }
       }
+      if (a.ydone != nullptr) {
+        // publish the unit for combine: every wave's y stores are issued (barrier), then
+        // one device-scope release and a count on the tile
+        __syncthreads();
+        if (tid == 0) {
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+          __hip_atomic_fetch_add(&a.ydone[m], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
     }
+  }
+  if constexpr (!GEMM_A) {
+    if (a.ydone != nullptr) combine_tail(a, &s_go);
   }
 }
 
@@ -1277,6 +1350,9 @@ int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream
   uint8_t* h = reinterpret_cast<uint8_t*>(ws + L.h);
   float* hs = fp8 ? reinterpret_cast<float*>(ws + L.hs) : nullptr;
   uint8_t* hs8 = mx ? reinterpret_cast<uint8_t*>(ws + L.hs) : nullptr;
+  // combine on completion runs in the big-tile GEMM Y kernel; elsewhere the combine
+  // kernel follows the FFN on the same stream
+  const bool fuse = f.comb_out != nullptr && bn_y == 512;
   const int ntiles_cap = std::min(p.rows_cap, f.pool_rows) / tile;
 
   FfnArgs a{};
@@ -1290,6 +1366,16 @@ int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream
   a.epoch = f.epoch;
   a.err = reinterpret_cast<uint32_t*>(ws + L.err);
   a.timeout = f.timeout_ticks;
+  if (fuse) {
+    a.ydone = reinterpret_cast<uint32_t*>(ws + L.ydone);
+    a.cq = reinterpret_cast<uint32_t*>(ws + L.cq);
+    a.pos = p.pos;
+    a.topk_w = f.topk_w;
+    a.comb_out = static_cast<uint8_t*>(f.comb_out);
+    a.T = p.T;
+    a.K = p.K;
+    a.pool_rows = f.pool_rows;
+  }
 
   // GEMM A: pool x w1^T -> SwiGLU -> h
   a.A = static_cast<const uint8_t*>(f.pool);
@@ -1355,12 +1441,21 @@ int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream
   a.unit_order = bn_y == 512 ? (f.unit_order ? f.unit_order : 3) : 1;
   int gy = (int)std::min<int64_t>(grid, (int64_t)ntiles_cap * a.n_units);
   if (gy < 1) gy = 1;
+  if (fuse) {
+    // every workgroup must be able to be resident at once (its combine waits on the
+    // units of the others), and the combine items want the whole device
+    const int cus = std::max(1, device_cu_count());
+    gy = std::min(grid, cus);
+  }
   a.ktiles = I / (fp8 || mx ? 128 : 32);
   rc = mx    ? launch_mx<false>(tile, bn_y, packed, a, gy, stream)
        : fp8 ? launch_shape<true, false>(tile, bn_y, packed, a, gy, stream)
              : launch_shape<false, false>(tile, bn_y, packed, a, gy, stream);
   if (rc != MOE_OK) return rc;
-  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
+  if (f.comb_out != nullptr && !fuse)
+    return launch_combine(f.y_pool, f.pool_rows, f.topk_w, p, H, f.comb_out, stream);
+  return MOE_OK;
 }
 
 }  // namespace moe

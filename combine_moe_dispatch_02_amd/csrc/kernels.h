@@ -31,6 +31,8 @@ struct FfnLaunch {
   int32_t unit_order;
   int32_t weight_layout;
   uint64_t timeout_ticks;   // s_memrealtime ticks (100 MHz)
+  const float* topk_w;      // combine on completion: [T][K] weights (null = FFN only)
+  void* comb_out;           // combine on completion: out [T][H] bf16 (null = FFN only)
 };
 
 int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream_t stream);

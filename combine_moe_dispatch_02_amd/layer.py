@@ -21,7 +21,8 @@ from ._abi import (MOE_BF16, MOE_FP8_E4M3_G128, MOE_MXFP4, MOE_WEIGHTS_MFMA_TILE
 __all__ = [
     "MOE_BF16", "MOE_FP8_E4M3_G128", "MOE_MXFP4", "MoeError", "Plan", "Workspace", "TileConfig",
     "pool_rows_upper_bound", "workspace_bytes", "moe_plan", "moe_query_pool_rows",
-    "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_get_error", "moe_pack_weights",
+    "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_combine", "moe_combine", "moe_get_error",
+    "moe_pack_weights",
     "moe_pack_mx_scales",
     "device_cu_count", "MOE_WEIGHTS_ROW_MAJOR", "MOE_WEIGHTS_MFMA_TILED",
     "make_streams", "StreamMoE", "stream_moe",
@@ -158,13 +159,9 @@ def moe_dispatch(x: torch.Tensor, plan: Plan, pool: torch.Tensor, pool_s: Option
                                               _stream(stream)))
 
 
-def moe_expert_ffn(plan: Plan, pool: torch.Tensor, pool_s: Optional[torch.Tensor],
-                   w1: torch.Tensor, w1_s: Optional[torch.Tensor], w2: torch.Tensor,
-                   w2_s: Optional[torch.Tensor], epoch: int, ws: Workspace, y_pool: torch.Tensor,
-                   dtype="bf16", cfg: Optional[TileConfig] = None, stream=None) -> None:
+def _ffn_shapes(plan: Plan, pool, w1, w2, y_pool, code):
     for t, n in ((pool, "pool"), (w1, "w1"), (w2, "w2"), (y_pool, "y_pool")):
         _need_cuda(t, n)
-    code = _dtype_code(dtype)
     E, twoI, H = w1.shape
     if code == MOE_MXFP4:          # packed e2m1: two codes per byte along K
         H *= 2
@@ -174,11 +171,40 @@ def moe_expert_ffn(plan: Plan, pool: torch.Tensor, pool_s: Optional[torch.Tensor
         raise ValueError("w1 [E_local, 2I, H] / w2 [E_local, H, I] shapes do not match")
     if y_pool.shape[0] != pool.shape[0] or y_pool.shape[1] != H:
         raise ValueError("y_pool must be [pool rows, H]")
+    return H, twoI // 2
+
+
+def moe_expert_ffn(plan: Plan, pool: torch.Tensor, pool_s: Optional[torch.Tensor],
+                   w1: torch.Tensor, w1_s: Optional[torch.Tensor], w2: torch.Tensor,
+                   w2_s: Optional[torch.Tensor], epoch: int, ws: Workspace, y_pool: torch.Tensor,
+                   dtype="bf16", cfg: Optional[TileConfig] = None, stream=None) -> None:
+    code = _dtype_code(dtype)
+    H, I = _ffn_shapes(plan, pool, w1, w2, y_pool, code)
     c = plan.c()
     cfgp = ctypes.byref(cfg) if cfg is not None else None
     check("moe_expert_ffn", load().moe_expert_ffn(
         ctypes.byref(c), pool.shape[0], _vp(pool), _vp(pool_s), _vp(w1), _vp(w1_s), _vp(w2),
-        _vp(w2_s), H, twoI // 2, code, epoch, _vp(ws.buf), ws.nbytes, _vp(y_pool),
+        _vp(w2_s), H, I, code, epoch, _vp(ws.buf), ws.nbytes, _vp(y_pool),
+        cfgp, _stream(stream)))
+
+
+def moe_expert_ffn_combine(plan: Plan, pool: torch.Tensor, pool_s: Optional[torch.Tensor],
+                           w1: torch.Tensor, w1_s: Optional[torch.Tensor], w2: torch.Tensor,
+                           w2_s: Optional[torch.Tensor], epoch: int, ws: Workspace, y_pool: torch.Tensor,
+                           topk_weights: torch.Tensor, out: torch.Tensor, dtype="bf16",
+                           cfg: Optional[TileConfig] = None, stream=None) -> None:
+    """moe_expert_ffn then moe_combine, with combine on completion inside GEMM Y."""
+    code = _dtype_code(dtype)
+    H, I = _ffn_shapes(plan, pool, w1, w2, y_pool, code)
+    _need_cuda(topk_weights, "topk_weights", torch.float32)
+    _need_cuda(out, "out", torch.bfloat16)
+    if topk_weights.shape != (plan.T, plan.K) or out.shape != (plan.T, H):
+        raise ValueError("topk_weights [T, K] / out [T, H] shapes do not match the plan")
+    c = plan.c()
+    cfgp = ctypes.byref(cfg) if cfg is not None else None
+    check("moe_expert_ffn_combine", load().moe_expert_ffn_combine(
+        ctypes.byref(c), pool.shape[0], _vp(pool), _vp(pool_s), _vp(w1), _vp(w1_s), _vp(w2),
+        _vp(w2_s), H, I, code, epoch, _vp(ws.buf), ws.nbytes, _vp(y_pool), _vp(topk_weights), _vp(out),
         cfgp, _stream(stream)))
 
 
@@ -235,8 +261,10 @@ class StreamMoE:
 
     def __init__(self, T, H, I, K, num_local_experts, *, expert_begin=0, tile=128, dtype="bf16",
                  device="cuda", pool_rows: Optional[int] = None, cfg: Optional[TileConfig] = None,
-                 weight_layout: str = "auto"):
+                 weight_layout: str = "auto", combine_on_completion: bool = False):
         self.T, self.H, self.I, self.K = T, H, I, K
+        # GEMM Y's workgroups combine each token once its tiles are done (no FFN -> combine join)
+        self.combine_on_completion = combine_on_completion
         self.E_local, self.expert_begin, self.tile = num_local_experts, expert_begin, tile
         self.dtype = _DTYPE_NAMES[_dtype_code(dtype)]
         # tiled weights feed the big-tile kernel, which needs whole 512-column blocks
@@ -296,6 +324,10 @@ class StreamMoE:
             s = torch.cuda.current_stream()
             moe_plan(topk_idx, self.plan, self.ws, s)
             moe_dispatch(x, self.plan, self.pool, self.pool_s, epoch, self.ws, self.dtype, s)
+            if self.combine_on_completion:
+                moe_expert_ffn_combine(self.plan, self.pool, self.pool_s, w1, w1_scale, w2, w2_scale, epoch,
+                                       self.ws, self.y_pool, topk_weights, self.out, self.dtype, self.cfg, s)
+                return self.out
             moe_expert_ffn(self.plan, self.pool, self.pool_s, w1, w1_scale, w2, w2_scale, epoch,
                            self.ws, self.y_pool, self.dtype, self.cfg, s)
             moe_combine(self.y_pool, topk_weights, self.plan, self.out, s)
@@ -308,6 +340,13 @@ class StreamMoE:
         planned.record(comm)
         moe_dispatch(x, self.plan, self.pool, self.pool_s, epoch, self.ws, self.dtype, comm)
         compute.wait_event(planned)
+        if self.combine_on_completion:
+            compute.wait_stream(cur)       # topk_weights and out belong to the caller's stream
+            moe_expert_ffn_combine(self.plan, self.pool, self.pool_s, w1, w1_scale, w2, w2_scale, epoch,
+                                   self.ws, self.y_pool, topk_weights, self.out, self.dtype, self.cfg, compute)
+            cur.wait_stream(compute)
+            cur.wait_stream(comm)
+            return self.out
         moe_expert_ffn(self.plan, self.pool, self.pool_s, w1, w1_scale, w2, w2_scale, epoch,
                        self.ws, self.y_pool, self.dtype, self.cfg, compute)
         done = torch.cuda.Event()

@@ -196,6 +196,27 @@ MOE355_API int moe_expert_ffn(const moe_plan_t* plan, int32_t pool_rows, const v
                               void* stream);
 
 /*
+ * A3 + A4 + A5 with combine on completion (StreamEP README, "How it works": combine
+ * starts on a token as soon as its compute is done). Does what moe_expert_ffn
+ * followed by moe_combine(y_pool, pool_rows, topk_weights, plan, H, out) on the same
+ * stream does, with the same bits in out and y_pool. When GEMM Y runs on the big-tile
+ * kernel (block N 512), each of its work units publishes the tile's progress in the
+ * workspace (device-scope release), and the kernel's workgroups, once out of GEMM
+ * work, take the tokens one per wave, wait (acquire) until every tile holding one of
+ * the token's pairs is finished, and write the token's row of out: there is no
+ * FFN -> combine join. The GEMM Y grid is then at most the CU count. For other
+ * shapes the combine kernel runs after the FFN. A wait that outlasts the timeout
+ * records MOE_ERR_TIMEOUT and writes the token's row as zeros.
+ * topk_weights: device fp32 [T][K]; out: device bf16 [T][H], every row written.
+ * Errors: those of moe_expert_ffn; MOE_ERR_INVALID for null topk_weights or out.
+ */
+MOE355_API int moe_expert_ffn_combine(const moe_plan_t* plan, int32_t pool_rows, const void* pool,
+                                      const void* pool_s, const void* w1, const void* w1_s, const void* w2,
+                                      const void* w2_s, int32_t H, int32_t I, int32_t dtype, uint32_t epoch,
+                                      void* ws, size_t ws_bytes, void* y_pool, const float* topk_weights, void* out,
+                                      const moe_tile_config* cfg, void* stream);
+
+/*
  * A5. Combine: out[t] = sum over k with pos[t,k] >= 0, in ascending k, of
  * topk_weights[t,k] * y_pool[pos[t,k]], accumulated in fp32 and stored bf16
  * (round to nearest even). Every row of out (bf16 [T][H]) is written; a token

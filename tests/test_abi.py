@@ -28,7 +28,7 @@ def lib():
 def test_header_declares_the_four_calls():
     names = set(declared_symbols())
     assert {"moe_plan", "moe_dispatch", "moe_expert_ffn", "moe_combine"} <= names
-    assert len(names) == 12
+    assert len(names) == 13
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -160,6 +160,21 @@ def test_ffn_validation(lib):
     assert call(dtype=2, scales=mx) == 2           # mxfp4 runs on tiled weights only
     tiled = _abi.TileConfig(0, 0, 0, 0, 1)
     assert call(H=512, I=256, dtype=2, scales=mx, cfg=ctypes.byref(tiled)) == 2   # tile 128 only
+
+
+def test_ffn_combine_validation(lib):
+    p = _fake_plan()
+    v = [ctypes.c_void_p(a) for a in range(0x10000, 0x10000 * 9, 0x10000)]
+    POOL, W1, W2, WS, Y, TW, OUT = v[:7]
+
+    def call(tw=TW, out=OUT, H=128, epoch=1):
+        return lib.moe_expert_ffn_combine(ctypes.byref(p), 256, POOL, None, W1, None, W2, None, H, 64, 0,
+                                          epoch, WS, 1 << 40, Y, tw, out, None, None)
+
+    assert call(tw=None) == 1
+    assert call(out=None) == 1
+    assert call(epoch=0) == 1
+    assert call(H=100) == 2
 
 
 def test_combine_validation(lib):
