@@ -168,6 +168,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="zipf_skew")
     ap.add_argument("--streams", action="store_true", help="dispatch/combine and FFN on two streams")
+    ap.add_argument("--combine-on-completion", action="store_true",
+                    help="GEMM Y's workgroups combine each token once its tiles are done (no separate combine)")
     ap.add_argument("--block-n", type=int, default=0, help="tile config override: N block (0 = auto)")
     ap.add_argument("--gemm-wgs", type=int, default=0, help="tile config override: GEMM grid (0 = auto)")
     ap.add_argument("--unit-order", type=int, default=0, help="tile config override: unit walk (0 = auto)")
@@ -220,7 +222,8 @@ def main():
     if args.block_n or args.gemm_wgs or args.unit_order:
         tcfg = moe.TileConfig(args.block_n, args.gemm_wgs, 0, args.unit_order, 0)
     layer = moe.StreamMoE(cfg.T, cfg.H, cfg.I, cfg.K, cfg.num_local_experts,
-                          expert_begin=cfg.expert_begin, tile=cfg.tile, dtype=cfg.dtype, cfg=tcfg)
+                          expert_begin=cfg.expert_begin, tile=cfg.tile, dtype=cfg.dtype, cfg=tcfg,
+                          combine_on_completion=args.combine_on_completion)
     # weight preprocessing at load time (not part of a step): MFMA fragment order when used
     w1, w2, w1s, w2s = layer.prepare_weights(w1, w2, w1s, w2s)
     torch.cuda.synchronize()
@@ -264,10 +267,16 @@ def main():
         ev[1].record(s)
         moe.moe_dispatch(x, layer.plan, layer.pool, layer.pool_s, epoch, layer.ws, cfg.dtype, s)
         ev[2].record(s)
-        moe.moe_expert_ffn(layer.plan, layer.pool, layer.pool_s, w1, w1s, w2, w2s, epoch, layer.ws,
-                           layer.y_pool, cfg.dtype, layer.cfg, s)
-        ev[3].record(s)
-        moe.moe_combine(layer.y_pool, w, layer.plan, layer.out, s)
+        if args.combine_on_completion:
+            # one call: the FFN with the combine inside GEMM Y (reported under "ffn"; combine 0)
+            moe.moe_expert_ffn_combine(layer.plan, layer.pool, layer.pool_s, w1, w1s, w2, w2s, epoch,
+                                       layer.ws, layer.y_pool, w, layer.out, cfg.dtype, layer.cfg, s)
+            ev[3].record(s)
+        else:
+            moe.moe_expert_ffn(layer.plan, layer.pool, layer.pool_s, w1, w1s, w2, w2s, epoch, layer.ws,
+                               layer.y_pool, cfg.dtype, layer.cfg, s)
+            ev[3].record(s)
+            moe.moe_combine(layer.y_pool, w, layer.plan, layer.out, s)
         ev[4].record(s)
         evs.append(ev)
     torch.cuda.synchronize()
@@ -287,7 +296,8 @@ def main():
     # the FFN's bound: MFMA unless streaming its least traffic takes longer at HBM peak
     hbm_bound = work["ffn_bytes"] / (PEAK_HBM_GBS * 1e9) > work["ffn_flops"] / (peak * 1e12)
     disp_gbs = work["dispatch_bytes"] / (stage_ms["dispatch"] * 1e-3) / 1e9
-    comb_gbs = work["combine_bytes"] / (stage_ms["combine"] * 1e-3) / 1e9
+    comb_gbs = (work["combine_bytes"] / (stage_ms["combine"] * 1e-3) / 1e9
+                if not args.combine_on_completion else None)
     src_hash = kernel_source_hash()
     traffic = read_traffic(cfg.name, src_hash)
     result = {
@@ -308,6 +318,8 @@ def main():
                    "tile": cfg.tile, "routing": cfg.routing, "pairs": work["pairs"],
                    "pool_rows": int(layer.plan.offsets[-1].item()),
                    "streams": "two (comm + compute)" if args.streams else "one",
+                   "combine": ("on completion, inside GEMM Y (stage 'ffn' includes it)"
+                               if args.combine_on_completion else "kernel after the FFN"),
                    "weights": "MFMA-tiled (permuted once at load time)" if layer.tiled else "row-major"},
         "roofline": ({"bound": "hbm", "kernel": "expert FFN (grouped GEMM A + Y)",
                       "achieved": round(ffn_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -320,10 +332,11 @@ def main():
         "ffn_GBps_least_traffic": round(ffn_gbs, 1),
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "dispatch_GBps": round(disp_gbs, 1),
-        "combine_GBps": round(comb_gbs, 1),
+        "combine_GBps": round(comb_gbs, 1) if comb_gbs is not None else None,
         "dispatch_combine_frac_hbm": round(
             (work["dispatch_bytes"] + work["combine_bytes"])
-            / ((stage_ms["dispatch"] + stage_ms["combine"]) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            / ((stage_ms["dispatch"] + stage_ms["combine"]) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+        if not args.combine_on_completion else None,
         "wall_s_timed": round(wall, 3),
     }
     if args.cpu_sample > 0:

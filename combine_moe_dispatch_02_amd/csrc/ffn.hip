@@ -496,7 +496,11 @@ __device__ inline void combine_tail(const FfnArgs& a, int* s_item) {
       }
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
-    combine_token<4>(a.out, p, wt, have, a.K, H, a.comb_out + (int64_t)t * H * 2, lane);
+    uint8_t* orow = a.comb_out + (int64_t)t * H * 2;
+    if (a.K <= 8)
+      combine_token_wide<2, 8>(a.out, p, wt, have, a.K, H, orow, lane);
+    else
+      combine_token<4>(a.out, p, wt, have, a.K, H, orow, lane);
   }
 }
 
