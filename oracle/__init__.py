@@ -5,6 +5,7 @@ CPU-baseline leg are its only users. Plain NumPy in float64; it shares no code
 with the GPU library and imports nothing from it.
 """
 from .e4m3 import E4M3_MAX, E4M3_VALUES, e4m3_decode, e4m3_encode  # noqa: F401
+from .moe_backward import OracleGrads, expert_backward, expert_forward, moe_layer_backward, silu_grad  # noqa: F401
 from .mx import (  # noqa: F401
     MX_BLOCK,
     dequantize_mx_e4m3,

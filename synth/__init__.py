@@ -5,6 +5,7 @@ from .inputs import (  # noqa: F401
     MoEInputs,
     config_by_name,
     expert_weights,
+    make_dout,
     make_inputs,
     make_routing,
     make_x,

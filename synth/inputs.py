@@ -46,10 +46,11 @@ __all__ = [
     "make_routing",
     "expert_weights",
     "make_inputs",
+    "make_dout",
 ]
 
 # tags keep every stream of draws independent of the others
-_TAG_X, _TAG_LOGITS, _TAG_W1, _TAG_W2 = 1, 2, 3, 4
+_TAG_X, _TAG_LOGITS, _TAG_W1, _TAG_W2, _TAG_DOUT = 1, 2, 3, 4, 5
 
 
 @dataclass(frozen=True)
@@ -116,6 +117,11 @@ def base_seed(cfg: MoEConfig, seed: Optional[int] = None) -> int:
 def make_x(cfg: MoEConfig, seed: int) -> torch.Tensor:
     """x[T, H] ~ N(0, 1), rounded to bf16 (round-to-nearest-even)."""
     return torch.randn(cfg.T, cfg.H, generator=_gen(seed, _TAG_X)).to(torch.bfloat16)
+
+
+def make_dout(cfg: MoEConfig, seed: int) -> torch.Tensor:
+    """The layer's output gradient dout[T, H] ~ N(0, 1), rounded to bf16 (backward pass input)."""
+    return torch.randn(cfg.T, cfg.H, generator=_gen(seed, _TAG_DOUT)).to(torch.bfloat16)
 
 
 def make_routing(cfg: MoEConfig, seed: int):
