@@ -17,6 +17,11 @@ from .layer import (  # noqa: F401
     device_cu_count,
     make_streams,
     moe_combine,
+    moe_combine_backward,
+    moe_dispatch_backward,
+    moe_expert_ffn_backward,
+    moe_expert_ffn_train,
+    moe_pack_weights_transposed,
     moe_dispatch,
     moe_expert_ffn,
     moe_expert_ffn_combine,

@@ -108,7 +108,8 @@ MOE355_API int moe_dispatch(const void* x, int32_t H, int32_t act_dtype, const m
 static int expert_ffn(const moe_plan_t* plan, int32_t pool_rows, const void* pool, const void* pool_s,
                       const void* w1, const void* w1_s, const void* w2, const void* w2_s, int32_t H, int32_t I,
                       int32_t dtype, uint32_t epoch, void* ws, size_t ws_bytes, void* y_pool,
-                      const float* topk_weights, void* out, const moe_tile_config* cfg, void* stream) {
+                      const float* topk_weights, void* out, void* g_pool, const moe_tile_config* cfg,
+                      void* stream) {
   int rc = check_plan(plan);
   if (rc != MOE_OK) return rc;
   if (!pool || !w1 || !w2 || !ws || !y_pool || epoch == 0 || H < 1 || I < 1) return MOE_ERR_INVALID;
@@ -126,7 +127,9 @@ static int expert_ffn(const moe_plan_t* plan, int32_t pool_rows, const void* poo
   const WsLayout L = ws_layout(plan->T, plan->K, plan->E_local, plan->tile, pool_rows, I, dtype);
   if (ws_bytes < L.total) return MOE_ERR_INVALID;
   if (cfg && cfg->gemm_workgroups < 0) return MOE_ERR_INVALID;
+  if (g_pool != nullptr && !ffn_train_ok(H, I, dtype, plan->tile, block_n)) return MOE_ERR_UNSUPPORTED;
   FfnLaunch f{};
+  f.g_pool = g_pool;
   f.topk_w = topk_weights;
   f.comb_out = out;
   f.plan = plan;
@@ -159,7 +162,7 @@ MOE355_API int moe_expert_ffn(const moe_plan_t* plan, int32_t pool_rows, const v
                               int32_t I, int32_t dtype, uint32_t epoch, void* ws, size_t ws_bytes, void* y_pool,
                               const moe_tile_config* cfg, void* stream) {
   return expert_ffn(plan, pool_rows, pool, pool_s, w1, w1_s, w2, w2_s, H, I, dtype, epoch, ws, ws_bytes, y_pool,
-                    nullptr, nullptr, cfg, stream);
+                    nullptr, nullptr, nullptr, cfg, stream);
 }
 
 MOE355_API int moe_expert_ffn_combine(const moe_plan_t* plan, int32_t pool_rows, const void* pool,
@@ -170,7 +173,69 @@ MOE355_API int moe_expert_ffn_combine(const moe_plan_t* plan, int32_t pool_rows,
   if (!topk_weights || !out) return MOE_ERR_INVALID;
   if (H % 8 != 0) return MOE_ERR_UNSUPPORTED;
   return expert_ffn(plan, pool_rows, pool, pool_s, w1, w1_s, w2, w2_s, H, I, dtype, epoch, ws, ws_bytes, y_pool,
-                    topk_weights, out, cfg, stream);
+                    topk_weights, out, nullptr, cfg, stream);
+}
+
+MOE355_API int moe_expert_ffn_train(const moe_plan_t* plan, int32_t pool_rows, const void* pool, const void* w1,
+                                    const void* w2, int32_t H, int32_t I, uint32_t epoch, void* ws, size_t ws_bytes,
+                                    void* y_pool, void* g_pool, const moe_tile_config* cfg, void* stream) {
+  if (!g_pool) return MOE_ERR_INVALID;
+  return expert_ffn(plan, pool_rows, pool, nullptr, w1, nullptr, w2, nullptr, H, I, MOE_BF16, epoch, ws, ws_bytes,
+                    y_pool, nullptr, nullptr, g_pool, cfg, stream);
+}
+
+MOE355_API int moe_combine_backward(const void* dout, const float* topk_weights, const void* y_pool,
+                                    int32_t pool_rows, const moe_plan_t* plan, int32_t H, void* dy_pool,
+                                    float* d_topk_weights, void* stream) {
+  int rc = check_plan(plan);
+  if (rc != MOE_OK) return rc;
+  if (!dout || !topk_weights || !y_pool || !dy_pool || !d_topk_weights || H < 8 || pool_rows < 0)
+    return MOE_ERR_INVALID;
+  if (H % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)H * 2 > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  return launch_combine_backward(dout, topk_weights, y_pool, pool_rows, *plan, H, dy_pool, d_topk_weights,
+                                 static_cast<hipStream_t>(stream));
+}
+
+MOE355_API int moe_expert_ffn_backward(const moe_plan_t* plan, int32_t pool_rows, const void* pool,
+                                       const void* dy_pool, void* g_pool, const void* w1t, const void* w2t, int32_t H,
+                                       int32_t I, void* ws, size_t ws_bytes, void* dx_pool, void* dw1, void* dw2,
+                                       const moe_tile_config* cfg, void* stream) {
+  int rc = check_plan(plan);
+  if (rc != MOE_OK) return rc;
+  if (!pool || !dy_pool || !g_pool || !w1t || !w2t || !ws || !dx_pool || !dw1 || !dw2 || H < 1 || I < 1)
+    return MOE_ERR_INVALID;
+  if (pool_rows < 1 || pool_rows % plan->tile != 0) return MOE_ERR_INVALID;
+  const int32_t block_n = cfg ? cfg->block_n : 0;
+  if (!ffn_train_ok(H, I, MOE_BF16, plan->tile, block_n)) return MOE_ERR_UNSUPPORTED;
+  // 32-bit buffer offsets over the pool-sized operands
+  if ((int64_t)pool_rows * std::max(2 * I, H) * 2 >= ((int64_t)1 << 32) - 16) return MOE_ERR_UNSUPPORTED;
+  if (cfg && (cfg->gemm_workgroups < 0 || cfg->unit_order < 0 || cfg->unit_order > 9)) return MOE_ERR_INVALID;
+  const WsLayout L = ws_layout(plan->T, plan->K, plan->E_local, plan->tile, pool_rows, I, MOE_BF16);
+  if (ws_bytes < L.total) return MOE_ERR_INVALID;
+  char* w = static_cast<char*>(ws);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int32_t wgs = cfg ? cfg->gemm_workgroups : 0;
+  const int32_t order = cfg ? cfg->unit_order : 0;
+  // backward GEMM Y: dh = dy . W2 -> dG (over G), and dW2 = dy^T h
+  rc = launch_ffn_dgrad(*plan, pool_rows, dy_pool, w2t, I, H, nullptr, g_pool, I, 1, wgs, order, L, w, s);
+  if (rc != MOE_OK) return rc;
+  rc = launch_wgrad(*plan, pool_rows, dy_pool, H, w + L.h, I, dw2, wgs, s);
+  if (rc != MOE_OK) return rc;
+  // backward GEMM A: dx_pool = dG . W1, and dW1 = dG^T X
+  rc = launch_ffn_dgrad(*plan, pool_rows, g_pool, w1t, H, 2 * I, dx_pool, nullptr, I, 0, wgs, order, L, w, s);
+  if (rc != MOE_OK) return rc;
+  return launch_wgrad(*plan, pool_rows, g_pool, 2 * I, pool, H, dw1, wgs, s);
+}
+
+MOE355_API int moe_dispatch_backward(const void* dx_pool, int32_t pool_rows, const moe_plan_t* plan, int32_t H,
+                                     void* dx, void* stream) {
+  int rc = check_plan(plan);
+  if (rc != MOE_OK) return rc;
+  if (!dx_pool || !dx || H < 8 || pool_rows < 0) return MOE_ERR_INVALID;
+  if (H % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)H * 2 > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  return launch_combine(dx_pool, pool_rows, nullptr, *plan, H, dx, static_cast<hipStream_t>(stream));
 }
 
 MOE355_API int moe_combine(const void* y_pool, int32_t pool_rows, const float* topk_weights,
@@ -194,6 +259,19 @@ MOE355_API int moe_pack_weights(const void* w, int32_t E, int32_t rows, int32_t 
   const char* b = static_cast<const char*>(out);
   if (a < b + bytes * E && b < a + bytes * E) return MOE_ERR_INVALID;  // overlap
   return launch_pack_weights(w, E, rows, K, dtype, out, static_cast<hipStream_t>(stream));
+}
+
+MOE355_API int moe_pack_weights_transposed(const void* w, int32_t E, int32_t rows, int32_t K, int32_t dtype,
+                                           void* out, void* stream) {
+  if (!w || !out || E < 1 || rows < 1 || K < 1) return MOE_ERR_INVALID;
+  if (dtype != MOE_BF16) return dtype == MOE_FP8_E4M3_G128 || dtype == MOE_MXFP4 ? MOE_ERR_UNSUPPORTED : MOE_ERR_INVALID;
+  if (K % 16 != 0 || rows % 32 != 0) return MOE_ERR_UNSUPPORTED;
+  const int64_t bytes = (int64_t)rows * K * 2;
+  if (bytes > ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
+  const char* a = static_cast<const char*>(w);
+  const char* b = static_cast<const char*>(out);
+  if (a < b + bytes * E && b < a + bytes * E) return MOE_ERR_INVALID;  // overlap
+  return launch_pack_weights_t(w, E, rows, K, out, static_cast<hipStream_t>(stream));
 }
 
 MOE355_API int moe_pack_mx_scales(const void* s, int32_t E, int32_t rows, int32_t K, void* out, void* stream) {

@@ -1,0 +1,345 @@
+// The backward pass around the expert GEMMs (StreamEP README, "How it works": the
+// layer trains, the backward pass mirrors the forward's overlaps, and the backward
+// grouped GEMMs A and Y are two of its four grouped GEMMs).
+//
+//   combine backward: dy_pool[pos[t,k]] = w[t,k] * dout[t] (bf16) and the gradient of
+//                     the routing weights dw[t,k] = <dout[t], y_pool[pos[t,k]]> (fp32);
+//                     the mirror of combine is a scatter into the pool, like dispatch.
+//   weight gradients: C[e] = A_e^T B_e over the rows of expert e's pool segment
+//                     (dW2[e] = dy_e^T h_e, dW1[e] = dG_e^T X_e), a grouped GEMM whose
+//                     contraction runs over pool rows.
+//   dispatch backward is the combine kernel with unit weights (combine.hip), and the
+//   data gradients run on the forward's big-tile kernel (ffn.hip).
+#include <algorithm>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// --------------------------------------------------------------------------------
+// combine backward: one wave per token, 16-byte lanes. dout[t] is read once; for each
+// local pair the y row is read for the dot product and the scaled dout row is stored.
+// --------------------------------------------------------------------------------
+struct CombineBwdArgs {
+  const uint8_t* dout;
+  const float* w;
+  const uint8_t* y;
+  const int32_t* pos;
+  int32_t T, K, H;
+  int32_t pool_rows;
+  uint8_t* dy;
+  float* dw;
+};
+
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+template <int CPL>
+__global__ __launch_bounds__(256) void combine_backward_kernel(CombineBwdArgs a) {
+  constexpr int KMAX = 16;
+  const int lane = lane_id();
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  const int64_t pair0 = (int64_t)t * a.K;
+  int p = lane < a.K ? a.pos[pair0 + lane] : -1;
+  if (p >= a.pool_rows) p = -1;
+  const float wt = lane < a.K ? a.w[pair0 + lane] : 0.f;
+  const uint64_t have = ballot(p >= 0);
+  const uint32_t row_bytes = (uint32_t)a.H * 2u;
+  const int nch = a.H >> 3;
+  const __amdgpu_buffer_rsrc_t dr = make_rsrc(a.dout + (int64_t)t * row_bytes, row_bytes);
+  float part[KMAX];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) part[k] = 0.f;
+  for (int c0 = 0; c0 < nch; c0 += kWave * CPL) {
+    u32x4 d[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) d[i] = buf_load16(dr, (uint32_t)(c0 + i * kWave + lane) * 16u);
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      if (k >= a.K || !((have >> k) & 1ull)) continue;
+      const int pk = readlane(p, k);
+      const float wk = __builtin_bit_cast(float, readlane(__builtin_bit_cast(int, wt), k));
+      const __amdgpu_buffer_rsrc_t yr = make_rsrc(a.y + (int64_t)pk * row_bytes, row_bytes);
+      const __amdgpu_buffer_rsrc_t or_ = make_rsrc(a.dy + (int64_t)pk * row_bytes, row_bytes);
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const uint32_t off = (uint32_t)(c0 + i * kWave + lane) * 16u;
+        const u32x4 yv = buf_load16(yr, off);
+        const uint32_t dd[4] = {d[i].x, d[i].y, d[i].z, d[i].w};
+        const uint32_t yy[4] = {yv.x, yv.y, yv.z, yv.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float d0 = bf16_lo(dd[q]), d1 = bf16_hi(dd[q]);
+          part[k] += d0 * bf16_lo(yy[q]);
+          part[k] += d1 * bf16_hi(yy[q]);
+          o[q] = pack_bf16x2(wk * d0, wk * d1);
+        }
+        buf_store16(u32x4{o[0], o[1], o[2], o[3]}, or_, off);
+      }
+    }
+  }
+  // every lane of the wave takes part in the reductions; lane k keeps pair k's sum
+  float mine = 0.f;
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    if (k < a.K) {
+      const float s = wave_sum(part[k]);
+      if (lane == k) mine = ((have >> k) & 1ull) ? s : 0.f;
+    }
+  }
+  if (lane < a.K) a.dw[pair0 + lane] = mine;
+}
+
+int launch_combine_backward(const void* dout, const float* topk_weights, const void* y_pool, int32_t pool_rows,
+                            const moe_plan_t& p, int32_t H, void* dy_pool, float* d_topk_weights,
+                            hipStream_t stream) {
+  CombineBwdArgs a;
+  a.dout = static_cast<const uint8_t*>(dout);
+  a.w = topk_weights;
+  a.y = static_cast<const uint8_t*>(y_pool);
+  a.pos = p.pos;
+  a.T = p.T;
+  a.K = p.K;
+  a.H = H;
+  a.pool_rows = pool_rows;
+  a.dy = static_cast<uint8_t*>(dy_pool);
+  a.dw = d_topk_weights;
+  const int nch = H / 8;
+  const dim3 grid((p.T + 3) / 4);
+  if (nch <= 64)
+    hipLaunchKernelGGL(combine_backward_kernel<1>, grid, dim3(256), 0, stream, a);
+  else if (nch <= 128)
+    hipLaunchKernelGGL(combine_backward_kernel<2>, grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(combine_backward_kernel<4>, grid, dim3(256), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+// --------------------------------------------------------------------------------
+// Weight gradients: C[e] (N1 x N2, bf16) = sum over the real rows r of expert e's pool
+// segment of A[r]^T B[r] (A [rows][N1], B [rows][N2], bf16), fp32 accumulation.
+//
+// Work unit = (expert, 256 x 256 output tile). Experts are ranked by row count, largest
+// first, in every workgroup (a rank sort of the counts in LDS), and the units go out
+// in that order, dealt boustrophedon over the grid's slots, so the long units start
+// first. 8 waves, each 128 (N1) x 64 (N2) of the tile: the forward's 16x16x32 bf16
+// MFMA layout with the B fragment first, so a lane holds one N1 row and four
+// consecutive N2 columns.
+//
+// The contraction runs over pool rows, while MFMA fragments want 8 consecutive K
+// values per lane: each K step (64 rows) every thread loads one 8 x 8 block (8 rows
+// x 16 bytes) of A or B, transposes it in registers (32 byte permutes), and writes
+// its 8 columns as 16-byte K chunks into an LDS tile [n][64 K] (128-byte rows, chunk
+// slot swizzled by (n ^ n/8) & 7: conflict-free for the fragment reads, which walk
+// n, and for the writes, which walk n/8). Rows past the segment's real rows load as
+// zeros (out of the buffer's range). Two LDS stages; the next step's loads are in
+// flight during this step's MFMAs; one barrier per step.
+// --------------------------------------------------------------------------------
+struct WgradArgs {
+  const uint8_t* A;
+  const uint8_t* B;
+  uint8_t* C;
+  int32_t N1, N2;
+  uint32_t a_bytes, b_bytes;   // buffer ranges of A and B (pool_rows rows)
+  const int32_t* offsets;
+  const int32_t* counts;
+  int32_t E;
+  int32_t tiles1, tiles2;      // N1 / 256, N2 / 256
+};
+
+constexpr int kWgTile = 256;
+constexpr int kWgK = 64;
+constexpr int kWgMaxE = 1024;
+
+__device__ inline uint32_t wg_swz(int n, int chunk) {
+  return (uint32_t)(n * 128 + (((chunk ^ n ^ (n >> 3)) & 7) << 4));
+}
+
+typedef __bf16 wg_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float wg_f32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(512, 1) void wgrad_kernel(WgradArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_t[2][2][kWgTile * 128];  // [stage][A,B]
+  __shared__ int s_order[kWgMaxE];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2;          // N1 half
+  const int wn = wave & 3;           // N2 quarter
+  const int l16 = lane & 15;
+  const int lhi = lane >> 4;
+
+  // experts by descending row count (ties: lower index first)
+  for (int e = tid; e < a.E; e += 512) {
+    const int c = a.counts[e];
+    int r = 0;
+    for (int f = 0; f < a.E; ++f) {
+      const int cf = a.counts[f];
+      r += (cf > c) || (cf == c && f < e);
+    }
+    s_order[r] = e;
+  }
+  __syncthreads();
+
+  const int per_e = a.tiles1 * a.tiles2;
+  const int total = a.E * per_e;
+  const int G = gridDim.x;
+  const int slot = (G & 7) == 0 ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+
+  // this thread's 8 x 8 block of the step: operand (A for tid < 256), row block, column block
+  const bool is_b = tid >= 256;
+  const int q = tid & 255;
+  const int rb = q >> 5;             // rows 8*rb .. 8*rb+7 of the step
+  const int cb = q & 31;             // columns 8*cb .. 8*cb+7 of the tile
+
+  for (int round = 0;; ++round) {
+    const int u = round * G + ((round & 1) ? G - 1 - slot : slot);
+    if (round * G >= total) break;
+    if (u >= total) continue;
+    const int e = s_order[u / per_e];
+    const int tix = u % per_e;
+    const int t1 = tix / a.tiles2, t2 = tix % a.tiles2;
+    const int r0 = a.offsets[e];
+    const int cnt = a.counts[e];
+    const int nsteps = (cnt + kWgK - 1) / kWgK;
+
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(is_b ? a.B : a.A, is_b ? a.b_bytes : a.a_bytes);
+    const uint32_t ld = (uint32_t)(is_b ? a.N2 : a.N1) * 2u;
+    const uint32_t col_off = (uint32_t)((is_b ? t2 : t1) * kWgTile + cb * 8) * 2u;
+    const uint32_t oob = is_b ? a.b_bytes : a.a_bytes;
+
+    u32x4 v[8];
+    auto load = [&](int s) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = s * kWgK + rb * 8 + i;   // row within the segment
+        const uint32_t off = r < cnt ? (uint32_t)(r0 + r) * ld + col_off : oob;  // past the range: zeros
+        v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+      }
+    };
+    auto store = [&](int st) {
+      uint8_t* base = &s_t[st][is_b ? 1 : 0][0];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+        u32x4 o;
+        o.x = __builtin_amdgcn_perm(v[1][c >> 1], v[0][c >> 1], sel);
+        o.y = __builtin_amdgcn_perm(v[3][c >> 1], v[2][c >> 1], sel);
+        o.z = __builtin_amdgcn_perm(v[5][c >> 1], v[4][c >> 1], sel);
+        o.w = __builtin_amdgcn_perm(v[7][c >> 1], v[6][c >> 1], sel);
+        *reinterpret_cast<u32x4*>(base + wg_swz(cb * 8 + c, rb)) = o;
+      }
+    };
+
+    wg_f32x4 acc[8][4];
+#pragma unroll
+    for (int tm = 0; tm < 8; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = wg_f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if (nsteps > 0) {
+      load(0);
+      store(0);
+    }
+    __syncthreads();
+    for (int s = 0; s < nsteps; ++s) {
+      const int st = s & 1;
+      if (s + 1 < nsteps) load(s + 1);
+      const uint8_t* ta = &s_t[st][0][0];
+      const uint8_t* tb = &s_t[st][1][0];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        wg_bf16x8 fb[4];
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn)
+          fb[tn] = *reinterpret_cast<const wg_bf16x8*>(tb + wg_swz(wn * 64 + tn * 16 + l16, kk * 4 + lhi));
+#pragma unroll
+        for (int tm = 0; tm < 8; ++tm) {
+          const wg_bf16x8 fa = *reinterpret_cast<const wg_bf16x8*>(ta + wg_swz(wm * 128 + tm * 16 + l16, kk * 4 + lhi));
+#pragma unroll
+          for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[tn], fa, acc[tm][tn], 0, 0, 0);
+        }
+      }
+      if (s + 1 < nsteps) store(st ^ 1);
+      __syncthreads();
+    }
+
+    // C[e][n1][n2]: lane holds n1 = t1*256 + wm*128 + tm*16 + l16, n2 = t2*256 + wn*64 + tn*16 + 4*lhi + (0..3)
+    uint8_t* cbase = a.C + ((int64_t)e * a.N1 + t1 * kWgTile + wm * 128 + l16) * a.N2 * 2 +
+                     (int64_t)(t2 * kWgTile + wn * 64 + 4 * lhi) * 2;
+#pragma unroll
+    for (int tm = 0; tm < 8; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < 4; ++tn) {
+        u32x2 o;
+        o.x = pack_bf16x2(acc[tm][tn][0], acc[tm][tn][1]);
+        o.y = pack_bf16x2(acc[tm][tn][2], acc[tm][tn][3]);
+        *reinterpret_cast<u32x2*>(cbase + (int64_t)tm * 16 * a.N2 * 2 + tn * 32) = o;
+      }
+  }
+}
+
+int launch_wgrad(const moe_plan_t& p, int32_t pool_rows, const void* A, int32_t N1, const void* B, int32_t N2,
+                 void* C, int32_t workgroups, hipStream_t stream) {
+  WgradArgs a;
+  a.A = static_cast<const uint8_t*>(A);
+  a.B = static_cast<const uint8_t*>(B);
+  a.C = static_cast<uint8_t*>(C);
+  a.N1 = N1;
+  a.N2 = N2;
+  a.a_bytes = (uint32_t)((int64_t)pool_rows * N1 * 2);
+  a.b_bytes = (uint32_t)((int64_t)pool_rows * N2 * 2);
+  a.offsets = p.offsets;
+  a.counts = p.counts;
+  a.E = p.E_local;
+  a.tiles1 = N1 / kWgTile;
+  a.tiles2 = N2 / kWgTile;
+  int grid = workgroups > 0 ? workgroups : device_cu_count();
+  if (grid <= 0) return MOE_ERR_HIP;
+  grid = std::min(grid, a.E * a.tiles1 * a.tiles2);
+  hipLaunchKernelGGL(wgrad_kernel, dim3(grid), dim3(512), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+// --------------------------------------------------------------------------------
+// Load-time transposed weight permutation (bf16): out[e] is the fragment-ordered
+// tiled layout (the bf16 one of moe_pack_weights) of w[e]^T, a [K][rows] matrix.
+// One thread per 16-byte destination chunk, gathering its 8 values from 8 rows.
+// --------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void pack_weights_t_kernel(const uint16_t* w, uint8_t* out, int64_t chunks,
+                                                             int32_t rows, int32_t K) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= chunks) return;
+  // transposed matrix per expert: n over K (its rows), k over rows (its K)
+  const int64_t per_e = (int64_t)rows * K / 8;     // chunks per expert
+  const int64_t e = c / per_e;
+  const int64_t ce = c - e * per_e;
+  const int64_t tile = ce >> 6;
+  const int lane = (int)(ce & 63);
+  const int ktiles = rows / 32;                     // K tiles per 16-row block of w^T
+  const int64_t nb = tile / ktiles;
+  const int kb = (int)(tile - nb * ktiles);
+  const int64_t n = nb * 16 + (lane & 15);          // a column of w
+  const int64_t k0 = (int64_t)kb * 32 + 8 * (lane >> 4);  // rows of w
+  const uint16_t* src = w + e * (int64_t)rows * K;
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = (uint32_t)src[(k0 + 2 * i) * K + n] | ((uint32_t)src[(k0 + 2 * i + 1) * K + n] << 16);
+  *reinterpret_cast<u32x4*>(out + c * 16) = u32x4{o[0], o[1], o[2], o[3]};
+}
+
+int launch_pack_weights_t(const void* w, int32_t E, int32_t rows, int32_t K, void* out, hipStream_t stream) {
+  const int64_t chunks = (int64_t)E * rows * K / 8;
+  hipLaunchKernelGGL(pack_weights_t_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(w), static_cast<uint8_t*>(out), chunks, rows, K);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+}  // namespace moe

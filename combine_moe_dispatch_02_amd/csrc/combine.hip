@@ -32,7 +32,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int64_t pair0 = (int64_t)t * a.K;
   int p = lane < a.K ? a.pos[pair0 + lane] : -1;
   if (p >= a.pool_rows) p = -1;  // past the allocation: dispatch has reported it
-  const float wt = lane < a.K ? a.w[pair0 + lane] : 0.f;
+  const float wt = lane < a.K ? (a.w != nullptr ? a.w[pair0 + lane] : 1.0f) : 0.f;
   const uint64_t have = ballot(p >= 0);
   combine_token<CPL>(a.y, p, wt, have, a.K, a.H, a.out + (int64_t)t * a.H * 2, lane);
 }

@@ -84,6 +84,10 @@ struct FfnArgs {
   uint8_t* comb_out;         // out [T][H] bf16
   int32_t T, K;
   int32_t pool_rows;
+  // training: GEMM A stores G = [gate | up] (bf16 [rows][2I]) before the activation;
+  // the backward GEMM Y's SwiGLU-backward epilogue reads G there and writes dG over it
+  uint8_t* g_save;
+  int64_t g_ld;              // bytes per row of g_save (2I * 2)
 };
 
 __device__ inline uint32_t swz(int row, int chunk) { return (uint32_t)(row * 128 + ((chunk ^ (row & 7)) << 4)); }
@@ -520,8 +524,11 @@ __device__ inline uint32_t swz_a(int r, int c) {
 // step, and pairs K [16b, 16b+16) + [64+16b, 64+16b+16) of an e4m3 operand lane
 // block b with K [32b, 32b+32) of an e2m1 one: A fragments are therefore 16-byte
 // chunks b and b+4 of the row's 128-byte step.
-template <int BM, int NW, bool FP8, bool GEMM_A, bool PACKED, bool MX = false>
+// EPI (GEMM Y only): 0 stores y; 1 is the backward GEMM Y's epilogue -- the product
+// is dh, and with g, u from G it writes dG = [dh u silu'(g) | dh silu(g)] in place of G.
+template <int BM, int NW, bool FP8, bool GEMM_A, bool PACKED, bool MX = false, int EPI = 0>
 __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
+  static_assert(EPI == 0 || (!GEMM_A && !FP8), "the SwiGLU-backward epilogue is a bf16 GEMM Y one");
   static_assert(!MX || (FP8 && PACKED), "mxfp4 runs on the tiled e4m3 path");
   using C = Big<BM, NW, FP8, GEMM_A>;
   constexpr int TN = C::kTN, TM = C::kTM, KS = C::kKS, HALF = C::kHalf;
@@ -1026,6 +1033,22 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
         }
       };
       if constexpr (!FP8) {
+        if (a.g_save != nullptr) {
+          // training: keep G (gate and up before the activation) for the backward pass
+#pragma unroll
+          for (int tm = 0; tm < TM; ++tm) {
+            uint8_t* grow = a.g_save + (int64_t)(m0 + tm * 16 + l16) * a.g_ld;
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) {
+              const int half = tn < TN / 2 ? 0 : a.up_row0;
+              const int col = half + j * 256 + wn * HALF + (tn % (TN / 2)) * 16 + 4 * lhi;
+              u32x2 v;
+              v.x = pack_bf16x2(acc[tm][tn][0], acc[tm][tn][1]);
+              v.y = pack_bf16x2(acc[tm][tn][2], acc[tm][tn][3]);
+              *reinterpret_cast<u32x2*>(grow + (int64_t)col * 2) = v;
+            }
+          }
+        }
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) {
           const int r = tm * 16 + l16;
@@ -1109,6 +1132,52 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
         }
         __syncthreads();  // (also: every s_red read is done before the next unit writes it)
         hstore();
+      }
+    } else if constexpr (EPI == 1) {
+      // backward GEMM Y: acc = dh for row tm*16+l16, h columns c..c+3 of tile tn with
+      // c = j*512 + wn*64 + tn*16 + 4*lhi. g and u come from G (columns c and I + c), the
+      // results replace them: dg = dh u silu'(g), du = dh silu(g), s = 1 / (1 + e^-g),
+      // silu'(g) = s (1 + g (1 - s)). The next row tile's G is loaded one ahead.
+      const int I = a.up_row0;
+      auto grow = [&](int tm) { return a.g_save + (int64_t)(m0 + tm * 16 + l16) * a.g_ld; };
+      auto col = [&](int tn) { return (int64_t)(j * 512 + wn * C::kWCols + tn * 16 + 4 * lhi) * 2; };
+      u32x2 gv[2][TN], uv[2][TN];
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        gv[0][tn] = *reinterpret_cast<const u32x2*>(grow(0) + col(tn));
+        uv[0][tn] = *reinterpret_cast<const u32x2*>(grow(0) + (int64_t)I * 2 + col(tn));
+      }
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+        const int cb = tm & 1;
+        if (tm + 1 < TM) {
+#pragma unroll
+          for (int tn = 0; tn < TN; ++tn) {
+            gv[cb ^ 1][tn] = *reinterpret_cast<const u32x2*>(grow(tm + 1) + col(tn));
+            uv[cb ^ 1][tn] = *reinterpret_cast<const u32x2*>(grow(tm + 1) + (int64_t)I * 2 + col(tn));
+          }
+        }
+        uint8_t* gr = grow(tm);
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const float g[4] = {bf16_lo(gv[cb][tn].x), bf16_hi(gv[cb][tn].x), bf16_lo(gv[cb][tn].y), bf16_hi(gv[cb][tn].y)};
+          const float u[4] = {bf16_lo(uv[cb][tn].x), bf16_hi(uv[cb][tn].x), bf16_lo(uv[cb][tn].y), bf16_hi(uv[cb][tn].y)};
+          float dg[4], du[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g[i]));
+            const float dh = acc[tm][tn][i];
+            dg[i] = dh * u[i] * (sg * (1.0f + g[i] * (1.0f - sg)));
+            du[i] = dh * (g[i] * sg);
+          }
+          u32x2 o;
+          o.x = pack_bf16x2(dg[0], dg[1]);
+          o.y = pack_bf16x2(dg[2], dg[3]);
+          *reinterpret_cast<u32x2*>(gr + col(tn)) = o;
+          o.x = pack_bf16x2(du[0], du[1]);
+          o.y = pack_bf16x2(du[2], du[3]);
+          *reinterpret_cast<u32x2*>(gr + (int64_t)I * 2 + col(tn)) = o;
+        }
       }
     } else {
       // y rows go out in whole 128-byte segments: the wave's 64 columns of 64 rows at
@@ -1226,6 +1295,13 @@ static bool big_a_ok(int32_t H, int32_t I, int32_t dtype, int32_t tile) {
 static bool big_y_ok(int32_t H, int32_t I, int32_t dtype, int32_t tile) {
   if (dtype == MOE_FP8_E4M3_G128 || dtype == MOE_MXFP4) return tile == 128 && H % 512 == 0 && I % 256 == 0;
   return dtype == MOE_BF16 && (tile == 64 || tile == 128) && H % 512 == 0 && I % 128 == 0;
+}
+
+// training (G kept, backward available): bf16 on the big-tile kernel for both forward
+// GEMMs and both backward data GEMMs (N = I and N = H in 512-column blocks)
+bool ffn_train_ok(int32_t H, int32_t I, int32_t dtype, int32_t tile, int32_t block_n) {
+  return dtype == MOE_BF16 && big_a_ok(H, I, dtype, tile) && big_y_ok(H, I, dtype, tile) && I % 512 == 0 &&
+         H % 512 == 0 && (block_n == 0 || block_n == 512);
 }
 
 int ffn_supported(int32_t H, int32_t I, int32_t dtype, int32_t tile, int32_t block_n, int32_t weight_layout) {
@@ -1370,6 +1446,10 @@ int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream
   a.epoch = f.epoch;
   a.err = reinterpret_cast<uint32_t*>(ws + L.err);
   a.timeout = f.timeout_ticks;
+  if (f.g_pool != nullptr) {
+    a.g_save = static_cast<uint8_t*>(f.g_pool);
+    a.g_ld = (int64_t)4 * I;
+  }
   if (fuse) {
     a.ydone = reinterpret_cast<uint32_t*>(ws + L.ydone);
     a.cq = reinterpret_cast<uint32_t*>(ws + L.cq);
@@ -1420,6 +1500,7 @@ int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream
   if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
 
   // GEMM Y: h x w2^T -> y_pool (same stream, so every h row is complete)
+  a.g_save = nullptr;
   a.A = h;
   a.A_s = hs;
   a.B = static_cast<const uint8_t*>(f.w2);
@@ -1460,6 +1541,56 @@ int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream
   if (f.comb_out != nullptr && !fuse)
     return launch_combine(f.y_pool, f.pool_rows, f.topk_w, p, H, f.comb_out, stream);
   return MOE_OK;
+}
+
+// Backward data gradients on the big-tile kernel (bf16, tiled transposed weights):
+// out[rows][N] = A[rows][K] . Bt[e]^T per pool tile, Bt[e] = w[e]^T in fragment order.
+// epi 1 (backward GEMM Y): A = dy, Bt = W2^T [I][H], N = I; the epilogue turns dh into
+// dG in place of G (g_pool [rows][2I]). epi 0 (backward GEMM A): A = dG, Bt = W1^T
+// [H][2I], N = H, out = dx_pool.
+int launch_ffn_dgrad(const moe_plan_t& p, int32_t pool_rows, const void* A, const void* Bt, int32_t N, int32_t K,
+                     void* out, void* g_pool, int32_t I, int epi, int32_t workgroups, int32_t unit_order,
+                     const WsLayout& L, char* ws, hipStream_t stream) {
+  const int tile = p.tile;
+  FfnArgs a{};
+  a.tile_shift = __builtin_ctz((unsigned)tile);
+  a.max_tiles = pool_rows / tile;
+  a.n_experts = p.E_local;
+  a.offsets = p.offsets;
+  a.num_tiles = p.num_tiles;
+  a.tile_expert = p.tile_expert;
+  a.tile_ready = p.tile_ready;
+  a.err = reinterpret_cast<uint32_t*>(ws + L.err);
+  a.A = static_cast<const uint8_t*>(A);
+  a.B = static_cast<const uint8_t*>(Bt);
+  a.out = static_cast<uint8_t*>(out);
+  a.ksteps = K * 2 / 128;
+  a.lda = (int64_t)K * 2;
+  a.b_expert = (int64_t)N * K * 2;
+  a.ldb = (int64_t)K * 2;
+  a.up_row0 = epi == 1 ? I : 0;
+  a.ldo = (int64_t)N * 2;
+  a.n_units = N / 512;
+  a.wait_ready = 0;
+  a.unit_order = unit_order ? unit_order : 3;
+  a.ktiles = K / 32;
+  a.g_save = static_cast<uint8_t*>(g_pool);
+  a.g_ld = (int64_t)4 * I;
+  int grid = workgroups > 0 ? workgroups : device_cu_count();
+  if (grid <= 0) return MOE_ERR_HIP;
+  const int ntiles_cap = std::min(p.rows_cap, pool_rows) / tile;
+  grid = (int)std::max<int64_t>(1, std::min<int64_t>(grid, (int64_t)ntiles_cap * a.n_units));
+  constexpr int NW = kBigWaves;
+  if (tile == 128) {
+    if (epi == 1) hipLaunchKernelGGL((ffn_big_kernel<128, NW, false, false, true, false, 1>), dim3(grid), dim3(64 * NW), 0, stream, a);
+    else hipLaunchKernelGGL((ffn_big_kernel<128, NW, false, false, true, false, 0>), dim3(grid), dim3(64 * NW), 0, stream, a);
+  } else if (tile == 64) {
+    if (epi == 1) hipLaunchKernelGGL((ffn_big_kernel<64, NW, false, false, true, false, 1>), dim3(grid), dim3(64 * NW), 0, stream, a);
+    else hipLaunchKernelGGL((ffn_big_kernel<64, NW, false, false, true, false, 0>), dim3(grid), dim3(64 * NW), 0, stream, a);
+  } else {
+    return MOE_ERR_UNSUPPORTED;
+  }
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 }  // namespace moe

@@ -23,7 +23,8 @@ __all__ = [
     "pool_rows_upper_bound", "workspace_bytes", "moe_plan", "moe_query_pool_rows",
     "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_combine", "moe_combine", "moe_get_error",
     "moe_pack_weights",
-    "moe_pack_mx_scales",
+    "moe_pack_mx_scales", "moe_expert_ffn_train", "moe_combine_backward", "moe_expert_ffn_backward",
+    "moe_dispatch_backward", "moe_pack_weights_transposed",
     "device_cu_count", "MOE_WEIGHTS_ROW_MAJOR", "MOE_WEIGHTS_MFMA_TILED",
     "make_streams", "StreamMoE", "stream_moe",
 ]
@@ -208,6 +209,85 @@ def moe_expert_ffn_combine(plan: Plan, pool: torch.Tensor, pool_s: Optional[torc
         cfgp, _stream(stream)))
 
 
+def moe_expert_ffn_train(plan: Plan, pool: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, epoch: int,
+                         ws: Workspace, y_pool: torch.Tensor, g_pool: torch.Tensor,
+                         cfg: Optional[TileConfig] = None, stream=None) -> None:
+    """Training forward (bf16): moe_expert_ffn that also keeps G = [gate | up] in g_pool."""
+    H, I = _ffn_shapes(plan, pool, w1, w2, y_pool, MOE_BF16)
+    _need_cuda(g_pool, "g_pool", torch.bfloat16)
+    if g_pool.shape != (pool.shape[0], 2 * I):
+        raise ValueError("g_pool must be [pool rows, 2I]")
+    c = plan.c()
+    cfgp = ctypes.byref(cfg) if cfg is not None else None
+    check("moe_expert_ffn_train", load().moe_expert_ffn_train(
+        ctypes.byref(c), pool.shape[0], _vp(pool), _vp(w1), _vp(w2), H, I, epoch, _vp(ws.buf), ws.nbytes,
+        _vp(y_pool), _vp(g_pool), cfgp, _stream(stream)))
+
+
+def moe_combine_backward(dout: torch.Tensor, topk_weights: torch.Tensor, y_pool: torch.Tensor, plan: Plan,
+                         dy_pool: torch.Tensor, d_topk_weights: torch.Tensor, stream=None) -> None:
+    """dy_pool[pos[t,k]] = w[t,k] dout[t]; d_topk_weights[t,k] = <dout[t], y_pool[pos[t,k]]>.
+    dy_pool may be y_pool itself (each row is read before it is overwritten, by the same lane)."""
+    _need_cuda(dout, "dout", torch.bfloat16)
+    _need_cuda(topk_weights, "topk_weights", torch.float32)
+    _need_cuda(d_topk_weights, "d_topk_weights", torch.float32)
+    _need_cuda(y_pool, "y_pool", torch.bfloat16)
+    _need_cuda(dy_pool, "dy_pool", torch.bfloat16)
+    if dout.shape[0] != plan.T or topk_weights.shape != (plan.T, plan.K) or d_topk_weights.shape != (plan.T, plan.K):
+        raise ValueError("dout [T, H] / topk_weights / d_topk_weights [T, K] do not match the plan")
+    if dy_pool.shape != y_pool.shape or y_pool.shape[1] != dout.shape[1]:
+        raise ValueError("dy_pool and y_pool must be [pool rows, H]")
+    c = plan.c()
+    check("moe_combine_backward", load().moe_combine_backward(
+        _vp(dout), _vp(topk_weights), _vp(y_pool), y_pool.shape[0], ctypes.byref(c), dout.shape[1], _vp(dy_pool),
+        _vp(d_topk_weights), _stream(stream)))
+
+
+def moe_expert_ffn_backward(plan: Plan, pool: torch.Tensor, dy_pool: torch.Tensor, g_pool: torch.Tensor,
+                            w1t: torch.Tensor, w2t: torch.Tensor, ws: Workspace, dx_pool: torch.Tensor,
+                            dw1: torch.Tensor, dw2: torch.Tensor, cfg: Optional[TileConfig] = None,
+                            stream=None) -> None:
+    """Backward grouped GEMMs Y and A; g_pool's G is replaced by dG."""
+    for t, n in ((pool, "pool"), (dy_pool, "dy_pool"), (g_pool, "g_pool"), (w1t, "w1t"), (w2t, "w2t"),
+                 (dx_pool, "dx_pool"), (dw1, "dw1"), (dw2, "dw2")):
+        _need_cuda(t, n, torch.bfloat16)
+    rows, H = pool.shape
+    E, Ht, twoI = w1t.shape
+    I = twoI // 2
+    if Ht != H or E != plan.E_local or w2t.shape != (E, I, H) or g_pool.shape != (rows, twoI):
+        raise ValueError("w1t [E_local, H, 2I] / w2t [E_local, I, H] / g_pool [rows, 2I] do not match")
+    if dy_pool.shape != (rows, H) or dx_pool.shape != (rows, H):
+        raise ValueError("dy_pool / dx_pool must be [pool rows, H]")
+    if dw1.shape != (E, twoI, H) or dw2.shape != (E, H, I):
+        raise ValueError("dw1 [E_local, 2I, H] / dw2 [E_local, H, I] do not match")
+    c = plan.c()
+    cfgp = ctypes.byref(cfg) if cfg is not None else None
+    check("moe_expert_ffn_backward", load().moe_expert_ffn_backward(
+        ctypes.byref(c), rows, _vp(pool), _vp(dy_pool), _vp(g_pool), _vp(w1t), _vp(w2t), H, I, _vp(ws.buf),
+        ws.nbytes, _vp(dx_pool), _vp(dw1), _vp(dw2), cfgp, _stream(stream)))
+
+
+def moe_dispatch_backward(dx_pool: torch.Tensor, plan: Plan, dx: torch.Tensor, stream=None) -> None:
+    """dx[t] = sum over the token's local pairs of dx_pool[pos[t,k]]."""
+    _need_cuda(dx_pool, "dx_pool", torch.bfloat16)
+    _need_cuda(dx, "dx", torch.bfloat16)
+    if dx.shape[0] != plan.T or dx.shape[1] != dx_pool.shape[1]:
+        raise ValueError("dx must be [T, H]")
+    c = plan.c()
+    check("moe_dispatch_backward", load().moe_dispatch_backward(
+        _vp(dx_pool), dx_pool.shape[0], ctypes.byref(c), dx.shape[1], _vp(dx), _stream(stream)))
+
+
+def moe_pack_weights_transposed(w: torch.Tensor, dtype="bf16", stream=None) -> torch.Tensor:
+    """w [E, rows, K] (bf16) -> the tiled layout of each w[e]^T, a new [E, K, rows] tensor."""
+    _need_cuda(w, "w")
+    E, rows, K = w.shape
+    out = torch.empty(E, K, rows, dtype=w.dtype, device=w.device)
+    check("moe_pack_weights_transposed", load().moe_pack_weights_transposed(
+        _vp(w), E, rows, K, _dtype_code(dtype), _vp(out), _stream(stream)))
+    return out
+
+
 def moe_combine(y_pool: torch.Tensor, topk_weights: torch.Tensor, plan: Plan, out: torch.Tensor,
                 stream=None) -> None:
     _need_cuda(y_pool, "y_pool")
@@ -261,7 +341,7 @@ class StreamMoE:
 
     def __init__(self, T, H, I, K, num_local_experts, *, expert_begin=0, tile=128, dtype="bf16",
                  device="cuda", pool_rows: Optional[int] = None, cfg: Optional[TileConfig] = None,
-                 weight_layout: str = "auto", combine_on_completion: bool = False):
+                 weight_layout: str = "auto", combine_on_completion: bool = False, train: bool = False):
         self.T, self.H, self.I, self.K = T, H, I, K
         # GEMM Y's workgroups combine each token once its tiles are done (no FFN -> combine join)
         self.combine_on_completion = combine_on_completion
@@ -297,6 +377,15 @@ class StreamMoE:
         self.y_pool = torch.empty(rows, H, dtype=torch.bfloat16, device=device)
         self.out = torch.empty(T, H, dtype=torch.bfloat16, device=device)
         self.epoch = 0
+        # training: G kept by the forward (replaced by dG in backward), and the backward's buffers
+        self.train = train
+        if train:
+            if self.dtype != "bf16" or not self.tiled:
+                raise MoeError("StreamMoE(train=True)", _abi.MOE_ERR_UNSUPPORTED)
+            self.g_pool = torch.empty(rows, 2 * I, dtype=torch.bfloat16, device=device)
+            self.dx_pool = torch.empty(rows, H, dtype=torch.bfloat16, device=device)
+            self.dx = torch.empty(T, H, dtype=torch.bfloat16, device=device)
+            self.dw = torch.empty(T, K, dtype=torch.float32, device=device)
 
     def prepare_weights(self, w1, w2, w1_scale=None, w2_scale=None):
         """(w1, w2, w1_scale, w2_scale) as forward() wants them: permuted once into MFMA fragment
@@ -307,6 +396,25 @@ class StreamMoE:
         if self.dtype == "mxfp4":
             w1_scale, w2_scale = moe_pack_mx_scales(w1_scale), moe_pack_mx_scales(w2_scale)
         return moe_pack_weights(w1, self.dtype), moe_pack_weights(w2, self.dtype), w1_scale, w2_scale
+
+    def prepare_backward_weights(self, w1, w2):
+        """(w1t, w2t): the transposed, tiled weights the backward data GEMMs read (load time)."""
+        return moe_pack_weights_transposed(w1), moe_pack_weights_transposed(w2)
+
+    def backward(self, dout, topk_weights, w1t, w2t):
+        """Gradients of the last forward (train=True) for the output gradient dout [T, H]:
+        returns (dx [T, H] bf16, d_topk_weights [T, K] fp32, dw1 [E_local, 2I, H], dw2 [E_local, H, I]).
+        Runs on the current stream; y_pool is overwritten by dy."""
+        if not self.train:
+            raise RuntimeError("StreamMoE was built without train=True")
+        s = torch.cuda.current_stream()
+        dw1 = torch.empty(self.E_local, 2 * self.I, self.H, dtype=torch.bfloat16, device=dout.device)
+        dw2 = torch.empty(self.E_local, self.H, self.I, dtype=torch.bfloat16, device=dout.device)
+        moe_combine_backward(dout, topk_weights, self.y_pool, self.plan, self.y_pool, self.dw, s)
+        moe_expert_ffn_backward(self.plan, self.pool, self.y_pool, self.g_pool, w1t, w2t, self.ws, self.dx_pool,
+                                dw1, dw2, self.cfg, s)
+        moe_dispatch_backward(self.dx_pool, self.plan, self.dx, s)
+        return self.dx, self.dw, dw1, dw2
 
     def next_epoch(self) -> int:
         self.epoch = (self.epoch % 0xFFFFFFFF) + 1      # 1 .. 2^32-1; 0 is never a valid epoch
@@ -328,8 +436,12 @@ class StreamMoE:
                 moe_expert_ffn_combine(self.plan, self.pool, self.pool_s, w1, w1_scale, w2, w2_scale, epoch,
                                        self.ws, self.y_pool, topk_weights, self.out, self.dtype, self.cfg, s)
                 return self.out
-            moe_expert_ffn(self.plan, self.pool, self.pool_s, w1, w1_scale, w2, w2_scale, epoch,
-                           self.ws, self.y_pool, self.dtype, self.cfg, s)
+            if self.train:
+                moe_expert_ffn_train(self.plan, self.pool, w1, w2, epoch, self.ws, self.y_pool, self.g_pool,
+                                     self.cfg, s)
+            else:
+                moe_expert_ffn(self.plan, self.pool, self.pool_s, w1, w1_scale, w2, w2_scale, epoch,
+                               self.ws, self.y_pool, self.dtype, self.cfg, s)
             moe_combine(self.y_pool, topk_weights, self.plan, self.out, s)
             return self.out
         compute, comm = streams
@@ -347,8 +459,12 @@ class StreamMoE:
             cur.wait_stream(compute)
             cur.wait_stream(comm)
             return self.out
-        moe_expert_ffn(self.plan, self.pool, self.pool_s, w1, w1_scale, w2, w2_scale, epoch,
-                       self.ws, self.y_pool, self.dtype, self.cfg, compute)
+        if self.train:
+            moe_expert_ffn_train(self.plan, self.pool, w1, w2, epoch, self.ws, self.y_pool, self.g_pool,
+                                 self.cfg, compute)
+        else:
+            moe_expert_ffn(self.plan, self.pool, self.pool_s, w1, w1_scale, w2, w2_scale, epoch,
+                           self.ws, self.y_pool, self.dtype, self.cfg, compute)
         done = torch.cuda.Event()
         done.record(compute)
         comm.wait_event(done)

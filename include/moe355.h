@@ -217,6 +217,65 @@ MOE355_API int moe_expert_ffn_combine(const moe_plan_t* plan, int32_t pool_rows,
                                       const moe_tile_config* cfg, void* stream);
 
 /*
+ * Training forward (bf16). moe_expert_ffn, plus G = [gate | up] = pool_tile . w1[e]^T
+ * (before the activation) stored bf16 into g_pool [pool_rows][2I] for the backward
+ * pass; h stays in the workspace, where moe_expert_ffn_backward reads it. Needs the
+ * big-tile kernel for every GEMM of the pass: tile 64 or 128, H % 512 == 0,
+ * I % 512 == 0 (block_n 0 or 512); weights as for moe_expert_ffn.
+ * Errors: those of moe_expert_ffn; MOE_ERR_INVALID for a null g_pool;
+ * MOE_ERR_UNSUPPORTED for other shapes.
+ */
+MOE355_API int moe_expert_ffn_train(const moe_plan_t* plan, int32_t pool_rows, const void* pool, const void* w1,
+                                    const void* w2, int32_t H, int32_t I, uint32_t epoch, void* ws, size_t ws_bytes,
+                                    void* y_pool, void* g_pool, const moe_tile_config* cfg, void* stream);
+
+/*
+ * Backward of A5 (StreamEP README, "How it works": the backward pass mirrors the
+ * forward, so combine's backward is a scatter into the pool). For every local pair
+ * (t, k) with row p = pos[t,k]: dy_pool[p] = topk_weights[t,k] * dout[t] (fp32 product,
+ * bf16 RNE store) and d_topk_weights[t,k] = sum_h dout[t,h] * y_pool[p,h] (fp32);
+ * d_topk_weights is 0 for non-local pairs. dout: device bf16 [T][H]; y_pool as
+ * written by the forward; dy_pool: device bf16 [pool_rows][H] (padding rows are not
+ * written); d_topk_weights: device fp32 [T][K].
+ * Errors: MOE_ERR_INVALID (null pointers), MOE_ERR_UNSUPPORTED (H % 8 != 0).
+ */
+MOE355_API int moe_combine_backward(const void* dout, const float* topk_weights, const void* y_pool,
+                                    int32_t pool_rows, const moe_plan_t* plan, int32_t H, void* dy_pool,
+                                    float* d_topk_weights, void* stream);
+
+/*
+ * Backward grouped GEMMs Y and A (StreamEP README, "How it works": the four grouped
+ * GEMMs are forward A / Y and backward A / Y), bf16, after moe_expert_ffn_train with
+ * the same plan, pool and workspace:
+ *   backward Y: dh = dy_pool . W2[e]; dG = [dh * u * silu'(g) | dh * silu(g)] with
+ *               g, u from G, written over G in g_pool; dW2[e] = sum over the expert's
+ *               real rows of dy^T h (h from the workspace);
+ *   backward A: dx_pool = dG . W1[e]; dW1[e] = sum over the real rows of dG^T x.
+ * silu'(z) = s (1 + z (1 - s)), s = 1 / (1 + exp(-z)); fp32 accumulation, bf16 (RNE)
+ * results. w1t / w2t: the weights transposed and tiled by moe_pack_weights_transposed
+ * (w1 [E][2I][H] -> its [H][2I] transposes, w2 [E][H][I] -> [I][H]). Outputs: dx_pool
+ * bf16 [pool_rows][H] (padding rows hold garbage, never read by moe_dispatch_backward),
+ * dw1 bf16 [E_local][2I][H], dw2 bf16 [E_local][H][I] (zero for an expert with no
+ * pair). Padding rows of dy_pool are excluded from the weight gradients.
+ * Errors: MOE_ERR_INVALID (null pointers, bad pool_rows, small workspace, bad cfg),
+ * MOE_ERR_UNSUPPORTED (shapes outside moe_expert_ffn_train's, or a pool whose
+ * pool_rows * max(2I, H) * 2 bytes reach 4 GiB).
+ */
+MOE355_API int moe_expert_ffn_backward(const moe_plan_t* plan, int32_t pool_rows, const void* pool,
+                                       const void* dy_pool, void* g_pool, const void* w1t, const void* w2t, int32_t H,
+                                       int32_t I, void* ws, size_t ws_bytes, void* dx_pool, void* dw1, void* dw2,
+                                       const moe_tile_config* cfg, void* stream);
+
+/*
+ * Backward of A2 (the mirror of dispatch: a gather-sum): dx[t] = sum over k with
+ * pos[t,k] >= 0, in ascending k, of dx_pool[pos[t,k]], fp32, bf16 (RNE) store; a token
+ * with no local pair gets zeros. dx_pool: device bf16 [pool_rows][H]; dx: device bf16
+ * [T][H]. Errors: MOE_ERR_INVALID (null pointers), MOE_ERR_UNSUPPORTED (H % 8 != 0).
+ */
+MOE355_API int moe_dispatch_backward(const void* dx_pool, int32_t pool_rows, const moe_plan_t* plan, int32_t H,
+                                     void* dx, void* stream);
+
+/*
  * A5. Combine: out[t] = sum over k with pos[t,k] >= 0, in ascending k, of
  * topk_weights[t,k] * y_pool[pos[t,k]], accumulated in fp32 and stored bf16
  * (round to nearest even). Every row of out (bf16 [T][H]) is written; a token
@@ -251,6 +310,17 @@ MOE355_API int moe_combine(const void* y_pool, int32_t pool_rows, const float* t
  */
 MOE355_API int moe_pack_weights(const void* w, int32_t E, int32_t rows, int32_t K, int32_t dtype, void* out,
                                 void* stream);
+
+/*
+ * Load-time transposed re-layout for the backward data GEMMs (bf16 only): out[e] is
+ * the bf16 tiled layout of moe_pack_weights applied to w[e]^T, the [K][rows] transpose
+ * of w[e] ([rows][K] row-major): tile (nb, kb) of 16 x 32 at byte ((nb * rows/32) + kb)
+ * * 1024, lane l holding w[e][kb*32 + 8*(l/16) + i][nb*16 + l%16], i = 0..7.
+ * Errors: MOE_ERR_INVALID (null pointers, sizes < 1, unknown dtype, overlap),
+ * MOE_ERR_UNSUPPORTED (fp8 / mxfp4, K % 16 != 0, rows % 32 != 0).
+ */
+MOE355_API int moe_pack_weights_transposed(const void* w, int32_t E, int32_t rows, int32_t K, int32_t dtype,
+                                           void* out, void* stream);
 
 /*
  * Load-time permutation of MXFP4 weight scales (E8M0 bytes, device, [E][rows][K/32]

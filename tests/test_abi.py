@@ -28,7 +28,7 @@ def lib():
 def test_header_declares_the_four_calls():
     names = set(declared_symbols())
     assert {"moe_plan", "moe_dispatch", "moe_expert_ffn", "moe_combine"} <= names
-    assert len(names) == 13
+    assert len(names) == 18
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -175,6 +175,37 @@ def test_ffn_combine_validation(lib):
     assert call(out=None) == 1
     assert call(epoch=0) == 1
     assert call(H=100) == 2
+
+
+def test_backward_validation(lib):
+    p = _fake_plan()
+    v = [ctypes.c_void_p(a) for a in range(0x10000, 0x10000 * 12, 0x10000)]
+    big = 1 << 40
+    # training forward: g_pool required; tile 16 is outside the big-tile kernel
+    assert lib.moe_expert_ffn_train(ctypes.byref(p), 256, v[0], v[1], v[2], 512, 512, 1, v[3], big, v[4], None,
+                                    None, None) == 1
+    assert lib.moe_expert_ffn_train(ctypes.byref(p), 256, v[0], v[1], v[2], 512, 512, 1, v[3], big, v[4], v[5],
+                                    None, None) == 2
+    # combine backward
+    assert lib.moe_combine_backward(None, v[1], v[2], 256, ctypes.byref(p), 128, v[3], v[4], None) == 1
+    assert lib.moe_combine_backward(v[0], v[1], v[2], 256, ctypes.byref(p), 100, v[3], v[4], None) == 2
+    # expert backward: null pointer, then tile 16 / shapes outside the kernels
+    assert lib.moe_expert_ffn_backward(ctypes.byref(p), 256, v[0], None, v[2], v[3], v[4], 512, 512, v[5], big,
+                                       v[6], v[7], v[8], None, None) == 1
+    assert lib.moe_expert_ffn_backward(ctypes.byref(p), 256, v[0], v[1], v[2], v[3], v[4], 512, 512, v[5], big,
+                                       v[6], v[7], v[8], None, None) == 2
+    q = _fake_plan(tile=128, rows_cap=oracle.pool_rows_bound(64, 2, 8, 128))
+    assert lib.moe_expert_ffn_backward(ctypes.byref(q), 256, v[0], v[1], v[2], v[3], v[4], 512, 256, v[5], big,
+                                       v[6], v[7], v[8], None, None) == 2      # I % 512
+    # dispatch backward
+    assert lib.moe_dispatch_backward(None, 256, ctypes.byref(p), 128, v[1], None) == 1
+    assert lib.moe_dispatch_backward(v[0], 256, ctypes.byref(p), 100, v[1], None) == 2
+    # transposed pack: bf16 only, K % 16, rows % 32
+    W, OUT = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x100000000)
+    assert lib.moe_pack_weights_transposed(W, 1, 32, 16, 1, OUT, None) == 2
+    assert lib.moe_pack_weights_transposed(W, 1, 32, 16, 7, OUT, None) == 1
+    assert lib.moe_pack_weights_transposed(W, 1, 48, 16, 0, OUT, None) == 2
+    assert lib.moe_pack_weights_transposed(W, 1, 32, 24, 0, OUT, None) == 2
 
 
 def test_combine_validation(lib):

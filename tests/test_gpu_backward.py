@@ -1,0 +1,126 @@
+"""The backward pass on the GPU against the oracle's exact gradients (bf16 workloads):
+dx, the gradient of topk_weights, dW1 and dW2, max-normwise relative error <= 1e-2
+each; the training forward keeps G (checked against the oracle's G) and leaves out
+bitwise unchanged; the transposed weight re-layout is checked bit for bit.
+
+Small shapes are compared on every element; the skew workload at full size on sampled
+tokens (dx, d_topk_weights) and on the weight gradients of sampled experts."""
+import numpy as np
+import pytest
+import torch
+
+import combine_moe_dispatch_02_amd as moe
+import oracle
+from synth import MoEConfig, config_by_name, make_dout, make_inputs
+
+from _gpu import dev_inputs, make_layer, rel_err, run_layer, say
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+
+CASES = [
+    MoEConfig("bwd_t128", 300, 512, 512, 6, 0, 6, 2, 128),
+    MoEConfig("bwd_t64_ep", 517, 1024, 512, 9, 2, 5, 4, 64),       # experts 2..6 local, ragged tiles
+    MoEConfig("bwd_wide", 640, 1536, 1024, 5, 0, 5, 3, 128),
+]
+
+
+def expected_t(w):                   # bf16 bits [E, R, K] -> tiled layout of each transpose
+    E, R, K = w.shape
+    wt = np.ascontiguousarray(w.transpose(0, 2, 1))          # [E, K, R]
+    return wt.reshape(E, K // 16, 16, R // 32, 4, 8).transpose(0, 1, 3, 4, 2, 5).reshape(E, K, R)
+
+
+@pytest.mark.parametrize("shape", [(1, 32, 16), (3, 64, 48), (2, 1024, 512)])
+def test_pack_transposed_exact(shape):
+    g = torch.Generator().manual_seed(sum(shape) + 7)
+    w = torch.randint(-32768, 32767, shape, generator=g, dtype=torch.int16)
+    say("pack transposed", shape)
+    got = moe.moe_pack_weights_transposed(w.cuda().view(torch.bfloat16))
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().view(torch.int16).numpy(), expected_t(w.numpy()))
+
+
+def _train_run(cfg, seed=None):
+    inp = make_inputs(cfg) if seed is None else make_inputs(cfg, seed)
+    d = dev_inputs(inp)
+    layer = make_layer(cfg, train=True)
+    w1, w2, _, _ = layer.prepare_weights(d["w1"], d["w2"])
+    w1t, w2t = layer.prepare_backward_weights(d["w1"], d["w2"])
+    out = layer.forward(d["x"], d["idx"], d["w"], w1, w2).clone()
+    g_saved = layer.g_pool.clone()
+    dout = make_dout(cfg, inp.seed)
+    dx, dw, dW1, dW2 = layer.backward(dout.cuda(), d["w"], w1t, w2t)
+    torch.cuda.synchronize()
+    assert moe.moe_get_error(layer.ws) == 0
+    return inp, d, layer, out, g_saved, dout, dx.clone(), dw.clone(), dW1, dW2
+
+
+def _bf(t):
+    return oracle.bf16_to_f64(t.cpu())
+
+
+@pytest.mark.parametrize("cfg", CASES, ids=[c.name for c in CASES])
+def test_backward_full_compare(cfg):
+    say("backward", cfg.name)
+    inp, d, layer, out, g_saved, dout, dx, dw, dW1, dW2 = _train_run(cfg)
+    # the training forward computes the same out as the inference one
+    ref_layer = make_layer(cfg)
+    ref_out = run_layer(ref_layer, d)
+    assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
+    g = oracle.moe_layer_backward(inp, dout)
+    errs = {
+        "dx": rel_err(_bf(dx), g.dx),
+        "dw": rel_err(dw.cpu().numpy().astype(np.float64), g.dw),
+        "dW1": rel_err(_bf(dW1), g.dW1),
+        "dW2": rel_err(_bf(dW2), g.dW2),
+    }
+    print(cfg.name, {k: f"{v:.2e}" for k, v in errs.items()})
+    assert max(errs.values()) <= TOL, errs
+    # G as kept by the forward, on the real rows
+    src = layer.plan.src.cpu().numpy()
+    rows = np.nonzero(src >= 0)[0]
+    x = oracle.bf16_to_f64(inp.x)
+    ids = inp.topk_idx.numpy().reshape(-1)[src[rows]] - cfg.expert_begin
+    G_ref = np.empty((rows.size, 2 * cfg.I))
+    for e in np.unique(ids):
+        W1 = oracle.bf16_to_f64(inp.w1[e])
+        m = ids == e
+        G_ref[m] = x[src[rows][m] // cfg.K] @ W1.T
+    assert rel_err(_bf(g_saved)[rows], G_ref) <= TOL
+    # tokens without a local pair get zero gradients
+    none_local = ~((inp.topk_idx.numpy() >= cfg.expert_begin)
+                   & (inp.topk_idx.numpy() < cfg.expert_begin + cfg.num_local_experts)).any(axis=1)
+    assert (_bf(dx)[none_local] == 0).all() and (dw.cpu().numpy()[none_local] == 0).all()
+
+
+def test_backward_full_size_skew_sampled():
+    cfg = config_by_name("zipf_skew")
+    say("backward full size", cfg.name)
+    inp, d, layer, out, g_saved, dout, dx, dw, dW1, dW2 = _train_run(cfg)
+    idx = inp.topk_idx.numpy()
+    counts = np.bincount(idx.reshape(-1), minlength=cfg.num_experts)
+    # weight gradients of four experts: the coldest non-empty one, a quartile, the median,
+    # and the eighth hottest (a few thousand rows: many K steps of the weight-gradient GEMM)
+    nz = np.nonzero(counts)[0]
+    order = nz[np.argsort(counts[nz])]
+    experts = [int(order[0]), int(order[len(order) // 4]), int(order[len(order) // 2]), int(order[-8])]
+    g = oracle.moe_layer_backward(inp, dout, experts=experts)
+    for e in experts:
+        e1 = rel_err(_bf(dW1[e]), g.dW1[e])
+        e2 = rel_err(_bf(dW2[e]), g.dW2[e])
+        print(f"expert {e} ({counts[e]} rows): dW1 {e1:.2e} dW2 {e2:.2e}")
+        assert e1 <= TOL and e2 <= TOL
+    # dx and d_topk_weights of tokens whose pairs all lie in those experts' segments are
+    # complete in g; check those tokens
+    full = np.isin(idx, experts).all(axis=1)
+    part = np.isin(idx, experts)
+    toks = np.nonzero(full)[0]
+    if toks.size:
+        assert rel_err(_bf(dx)[toks], g.dx[toks]) <= TOL
+    assert rel_err(dw.cpu().numpy()[part].astype(np.float64), g.dw[part]) <= TOL
+    # an expert with no pair has zero weight gradients
+    empty = np.nonzero(counts == 0)[0]
+    if empty.size:
+        assert not bool(dW1[int(empty[0])].float().abs().sum()) and not bool(dW2[int(empty[0])].float().abs().sum())
