@@ -161,6 +161,100 @@ def summarize_profiles(workload, trace_dir, fetch_dir, write_dir, out_dir, comma
     print(js)
 
 
+def train_bench(args, cfg):
+    """Training step = forward (plan, dispatch, FFN keeping G, combine) + backward (combine
+    backward, backward grouped GEMMs Y and A with their weight gradients, dispatch backward)."""
+    import torch
+
+    import combine_moe_dispatch_02_amd as moe
+    from synth import make_dout, make_inputs
+
+    if cfg.dtype != "bf16":
+        raise SystemExit("--train runs the bf16 workloads")
+    log(f"[bench] generating {cfg.name} inputs (training)")
+    inp = make_inputs(cfg, pin_memory=True)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x, idx, w = inp.x.to(dev), inp.topk_idx.to(dev), inp.topk_weights.to(dev)
+    dout = make_dout(cfg, inp.seed).to(dev)
+    layer = moe.StreamMoE(cfg.T, cfg.H, cfg.I, cfg.K, cfg.num_local_experts, expert_begin=cfg.expert_begin,
+                          tile=cfg.tile, dtype="bf16", train=True)
+    w1d, w2d = inp.w1.to(dev), inp.w2.to(dev)
+    w1, w2, _, _ = layer.prepare_weights(w1d, w2d)
+    w1t, w2t = layer.prepare_backward_weights(w1d, w2d)
+    del w1d, w2d
+    torch.cuda.synchronize()
+    work = algorithmic_work(cfg, inp.topk_idx.numpy())
+
+    def step():
+        layer.forward(x, idx, w, w1, w2)
+        return layer.backward(dout, w, w1t, w2t)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if moe.moe_get_error(layer.ws) != 0:
+        raise RuntimeError("device error during warmup")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # stages on the stream the calls run on
+    s = torch.cuda.current_stream()
+    names = ["plan", "dispatch", "ffn_train", "combine", "combine_backward", "ffn_backward", "dispatch_backward"]
+    acc = dict.fromkeys(names, 0.0)
+    dw1 = torch.empty(cfg.num_local_experts, 2 * cfg.I, cfg.H, dtype=torch.bfloat16, device=dev)
+    dw2 = torch.empty(cfg.num_local_experts, cfg.H, cfg.I, dtype=torch.bfloat16, device=dev)
+    evs = []
+    for _ in range(args.steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+        ep = layer.next_epoch()
+        ev[0].record(s)
+        moe.moe_plan(idx, layer.plan, layer.ws, s); ev[1].record(s)
+        moe.moe_dispatch(x, layer.plan, layer.pool, None, ep, layer.ws, "bf16", s); ev[2].record(s)
+        moe.moe_expert_ffn_train(layer.plan, layer.pool, w1, w2, ep, layer.ws, layer.y_pool, layer.g_pool,
+                                 layer.cfg, s); ev[3].record(s)
+        moe.moe_combine(layer.y_pool, w, layer.plan, layer.out, s); ev[4].record(s)
+        moe.moe_combine_backward(dout, w, layer.y_pool, layer.plan, layer.y_pool, layer.dw, s); ev[5].record(s)
+        moe.moe_expert_ffn_backward(layer.plan, layer.pool, layer.y_pool, layer.g_pool, w1t, w2t, layer.ws,
+                                    layer.dx_pool, dw1, dw2, layer.cfg, s); ev[6].record(s)
+        moe.moe_dispatch_backward(layer.dx_pool, layer.plan, layer.dx, s); ev[7].record(s)
+        evs.append(ev)
+    torch.cuda.synchronize()
+    if moe.moe_get_error(layer.ws) != 0:
+        raise RuntimeError("device error during timing")
+    for ev in evs:
+        for i, k in enumerate(names):
+            acc[k] += ev[i].elapsed_time(ev[i + 1]) / len(evs)
+    bwd_flops = 2 * work["ffn_flops"]          # data and weight gradients of both GEMMs
+    bwd_tflops = bwd_flops / (acc["ffn_backward"] * 1e-3) / 1e12
+    result = {
+        "metric": "MoE layer training step tokens/s (forward + backward); backward grouped GEMMs % MFMA peak",
+        "value": round(cfg.T / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "I": cfg.I, "experts": cfg.num_experts,
+                   "local_experts": cfg.num_local_experts, "K": cfg.K, "tile": cfg.tile, "routing": cfg.routing,
+                   "pairs": work["pairs"], "mode": "training step (forward keeping G + backward)"},
+        "roofline": {"bound": "mfma", "kernel": "backward grouped GEMMs (dgrad + wgrad of A and Y)",
+                     "achieved": round(bwd_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "stages_ms": {k: round(v, 4) for k, v in acc.items()},
+        "ffn_train_TFLOPs": round(work["ffn_flops"] / (acc["ffn_train"] * 1e-3) / 1e12, 1),
+        "ffn_backward_TFLOPs": round(bwd_tflops, 1),
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -168,6 +262,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="zipf_skew")
     ap.add_argument("--streams", action="store_true", help="dispatch/combine and FFN on two streams")
+    ap.add_argument("--train", action="store_true",
+                    help="time a training step: the forward (keeping G) plus the backward pass (bf16 workloads)")
     ap.add_argument("--combine-on-completion", action="store_true",
                     help="GEMM Y's workgroups combine each token once its tiles are done (no separate combine)")
     ap.add_argument("--block-n", type=int, default=0, help="tile config override: N block (0 = auto)")
@@ -197,6 +293,9 @@ def main():
     from synth import config_by_name, make_inputs
 
     cfg = config_by_name(args.workload)
+    if args.train:
+        train_bench(args, cfg)
+        return
     fp8 = cfg.dtype == "fp8"
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0").fill_(1)

@@ -11,6 +11,7 @@
 //   dispatch backward is the combine kernel with unit weights (combine.hip), and the
 //   data gradients run on the forward's big-tile kernel (ffn.hip).
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -132,14 +133,20 @@ int launch_combine_backward(const void* dout, const float* topk_weights, const v
 // MFMA layout with the B fragment first, so a lane holds one N1 row and four
 // consecutive N2 columns.
 //
-// The contraction runs over pool rows, while MFMA fragments want 8 consecutive K
-// values per lane: each K step (64 rows) every thread loads one 8 x 8 block (8 rows
-// x 16 bytes) of A or B, transposes it in registers (32 byte permutes), and writes
-// its 8 columns as 16-byte K chunks into an LDS tile [n][64 K] (128-byte rows, chunk
-// slot swizzled by (n ^ n/8) & 7: conflict-free for the fragment reads, which walk
-// n, and for the writes, which walk n/8). Rows past the segment's real rows load as
-// zeros (out of the buffer's range). Two LDS stages; the next step's loads are in
-// flight during this step's MFMAs; one barrier per step.
+// The contraction runs over pool rows, so both operands arrive K-major: a K step is 32
+// pool rows of the 256 A columns and of the 256 B columns, copied as they are into LDS
+// by LDS-DMA (512-byte rows, 16-byte chunks permuted per row by wg_swz; the DMA lands
+// lane i at base + 16 i, so the permutation goes into the source addresses). The
+// MFMA fragments (8 consecutive K of one column per lane) come out of the row-major
+// tile through gfx950's transposing LDS read, ds_read_b64_tr_b16: within each group of
+// 16 lanes, lane j reads 4 consecutive bf16 and lane i receives element i%4 of lanes
+// i/4 + 4q, q = 0..3 -- so lane j of group g addresses row 8g + j/4 (+4 for the second
+// half of the fragment), columns 4(j%4)..+4 of the 16-column block. Rows past the
+// segment's real rows are read out of the buffer's range and land as zeros. A ring of
+// four stages keeps three steps of DMA in flight (no registers held); one barrier per
+// step, after a vmcnt wait that leaves the two newer steps outstanding. The stages are
+// separate LDS objects used with constant indices, so the compiler can tell a step's
+// reads from the DMA writes in flight (and adds no wait of its own).
 // --------------------------------------------------------------------------------
 struct WgradArgs {
   const uint8_t* A;
@@ -154,18 +161,31 @@ struct WgradArgs {
 };
 
 constexpr int kWgTile = 256;
-constexpr int kWgK = 64;
+constexpr int kWgK = 32;                        // pool rows per K step
+constexpr int kWgOpBytes = kWgK * kWgTile * 2;  // one operand's rows of a step: 16 KiB
 constexpr int kWgMaxE = 1024;
 
-__device__ inline uint32_t wg_swz(int n, int chunk) {
-  return (uint32_t)(n * 128 + (((chunk ^ n ^ (n >> 3)) & 7) << 4));
-}
-
+typedef __bf16 wg_bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 wg_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float wg_f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) wg_bf16x4 wg_lds_bf16x4;
+
+// byte of (row, byte b of the row) in a step's operand tile (512-byte rows)
+__device__ inline void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0) only
+
+// A transposing read touches 16 rows (8g + q and, for the second half, 8g + 4 + q; g, q
+// = 0..3) at one 32-byte column segment; rows are 512 bytes apart, so the segment is moved
+// by (q | g << 2) pairs of chunks: the 16 rows of a read land on 16 distinct 32-byte slots.
+__device__ inline int wg_swz(int row) { return (((row & 3) | (((row >> 3) & 3) << 2)) << 1); }
+__device__ inline uint32_t wg_at(int row, int b) {
+  return (uint32_t)(row * 512 + ((((b >> 4) ^ wg_swz(row))) << 4) + (b & 15));
+}
 
 __global__ __launch_bounds__(512, 1) void wgrad_kernel(WgradArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_t[2][2][kWgTile * 128];  // [stage][A,B]
+  __shared__ __attribute__((aligned(16))) uint8_t s_t0[2][kWgOpBytes];  // [A, B]
+  __shared__ __attribute__((aligned(16))) uint8_t s_t1[2][kWgOpBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_t2[2][kWgOpBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_t3[2][kWgOpBytes];
   __shared__ int s_order[kWgMaxE];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -192,15 +212,19 @@ __global__ __launch_bounds__(512, 1) void wgrad_kernel(WgradArgs a) {
   const int G = gridDim.x;
   const int slot = (G & 7) == 0 ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
 
-  // this thread's 8 x 8 block of the step: operand (A for tid < 256), row block, column block
-  const bool is_b = tid >= 256;
-  const int q = tid & 255;
-  const int rb = q >> 5;             // rows 8*rb .. 8*rb+7 of the step
-  const int cb = q & 31;             // columns 8*cb .. 8*cb+7 of the tile
+  // DMA duty: wave w copies 1 KiB blocks 4w..4w+3 of a step (blocks 0..15: A, 16..31: B),
+  // a block being two 512-byte rows; lane i lands at byte 16 i of its block
+  const int blk0 = wave * 4;
+  const bool dma_b = blk0 >= 16;
+  const int lrow = (lane >> 5);      // row of the block this lane fills
+  const int lchunk = lane & 31;      // LDS chunk slot it fills
+  // fragment addressing: this lane's row in the 4-row group and its byte in the 16-column block
+  const int frow = 8 * lhi + (l16 >> 2);
+  const int fbyte = 8 * (l16 & 3);
 
   for (int round = 0;; ++round) {
-    const int u = round * G + ((round & 1) ? G - 1 - slot : slot);
     if (round * G >= total) break;
+    const int u = round * G + ((round & 1) ? G - 1 - slot : slot);
     if (u >= total) continue;
     const int e = s_order[u / per_e];
     const int tix = u % per_e;
@@ -209,32 +233,39 @@ __global__ __launch_bounds__(512, 1) void wgrad_kernel(WgradArgs a) {
     const int cnt = a.counts[e];
     const int nsteps = (cnt + kWgK - 1) / kWgK;
 
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(is_b ? a.B : a.A, is_b ? a.b_bytes : a.a_bytes);
-    const uint32_t ld = (uint32_t)(is_b ? a.N2 : a.N1) * 2u;
-    const uint32_t col_off = (uint32_t)((is_b ? t2 : t1) * kWgTile + cb * 8) * 2u;
-    const uint32_t oob = is_b ? a.b_bytes : a.a_bytes;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(dma_b ? a.B : a.A, dma_b ? a.b_bytes : a.a_bytes);
+    const uint32_t ld = (uint32_t)(dma_b ? a.N2 : a.N1) * 2u;
+    const uint32_t col0 = (uint32_t)((dma_b ? t2 : t1) * kWgTile) * 2u;
+    const uint32_t oob = dma_b ? a.b_bytes : a.a_bytes;
 
-    u32x4 v[8];
-    auto load = [&](int s) {
+    auto stage = [&](auto ST) -> uint8_t(*)[kWgOpBytes] {
+      constexpr int k = decltype(ST)::value;
+      if constexpr (k == 0) return s_t0;
+      else if constexpr (k == 1) return s_t1;
+      else if constexpr (k == 2) return s_t2;
+      else return s_t3;
+    };
+    auto dma = [&](int s, auto ST) {
+      uint8_t* base = &stage(ST)[dma_b ? 1 : 0][0];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = s * kWgK + rb * 8 + i;   // row within the segment
-        const uint32_t off = r < cnt ? (uint32_t)(r0 + r) * ld + col_off : oob;  // past the range: zeros
-        v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+      for (int q = 0; q < 4; ++q) {
+        const int blk = (blk0 + q) & 15;
+        const int row = 2 * blk + lrow;                  // row of the step
+        const int r = s * kWgK + row;                    // row of the segment
+        const uint32_t off = r < cnt ? (uint32_t)(r0 + r) * ld + col0 + (uint32_t)((lchunk ^ wg_swz(row)) << 4) : oob;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void*)(base + blk * 1024), 16, off, 0, 0, 0);
       }
     };
-    auto store = [&](int st) {
-      uint8_t* base = &s_t[st][is_b ? 1 : 0][0];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-        u32x4 o;
-        o.x = __builtin_amdgcn_perm(v[1][c >> 1], v[0][c >> 1], sel);
-        o.y = __builtin_amdgcn_perm(v[3][c >> 1], v[2][c >> 1], sel);
-        o.z = __builtin_amdgcn_perm(v[5][c >> 1], v[4][c >> 1], sel);
-        o.w = __builtin_amdgcn_perm(v[7][c >> 1], v[6][c >> 1], sel);
-        *reinterpret_cast<u32x4*>(base + wg_swz(cb * 8 + c, rb)) = o;
-      }
+    // fr, fb: this lane's fragment row and byte, passed through an empty asm at each step
+    // so the compiler recomputes the 48 read addresses per step instead of keeping them
+    // all live across the loop
+    auto frag = [&](const uint8_t* tile, int col16, int fr, int fbt) {   // columns col16..col16+15
+      const uint8_t* p0 = tile + wg_at(fr, col16 * 2 + fbt);
+      const uint8_t* p1 = tile + wg_at(fr + 4, col16 * 2 + fbt);
+      const wg_bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((wg_lds_bf16x4*)(p0));
+      const wg_bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((wg_lds_bf16x4*)(p1));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     };
 
     wg_f32x4 acc[8][4];
@@ -243,32 +274,58 @@ __global__ __launch_bounds__(512, 1) void wgrad_kernel(WgradArgs a) {
 #pragma unroll
       for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = wg_f32x4{0.f, 0.f, 0.f, 0.f};
 
-    if (nsteps > 0) {
-      load(0);
-      store(0);
-    }
+    // prologue: steps 0..2 in flight, wait for step 0. Every step issues its 4 DMAs
+    // (rows past the segment read zeros), so the counts below are exact.
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    using C2 = std::integral_constant<int, 2>;
+    using C3 = std::integral_constant<int, 3>;
+    dma(0, C0{});
+    dma(1, C1{});
+    dma(2, C2{});
+    __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): step 0 has landed
     __syncthreads();
-    for (int s = 0; s < nsteps; ++s) {
-      const int st = s & 1;
-      if (s + 1 < nsteps) load(s + 1);
-      const uint8_t* ta = &s_t[st][0][0];
-      const uint8_t* tb = &s_t[st][1][0];
+    // step s computes from stage s % 4 and sends step s+3 into stage (s+3) % 4, the one
+    // step s-1 read (all its reads are behind the last barrier)
+    auto step = [&](int s, auto ST, auto SN) {
+      int fr = frow, fbt = fbyte;
+      asm volatile("" : "+v"(fr), "+v"(fbt));
+      __builtin_amdgcn_sched_barrier(0);
+      dma(s + 3, SN);
+      const uint8_t* ta = &stage(ST)[0][0];
+      const uint8_t* tb = &stage(ST)[1][0];
+      wg_bf16x8 fb[4];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        wg_bf16x8 fb[4];
+      for (int tn = 0; tn < 4; ++tn) fb[tn] = frag(tb, wn * 64 + tn * 16, fr, fbt);
+      wg_bf16x8 fa_cur = frag(ta, wm * 128, fr, fbt);
+#pragma unroll
+      for (int tm = 0; tm < 8; ++tm) {
+        wg_bf16x8 fa_next = fa_cur;
+        if (tm + 1 < 8) fa_next = frag(ta, wm * 128 + (tm + 1) * 16, fr, fbt);
 #pragma unroll
         for (int tn = 0; tn < 4; ++tn)
-          fb[tn] = *reinterpret_cast<const wg_bf16x8*>(tb + wg_swz(wn * 64 + tn * 16 + l16, kk * 4 + lhi));
-#pragma unroll
-        for (int tm = 0; tm < 8; ++tm) {
-          const wg_bf16x8 fa = *reinterpret_cast<const wg_bf16x8*>(ta + wg_swz(wm * 128 + tm * 16 + l16, kk * 4 + lhi));
-#pragma unroll
-          for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[tn], fa, acc[tm][tn], 0, 0, 0);
-        }
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[tn], fa_cur, acc[tm][tn], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        fa_cur = fa_next;
       }
-      if (s + 1 < nsteps) store(st ^ 1);
-      __syncthreads();
+      // vmcnt(8): this wave's DMAs of step s+1 have landed (s+2, s+3 may not); a bare
+      // barrier then makes step s+1 whole for every wave. (A __syncthreads would add a
+      // workgroup release, which waits for every DMA in flight.) The stage the next step
+      // overwrites was read by this step, whose reads the MFMAs above have consumed.
+      __builtin_amdgcn_s_waitcnt(0x0F78);
+      __builtin_amdgcn_s_barrier();
+    };
+    // whole rounds of four steps (a branch between the steps would make the compiler
+    // copy the accumulators at each exit): the steps past the segment add zeros
+    for (int s = 0; s < nsteps; s += 4) {
+      step(s, C0{}, C3{});
+      step(s + 1, C1{}, C0{});
+      step(s + 2, C2{}, C1{});
+      step(s + 3, C3{}, C2{});
     }
+    // the DMAs still in flight (up to three steps past the end) land before the ring is reused
+    wait_vm0();
+    __syncthreads();
 
     // C[e][n1][n2]: lane holds n1 = t1*256 + wm*128 + tm*16 + l16, n2 = t2*256 + wn*64 + tn*16 + 4*lhi + (0..3)
     uint8_t* cbase = a.C + ((int64_t)e * a.N1 + t1 * kWgTile + wm * 128 + l16) * a.N2 * 2 +
