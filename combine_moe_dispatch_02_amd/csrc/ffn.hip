@@ -26,6 +26,7 @@
 // mxfp4: the same instruction with e2m1 weights (format 4) and e4m3 activations,
 // its per-lane E8M0 operands carrying the 1x32 block scales of both sides.
 #include <algorithm>
+#include <cstdlib>
 #include <type_traits>
 
 #include "combine.h"
@@ -511,6 +512,8 @@ __device__ inline void combine_tail(const FfnArgs& a, int* s_item) {
 // s_waitcnt vmcnt(0), the other counters left alone (LDS-DMA loads have no
 // register result for the compiler to wait on)
 __device__ inline void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(n) (n < 64), the other counters left alone
+constexpr int vmcnt_enc(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
 __device__ inline uint32_t swz_a(int r, int c) {
   // 8 consecutive rows reading one chunk column hit 8 distinct 16-byte bank groups
@@ -526,14 +529,24 @@ __device__ inline uint32_t swz_a(int r, int c) {
 // chunks b and b+4 of the row's 128-byte step.
 // EPI (GEMM Y only): 0 stores y; 1 is the backward GEMM Y's epilogue -- the product
 // is dh, and with g, u from G it writes dG = [dh u silu'(g) | dh silu(g)] in place of G.
-template <int BM, int NW, bool FP8, bool GEMM_A, bool PACKED, bool MX = false, int EPI = 0>
+// RING (bf16, K steps a multiple of 4): the pool rows come by LDS-DMA into a ring of four
+// stages, three K steps ahead (registers hold none of them), instead of through registers
+// two steps ahead into two stages. The stages are separate LDS objects used with
+// constant indices (the loop runs four steps per round), so the compiler can tell a
+// step's reads from the DMA writes in flight and adds no wait of its own; each step ends
+// with a vmcnt wait that leaves the two newer steps' DMAs outstanding and a bare barrier.
+template <int BM, int NW, bool FP8, bool GEMM_A, bool PACKED, bool MX = false, int EPI = 0, bool RING = false>
 __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
   static_assert(EPI == 0 || (!GEMM_A && !FP8), "the SwiGLU-backward epilogue is a bf16 GEMM Y one");
   static_assert(!MX || (FP8 && PACKED), "mxfp4 runs on the tiled e4m3 path");
   using C = Big<BM, NW, FP8, GEMM_A>;
   constexpr int TN = C::kTN, TM = C::kTM, KS = C::kKS, HALF = C::kHalf;
   static_assert(!MX || (TM >= TN && HALF % 32 == 0), "mxfp4 step and h block layout");
-  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][C::kAStage];
+  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][RING ? 16 : C::kAStage];
+  __shared__ __attribute__((aligned(16))) uint8_t s_r0[RING ? C::kAStage : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t s_r1[RING ? C::kAStage : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t s_r2[RING ? C::kAStage : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t s_r3[RING ? C::kAStage : 16];
   __shared__ float s_as[2][FP8 && !MX ? BM : 1];
   __shared__ uint32_t s_ax[2][MX ? BM : 1];          // mxfp4: a row's 4 E8M0 bytes of a step
   __shared__ float s_rt[2][FP8 && PACKED && !MX ? BM : 1];  // fp8: a_s(previous step) / a_s(this step) per row
@@ -754,7 +767,35 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
 
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    if constexpr (MX) {
+    auto ring = [&](auto ST) -> uint8_t* {
+      constexpr int k = decltype(ST)::value;
+      if constexpr (k == 0) return s_r0;
+      else if constexpr (k == 1) return s_r1;
+      else if constexpr (k == 2) return s_r2;
+      else return s_r3;
+    };
+    // the pool rows of step ks into ring stage ST (the layout of dma_a)
+    constexpr int kDma = C::kAStage / 1024 / NW;   // DMA instructions per wave per step
+    auto dma_r = [&](auto ST, int ks) {
+      uint8_t* base = ring(ST);
+#pragma unroll
+      for (int i = 0; i < kDma; ++i) {
+        const int q = wn * kDma + i;
+        const uint32_t off = (uint32_t)(q * 8 + (lane >> 3)) * (uint32_t)a.lda +
+                             (uint32_t)((lane & 7) ^ (lane >> 3)) * 16u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ar, (__attribute__((address_space(3))) void*)(base + q * 1024), 16, off, (uint32_t)ks * 128u, 0, 0);
+      }
+    };
+    if constexpr (RING) {
+      using I2 = std::integral_constant<int, 2>;
+      dma_r(I0{}, 0);
+      dma_r(I1{}, 1);
+      dma_r(I2{}, 2);
+      load_b(I0{}, 0);
+      // the DMAs of steps 1 and 2 and the weight loads of step 0 may still be in flight
+      __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * kDma + 2 * TN));
+    } else if constexpr (MX) {
       dma_a(I0{}, 0);
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) load_bmx(I0{}, tn, 0);
@@ -777,7 +818,10 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
       load_a(I1{}, nk > 1 ? 1 : 0);
       store_a(I0{}, 0);
     }
-    __syncthreads();
+    if constexpr (RING)
+      __builtin_amdgcn_s_barrier();   // a __syncthreads would wait for every DMA in flight
+    else
+      __syncthreads();
 
     auto step = [&](auto BUF, int ks) {
       constexpr int bb = decltype(BUF)::value;
@@ -979,8 +1023,57 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     };
 
-    for (int ks = 0; ks < nk; ks += 2) {
-      if constexpr (MX) {
+    // ring step: stage ST (= ks % 4), weights in buffer ks % 2; sends step ks+3 into the
+    // stage step ks-1 read (every read of it is behind the last barrier)
+    auto step_ring = [&](auto ST, auto BUF, int ks) {
+      constexpr int st = decltype(ST)::value;
+      constexpr int bb = decltype(BUF)::value;
+      using NB = std::integral_constant<int, bb ^ 1>;
+      using SN = std::integral_constant<int, (st + 3) & 3>;
+      const int kn = ks + 1 < nk ? ks + 1 : ks;
+      const int kd = ks + 3 < nk ? ks + 3 : nk - 1;   // past the end: reload the last step (unread)
+      const uint8_t* sa = ring(ST);
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8_t fa_cur = *reinterpret_cast<const bf16x8_t*>(sa + swz_a(l16, lhi));
+#pragma unroll
+      for (int g = 0; g < 2 * TM; ++g) {
+        const int kk = g / TM, tm = g % TM;
+        bf16x8_t fa_next = fa_cur;
+        if (g + 1 < 2 * TM) {
+          const int kk1 = (g + 1) / TM, tm1 = (g + 1) % TM;
+          fa_next = *reinterpret_cast<const bf16x8_t*>(sa + swz_a(tm1 * 16 + l16, kk1 * 4 + lhi));
+        }
+        if (g == 0) dma_r(SN{}, kd);
+        if (g >= 1 && g <= TN) load_b1(NB{}, g - 1, 0, kn);
+        if (g >= TM && g < TM + TN) load_b1(NB{}, g - TM, 1, kn);
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_t, rb[bb][tn][kk]), fa_cur, acc[tm][tn], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        fa_cur = fa_next;
+      }
+      // in flight after step ks+1's DMAs (issued two steps ago), in order: weights of
+      // ks-1, DMAs of ks+2, weights of ks, DMAs of ks+3, weights of ks+1
+      __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * kDma + 3 * 2 * TN));
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    if constexpr (RING) {
+      using I2 = std::integral_constant<int, 2>;
+      using I3 = std::integral_constant<int, 3>;
+      for (int ks = 0; ks < nk; ks += 4) {
+        step_ring(I0{}, I0{}, ks);
+        step_ring(I1{}, I1{}, ks + 1);
+        step_ring(I2{}, I0{}, ks + 2);
+        step_ring(I3{}, I1{}, ks + 3);
+      }
+      wait_vm0();   // the reloads past the end land before the ring is refilled
+    }
+    for (int ks = 0; ks < (RING ? 0 : nk); ks += 2) {
+      if constexpr (RING) {
+      } else if constexpr (MX) {
         step_mx(std::integral_constant<int, 0>{}, ks);
         step_mx(std::integral_constant<int, 1>{}, ks + 1);
       } else if constexpr (FP8 && PACKED) {
@@ -1333,6 +1426,15 @@ int ffn_supported(int32_t H, int32_t I, int32_t dtype, int32_t tile, int32_t blo
   return MOE_ERR_INVALID;
 }
 
+// the bf16 ring variant of the big-tile kernel (RING); on unless MOE_FFN_RING=0
+static bool ffn_ring_enabled() {
+  static const bool on = [] {
+    const char* v = std::getenv("MOE_FFN_RING");
+    return !(v && v[0] == '0');
+  }();
+  return on;
+}
+
 #ifndef MOE_BIG_WAVES
 #define MOE_BIG_WAVES 8
 #endif
@@ -1346,7 +1448,10 @@ static void launch_one(const FfnArgs& a, int grid, hipStream_t s) {
 template <bool FP8, bool GEMM_A, bool PACKED>
 static int launch_big(int tile, const FfnArgs& a, int grid, hipStream_t s) {
   constexpr int NW = kBigWaves;
-  if (tile == 128) hipLaunchKernelGGL((ffn_big_kernel<128, NW, FP8, GEMM_A, PACKED>), dim3(grid), dim3(64 * NW), 0, s, a);
+  if (!FP8 && tile == 128 && a.ksteps % 4 == 0 && ffn_ring_enabled())
+    hipLaunchKernelGGL((ffn_big_kernel<128, NW, false, GEMM_A, PACKED, false, 0, true>), dim3(grid), dim3(64 * NW), 0,
+                       s, a);
+  else if (tile == 128) hipLaunchKernelGGL((ffn_big_kernel<128, NW, FP8, GEMM_A, PACKED>), dim3(grid), dim3(64 * NW), 0, s, a);
   else if (tile == 64) hipLaunchKernelGGL((ffn_big_kernel<64, NW, FP8, GEMM_A, PACKED>), dim3(grid), dim3(64 * NW), 0, s, a);
   else return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
@@ -1581,7 +1686,11 @@ int launch_ffn_dgrad(const moe_plan_t& p, int32_t pool_rows, const void* A, cons
   const int ntiles_cap = std::min(p.rows_cap, pool_rows) / tile;
   grid = (int)std::max<int64_t>(1, std::min<int64_t>(grid, (int64_t)ntiles_cap * a.n_units));
   constexpr int NW = kBigWaves;
-  if (tile == 128) {
+  const bool ring = a.ksteps % 4 == 0 && ffn_ring_enabled();
+  if (tile == 128 && ring) {
+    if (epi == 1) hipLaunchKernelGGL((ffn_big_kernel<128, NW, false, false, true, false, 1, true>), dim3(grid), dim3(64 * NW), 0, stream, a);
+    else hipLaunchKernelGGL((ffn_big_kernel<128, NW, false, false, true, false, 0, true>), dim3(grid), dim3(64 * NW), 0, stream, a);
+  } else if (tile == 128) {
     if (epi == 1) hipLaunchKernelGGL((ffn_big_kernel<128, NW, false, false, true, false, 1>), dim3(grid), dim3(64 * NW), 0, stream, a);
     else hipLaunchKernelGGL((ffn_big_kernel<128, NW, false, false, true, false, 0>), dim3(grid), dim3(64 * NW), 0, stream, a);
   } else if (tile == 64) {
