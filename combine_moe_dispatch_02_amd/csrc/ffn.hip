@@ -514,6 +514,8 @@ __device__ inline void combine_tail(const FfnArgs& a, int* s_item) {
 __device__ inline void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 // s_waitcnt vmcnt(n) (n < 64), the other counters left alone
 constexpr int vmcnt_enc(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+// s_waitcnt lgkmcnt(0), the other counters left alone
+constexpr int kLgkm0 = 0xC07F;
 
 __device__ inline uint32_t swz_a(int r, int c) {
   // 8 consecutive rows reading one chunk column hit 8 distinct 16-byte bank groups
@@ -542,11 +544,23 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
   using C = Big<BM, NW, FP8, GEMM_A>;
   constexpr int TN = C::kTN, TM = C::kTM, KS = C::kKS, HALF = C::kHalf;
   static_assert(!MX || (TM >= TN && HALF % 32 == 0), "mxfp4 step and h block layout");
-  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][RING ? 16 : C::kAStage];
-  __shared__ __attribute__((aligned(16))) uint8_t s_r0[RING ? C::kAStage : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t s_r1[RING ? C::kAStage : 16];
+  // A stages: s_a for the register-staged bf16 path; separate objects s_r0..s_r3 where
+  // A arrives by LDS-DMA (fp8 / mxfp4 use two of them, the bf16 ring four), so that the
+  // compiler can tell a step's LDS reads from the DMA writes in flight to another stage
+  // and does not wait for those
+  constexpr bool kDmaA = RING || FP8;
+  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][kDmaA ? 16 : C::kAStage];
+  __shared__ __attribute__((aligned(16))) uint8_t s_r0[kDmaA ? C::kAStage : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t s_r1[kDmaA ? C::kAStage : 16];
   __shared__ __attribute__((aligned(16))) uint8_t s_r2[RING ? C::kAStage : 16];
   __shared__ __attribute__((aligned(16))) uint8_t s_r3[RING ? C::kAStage : 16];
+  auto ring = [&](auto ST) -> uint8_t* {
+    constexpr int k = decltype(ST)::value;
+    if constexpr (k == 0) return s_r0;
+    else if constexpr (k == 1) return s_r1;
+    else if constexpr (k == 2) return s_r2;
+    else return s_r3;
+  };
   __shared__ float s_as[2][FP8 && !MX ? BM : 1];
   __shared__ uint32_t s_ax[2][MX ? BM : 1];          // mxfp4: a row's 4 E8M0 bytes of a step
   __shared__ float s_rt[2][FP8 && PACKED && !MX ? BM : 1];  // fp8: a_s(previous step) / a_s(this step) per row
@@ -708,14 +722,13 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
     // at slot c ^ (r & 7): lane i of a 1 KiB load fetches row i/8, chunk (i%8)^(i/8)),
     // and the rows' activation scales into ras[0] (stored to LDS before the barrier)
     auto dma_a = [&](auto STAGE, int ks) {
-      constexpr int st = decltype(STAGE)::value;
 #pragma unroll
       for (int i = 0; i < C::kAStage / 1024 / NW; ++i) {
         const int q = wn * (C::kAStage / 1024 / NW) + i;
         const uint32_t off = (uint32_t)(q * 8 + (lane >> 3)) * (uint32_t)a.lda +
                              (uint32_t)((lane & 7) ^ (lane >> 3)) * 16u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            ar, (__attribute__((address_space(3))) void*)(&s_a[st][0] + q * 1024), 16, off, (uint32_t)ks * 128u, 0, 0);
+            ar, (__attribute__((address_space(3))) void*)(ring(STAGE) + q * 1024), 16, off, (uint32_t)ks * 128u, 0, 0);
       }
       // branch-free (a branch here would split the step into blocks, and the compiler
       // then hoists every LDS read of the step above its MFMAs): threads past the
@@ -767,13 +780,6 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
 
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    auto ring = [&](auto ST) -> uint8_t* {
-      constexpr int k = decltype(ST)::value;
-      if constexpr (k == 0) return s_r0;
-      else if constexpr (k == 1) return s_r1;
-      else if constexpr (k == 2) return s_r2;
-      else return s_r3;
-    };
     // the pool rows of step ks into ring stage ST (the layout of dma_a)
     constexpr int kDma = C::kAStage / 1024 / NW;   // DMA instructions per wave per step
     auto dma_r = [&](auto ST, int ks) {
@@ -887,7 +893,7 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
       constexpr int bb = decltype(BUF)::value;
       using NB = std::integral_constant<int, bb ^ 1>;
       const int kn = ks + 1 < nk ? ks + 1 : ks;
-      const uint8_t* sa = &s_a[bb][0];
+      const uint8_t* sa = ring(BUF);
       __builtin_amdgcn_sched_barrier(0);
       // weight part of old/new, uniform over the wave (acc is zero at step 0)
       const float sbc0 = sbn[bb][0], sbc1 = sbn[bb][1];
@@ -932,11 +938,15 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
       }
       sbq[0] = sbc0;
       sbq[1] = sbc1;
-      // every load of this step is in: the next step's A rows (LDS-DMA, which no
-      // register dependency waits for), its weights and scales
-      wait_vm0();
+      // the next step's A rows (LDS-DMA, which no register dependency waits for) are in,
+      // issued in group 0; the weight loads of groups 1..TN-1 may stay in flight (their
+      // registers are waited for where the next step uses them). Then the rows' scales go
+      // to LDS and a bare barrier (a __syncthreads would add a workgroup release, which
+      // waits for every load in flight) after this wave's LDS writes are done.
+      __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * (TN - 1)));
       stage_scale(NB{});
-      __syncthreads();
+      __builtin_amdgcn_s_waitcnt(kLgkm0);
+      __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
     };
 
@@ -948,7 +958,7 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
       constexpr int bb = decltype(BUF)::value;
       using NB = std::integral_constant<int, bb ^ 1>;
       const int kn = ks + 1 < nk ? ks + 1 : ks;
-      const uint8_t* sa = &s_a[bb][0];
+      const uint8_t* sa = ring(BUF);
       const uint8_t* sx = reinterpret_cast<const uint8_t*>(&s_ax[bb][0]);
       __builtin_amdgcn_sched_barrier(0);
       auto rd_a = [&](int tm) {
@@ -980,9 +990,12 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
         fa_cur = fa_next;
         xs_cur = xs_next;
       }
-      wait_vm0();
+      // as in the fp8 step: the A rows (group 0) are in, the weight loads of groups
+      // 1..TN-1 may stay in flight
+      __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * (TN - 1)));
       stage_mx(NB{});
-      __syncthreads();
+      __builtin_amdgcn_s_waitcnt(kLgkm0);
+      __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
     };
 
