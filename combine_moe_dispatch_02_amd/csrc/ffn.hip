@@ -531,9 +531,10 @@ __device__ inline uint32_t swz_a(int r, int c) {
 // chunks b and b+4 of the row's 128-byte step.
 // EPI (GEMM Y only): 0 stores y; 1 is the backward GEMM Y's epilogue -- the product
 // is dh, and with g, u from G it writes dG = [dh u silu'(g) | dh silu(g)] in place of G.
-// RING (bf16, K steps a multiple of 4): the pool rows come by LDS-DMA into a ring of four
-// stages, three K steps ahead (registers hold none of them), instead of through registers
-// two steps ahead into two stages. The stages are separate LDS objects used with
+// RING (K steps a multiple of 4; used for bf16 and mxfp4): the pool rows come by LDS-DMA
+// into a ring of four stages, three K steps ahead (registers hold none of them), instead
+// of two stages (bf16: through registers, two steps ahead; fp8 / mxfp4: by LDS-DMA, one
+// step ahead). The activation scales of fp8 / mxfp4 stay one step ahead, in two stages. The stages are separate LDS objects used with
 // constant indices (the loop runs four steps per round), so the compiler can tell a
 // step's reads from the DMA writes in flight and adds no wait of its own; each step ends
 // with a vmcnt wait that leaves the two newer steps' DMAs outstanding and a bare barrier.
@@ -721,7 +722,7 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
     // fp8: the A rows of step ks into LDS stage ST by LDS-DMA (row r at r*128, chunk c
     // at slot c ^ (r & 7): lane i of a 1 KiB load fetches row i/8, chunk (i%8)^(i/8)),
     // and the rows' activation scales into ras[0] (stored to LDS before the barrier)
-    auto dma_a = [&](auto STAGE, int ks) {
+    auto dma_rows = [&](auto STAGE, int ks) {
 #pragma unroll
       for (int i = 0; i < C::kAStage / 1024 / NW; ++i) {
         const int q = wn * (C::kAStage / 1024 / NW) + i;
@@ -730,13 +731,20 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             ar, (__attribute__((address_space(3))) void*)(ring(STAGE) + q * 1024), 16, off, (uint32_t)ks * 128u, 0, 0);
       }
-      // branch-free (a branch here would split the step into blocks, and the compiler
-      // then hoists every LDS read of the step above its MFMAs): threads past the
-      // tile's rows read, and later store, the last row's scale again
+    };
+    // the rows' activation scales of step ks into ras[0] / rax (stored to LDS before the
+    // barrier). Branch-free (a branch here would split the step into blocks, and the
+    // compiler then hoists every LDS read of the step above its MFMAs): threads past the
+    // tile's rows read, and later store, the last row's scale again
+    auto load_ascale = [&](int ks) {
       if constexpr (MX)
         rax = *reinterpret_cast<const uint32_t*>(a.A_e8 + (int64_t)(m0 + min(tid, BM - 1)) * a.e8_lda + 4 * ks);
       else
         ras[0] = a.A_s[(int64_t)(m0 + min(tid, BM - 1)) * a.s_kblocks + ks];
+    };
+    auto dma_a = [&](auto STAGE, int ks) {
+      dma_rows(STAGE, ks);
+      load_ascale(ks);
     };
     // mxfp4: tile tn's fragment and scale byte of step ks into buffer BUF
     auto load_bmx = [&](auto BUF, int tn, int ks) {
@@ -793,7 +801,30 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
             ar, (__attribute__((address_space(3))) void*)(base + q * 1024), 16, off, (uint32_t)ks * 128u, 0, 0);
       }
     };
-    if constexpr (RING) {
+    if constexpr (RING && FP8) {
+      // the ring's first three steps, then this step's scales and weights; one full wait
+      using I2 = std::integral_constant<int, 2>;
+      dma_rows(I0{}, 0);
+      dma_rows(I1{}, nk > 1 ? 1 : 0);
+      dma_rows(I2{}, nk > 2 ? 2 : nk - 1);
+      load_ascale(0);
+      if constexpr (MX) {
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) load_bmx(I0{}, tn, 0);
+        wait_vm0();
+        stage_mx(I0{});
+      } else {
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          load_b8h(I0{}, tn, 0, 0);
+          load_b8h(I0{}, tn, 1, 0);
+        }
+        load_sb(I0{}, 0);
+        wait_vm0();
+        pa = ras[0];
+        stage_scale(I0{});
+      }
+    } else if constexpr (RING) {
       using I2 = std::integral_constant<int, 2>;
       dma_r(I0{}, 0);
       dma_r(I1{}, 1);
@@ -824,10 +855,14 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
       load_a(I1{}, nk > 1 ? 1 : 0);
       store_a(I0{}, 0);
     }
-    if constexpr (RING)
-      __builtin_amdgcn_s_barrier();   // a __syncthreads would wait for every DMA in flight
-    else
+    if constexpr (RING) {
+      // a __syncthreads would wait for every DMA in flight; the LDS writes above (fp8,
+      // mxfp4 scales) are waited for here
+      __builtin_amdgcn_s_waitcnt(kLgkm0);
+      __builtin_amdgcn_s_barrier();
+    } else {
       __syncthreads();
+    }
 
     auto step = [&](auto BUF, int ks) {
       constexpr int bb = decltype(BUF)::value;
@@ -889,11 +924,14 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
     // accumulates the block's code product in place. The next step's 8 weight loads
     // and 2 weight-scale loads go out over the first groups (all of them are needed
     // at the next step's first group); A for step ks+2 in group 0.
-    auto step_fp8 = [&](auto BUF, int ks) {
+    // ST: the A stage this step reads (= BUF with two stages, ks % 4 in the ring)
+    auto step_fp8 = [&](auto ST, auto BUF, int ks) {
       constexpr int bb = decltype(BUF)::value;
       using NB = std::integral_constant<int, bb ^ 1>;
+      using SN = std::integral_constant<int, (decltype(ST)::value + 3) & 3>;
       const int kn = ks + 1 < nk ? ks + 1 : ks;
-      const uint8_t* sa = ring(BUF);
+      const int kd = ks + 3 < nk ? ks + 3 : nk - 1;   // ring: past the end, reload the last step (unread)
+      const uint8_t* sa = ring(ST);
       __builtin_amdgcn_sched_barrier(0);
       // weight part of old/new, uniform over the wave (acc is zero at step 0)
       const float sbc0 = sbn[bb][0], sbc1 = sbn[bb][1];
@@ -917,7 +955,13 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
           rt_next = s_rt[bb][(tm + 1) * 16 + l16];
         }
         if (tm == 0) {
-          dma_a(NB{}, kn);
+          if constexpr (RING) {
+            load_ascale(kn);                        // first: the end-of-step wait counts from it
+            __builtin_amdgcn_sched_barrier(0);
+            dma_rows(SN{}, kd);
+          } else {
+            dma_a(NB{}, kn);
+          }
           load_sb(NB{}, kn);
         }
         if (tm < TN) {
@@ -943,7 +987,10 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
       // registers are waited for where the next step uses them). Then the rows' scales go
       // to LDS and a bare barrier (a __syncthreads would add a workgroup release, which
       // waits for every load in flight) after this wave's LDS writes are done.
-      __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * (TN - 1)));
+      // ring: this step's scale load is in (and with it step ks+1's rows, issued two
+      // steps earlier); after it came its rows' DMA of step ks+3 and the step's 2 + 2 TN
+      // weight and weight-scale loads, which may stay in flight
+      __builtin_amdgcn_s_waitcnt(vmcnt_enc(RING ? C::kAStage / 1024 / NW + 2 + 2 * TN : 2 * (TN - 1)));
       stage_scale(NB{});
       __builtin_amdgcn_s_waitcnt(kLgkm0);
       __builtin_amdgcn_s_barrier();
@@ -954,11 +1001,13 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
     // next step's weight fragments and scale bytes go out over the first TN groups,
     // its A rows (LDS-DMA) and A scales in group 0; fragments and the lane's A scale
     // byte are read from LDS one group ahead.
-    auto step_mx = [&](auto BUF, int ks) {
+    auto step_mx = [&](auto ST, auto BUF, int ks) {
       constexpr int bb = decltype(BUF)::value;
       using NB = std::integral_constant<int, bb ^ 1>;
+      using SN = std::integral_constant<int, (decltype(ST)::value + 3) & 3>;
       const int kn = ks + 1 < nk ? ks + 1 : ks;
-      const uint8_t* sa = ring(BUF);
+      const int kd = ks + 3 < nk ? ks + 3 : nk - 1;
+      const uint8_t* sa = ring(ST);
       const uint8_t* sx = reinterpret_cast<const uint8_t*>(&s_ax[bb][0]);
       __builtin_amdgcn_sched_barrier(0);
       auto rd_a = [&](int tm) {
@@ -977,7 +1026,15 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
           fa_next = rd_a(tm + 1);
           xs_next = sx[((tm + 1) * 16 + l16) * 4 + lhi];
         }
-        if (tm == 0) dma_a(NB{}, kn);
+        if (tm == 0) {
+          if constexpr (RING) {
+            load_ascale(kn);
+            __builtin_amdgcn_sched_barrier(0);
+            dma_rows(SN{}, kd);
+          } else {
+            dma_a(NB{}, kn);
+          }
+        }
         if (tm < TN) load_bmx(NB{}, tm, kn);
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
@@ -992,7 +1049,7 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
       }
       // as in the fp8 step: the A rows (group 0) are in, the weight loads of groups
       // 1..TN-1 may stay in flight
-      __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * (TN - 1)));
+      __builtin_amdgcn_s_waitcnt(vmcnt_enc(RING ? C::kAStage / 1024 / NW + 2 * TN : 2 * (TN - 1)));
       stage_mx(NB{});
       __builtin_amdgcn_s_waitcnt(kLgkm0);
       __builtin_amdgcn_s_barrier();
@@ -1073,7 +1130,24 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     };
 
-    if constexpr (RING) {
+    if constexpr (RING && FP8) {
+      using I2 = std::integral_constant<int, 2>;
+      using I3 = std::integral_constant<int, 3>;
+      for (int ks = 0; ks < nk; ks += 4) {
+        if constexpr (MX) {
+          step_mx(I0{}, I0{}, ks);
+          step_mx(I1{}, I1{}, ks + 1);
+          step_mx(I2{}, I0{}, ks + 2);
+          step_mx(I3{}, I1{}, ks + 3);
+        } else {
+          step_fp8(I0{}, I0{}, ks);
+          step_fp8(I1{}, I1{}, ks + 1);
+          step_fp8(I2{}, I0{}, ks + 2);
+          step_fp8(I3{}, I1{}, ks + 3);
+        }
+      }
+      wait_vm0();   // the reloads past the end land before the ring is refilled
+    } else if constexpr (RING) {
       using I2 = std::integral_constant<int, 2>;
       using I3 = std::integral_constant<int, 3>;
       for (int ks = 0; ks < nk; ks += 4) {
@@ -1087,11 +1161,11 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
     for (int ks = 0; ks < (RING ? 0 : nk); ks += 2) {
       if constexpr (RING) {
       } else if constexpr (MX) {
-        step_mx(std::integral_constant<int, 0>{}, ks);
-        step_mx(std::integral_constant<int, 1>{}, ks + 1);
+        step_mx(I0{}, I0{}, ks);
+        step_mx(I1{}, I1{}, ks + 1);
       } else if constexpr (FP8 && PACKED) {
-        step_fp8(std::integral_constant<int, 0>{}, ks);
-        step_fp8(std::integral_constant<int, 1>{}, ks + 1);
+        step_fp8(I0{}, I0{}, ks);
+        step_fp8(I1{}, I1{}, ks + 1);
       } else if constexpr (!FP8 && TM >= TN + 1) {
         step_bf16(std::integral_constant<int, 0>{}, ks);
         step_bf16(std::integral_constant<int, 1>{}, ks + 1);
@@ -1473,8 +1547,12 @@ static int launch_big(int tile, const FfnArgs& a, int grid, hipStream_t s) {
 template <bool GEMM_A>
 static int launch_mx(int tile, int bn, bool packed, const FfnArgs& a, int grid, hipStream_t s) {
   if (bn != 512 || !packed || tile != 128) return MOE_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL((ffn_big_kernel<128, kBigWaves, true, GEMM_A, true, true>), dim3(grid), dim3(64 * kBigWaves), 0,
-                     s, a);
+  if (a.ksteps % 4 == 0 && ffn_ring_enabled())
+    hipLaunchKernelGGL((ffn_big_kernel<128, kBigWaves, true, GEMM_A, true, true, 0, true>), dim3(grid),
+                       dim3(64 * kBigWaves), 0, s, a);
+  else
+    hipLaunchKernelGGL((ffn_big_kernel<128, kBigWaves, true, GEMM_A, true, true>), dim3(grid), dim3(64 * kBigWaves),
+                       0, s, a);
   return MOE_OK;
 }
 
@@ -1483,6 +1561,7 @@ static int launch_shape(int tile, int bn, bool packed, const FfnArgs& a, int gri
   if (bn == 512) {
     if constexpr (FP8) {
       if (!packed || tile != 128) return MOE_ERR_UNSUPPORTED;  // fp8 big tiles read tiled weights
+      // (the four-stage ring measured no faster for fp8, unlike bf16 and mxfp4: two stages)
       hipLaunchKernelGGL((ffn_big_kernel<128, kBigWaves, true, GEMM_A, true>), dim3(grid), dim3(64 * kBigWaves), 0, s, a);
       return MOE_OK;
     } else {
