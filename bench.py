@@ -269,6 +269,8 @@ def main():
     ap.add_argument("--block-n", type=int, default=0, help="tile config override: N block (0 = auto)")
     ap.add_argument("--gemm-wgs", type=int, default=0, help="tile config override: GEMM grid (0 = auto)")
     ap.add_argument("--unit-order", type=int, default=0, help="tile config override: unit walk (0 = auto)")
+    ap.add_argument("--a-stages", type=int, default=0,
+                    help="tile config override: pool-row pipeline depth of the big-tile GEMMs (0 = auto, 2, 4)")
     ap.add_argument("--cpu-sample", type=int, default=512, help="tokens of the oracle CPU baseline (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run three 1 GiB device-to-device copies (a known-size reference for "
@@ -318,8 +320,8 @@ def main():
         w1, w2, w1s, w2s = inp.w1.to(dev), inp.w2.to(dev), None, None
     torch.cuda.synchronize()
     tcfg = None
-    if args.block_n or args.gemm_wgs or args.unit_order:
-        tcfg = moe.TileConfig(args.block_n, args.gemm_wgs, 0, args.unit_order, 0)
+    if args.block_n or args.gemm_wgs or args.unit_order or args.a_stages:
+        tcfg = moe.TileConfig(args.block_n, args.gemm_wgs, 0, args.unit_order, 0, args.a_stages)
     layer = moe.StreamMoE(cfg.T, cfg.H, cfg.I, cfg.K, cfg.num_local_experts,
                           expert_begin=cfg.expert_begin, tile=cfg.tile, dtype=cfg.dtype, cfg=tcfg,
                           combine_on_completion=args.combine_on_completion)

@@ -60,6 +60,7 @@ class TileConfig(ctypes.Structure):
         ("spin_timeout_us", ctypes.c_uint32),
         ("unit_order", ctypes.c_int32),
         ("weight_layout", ctypes.c_int32),
+        ("a_stages", ctypes.c_int32),
     ]
 
 

@@ -149,6 +149,8 @@ static int expert_ffn(const moe_plan_t* plan, int32_t pool_rows, const void* poo
   f.workgroups = cfg ? cfg->gemm_workgroups : 0;
   f.unit_order = cfg ? cfg->unit_order : 0;
   f.weight_layout = layout;
+  f.a_stages = cfg ? cfg->a_stages : 0;
+  if (f.a_stages != 0 && f.a_stages != 2 && f.a_stages != 4) return MOE_ERR_INVALID;
   if (f.unit_order < 0 || f.unit_order > 9) return MOE_ERR_INVALID;
   const uint64_t us = (cfg && cfg->spin_timeout_us) ? cfg->spin_timeout_us : 2000000u;
   f.timeout_ticks = us * 100u;  // s_memrealtime counts at 100 MHz
@@ -211,19 +213,21 @@ MOE355_API int moe_expert_ffn_backward(const moe_plan_t* plan, int32_t pool_rows
   // 32-bit buffer offsets over the pool-sized operands
   if ((int64_t)pool_rows * std::max(2 * I, H) * 2 >= ((int64_t)1 << 32) - 16) return MOE_ERR_UNSUPPORTED;
   if (cfg && (cfg->gemm_workgroups < 0 || cfg->unit_order < 0 || cfg->unit_order > 9)) return MOE_ERR_INVALID;
+  if (cfg && cfg->a_stages != 0 && cfg->a_stages != 2 && cfg->a_stages != 4) return MOE_ERR_INVALID;
   const WsLayout L = ws_layout(plan->T, plan->K, plan->E_local, plan->tile, pool_rows, I, MOE_BF16);
   if (ws_bytes < L.total) return MOE_ERR_INVALID;
   char* w = static_cast<char*>(ws);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int32_t wgs = cfg ? cfg->gemm_workgroups : 0;
   const int32_t order = cfg ? cfg->unit_order : 0;
+  const int32_t stages = cfg ? cfg->a_stages : 0;
   // backward GEMM Y: dh = dy . W2 -> dG (over G), and dW2 = dy^T h
-  rc = launch_ffn_dgrad(*plan, pool_rows, dy_pool, w2t, I, H, nullptr, g_pool, I, 1, wgs, order, L, w, s);
+  rc = launch_ffn_dgrad(*plan, pool_rows, dy_pool, w2t, I, H, nullptr, g_pool, I, 1, wgs, order, stages, L, w, s);
   if (rc != MOE_OK) return rc;
   rc = launch_wgrad(*plan, pool_rows, dy_pool, H, w + L.h, I, dw2, wgs, s);
   if (rc != MOE_OK) return rc;
   // backward GEMM A: dx_pool = dG . W1, and dW1 = dG^T X
-  rc = launch_ffn_dgrad(*plan, pool_rows, g_pool, w1t, H, 2 * I, dx_pool, nullptr, I, 0, wgs, order, L, w, s);
+  rc = launch_ffn_dgrad(*plan, pool_rows, g_pool, w1t, H, 2 * I, dx_pool, nullptr, I, 0, wgs, order, stages, L, w, s);
   if (rc != MOE_OK) return rc;
   return launch_wgrad(*plan, pool_rows, g_pool, 2 * I, pool, H, dw1, wgs, s);
 }

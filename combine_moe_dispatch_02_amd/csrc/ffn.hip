@@ -26,7 +26,6 @@
 // mxfp4: the same instruction with e2m1 weights (format 4) and e4m3 activations,
 // its per-lane E8M0 operands carrying the 1x32 block scales of both sides.
 #include <algorithm>
-#include <cstdlib>
 #include <type_traits>
 
 #include "combine.h"
@@ -89,6 +88,7 @@ struct FfnArgs {
   // the backward GEMM Y's SwiGLU-backward epilogue reads G there and writes dG over it
   uint8_t* g_save;
   int64_t g_ld;              // bytes per row of g_save (2I * 2)
+  int32_t a_stages;          // 2: two A stages; else the four-stage ring where the kernel has it
 };
 
 __device__ inline uint32_t swz(int row, int chunk) { return (uint32_t)(row * 128 + ((chunk ^ (row & 7)) << 4)); }
@@ -1513,15 +1513,6 @@ int ffn_supported(int32_t H, int32_t I, int32_t dtype, int32_t tile, int32_t blo
   return MOE_ERR_INVALID;
 }
 
-// the bf16 ring variant of the big-tile kernel (RING); on unless MOE_FFN_RING=0
-static bool ffn_ring_enabled() {
-  static const bool on = [] {
-    const char* v = std::getenv("MOE_FFN_RING");
-    return !(v && v[0] == '0');
-  }();
-  return on;
-}
-
 #ifndef MOE_BIG_WAVES
 #define MOE_BIG_WAVES 8
 #endif
@@ -1535,7 +1526,7 @@ static void launch_one(const FfnArgs& a, int grid, hipStream_t s) {
 template <bool FP8, bool GEMM_A, bool PACKED>
 static int launch_big(int tile, const FfnArgs& a, int grid, hipStream_t s) {
   constexpr int NW = kBigWaves;
-  if (!FP8 && tile == 128 && a.ksteps % 4 == 0 && ffn_ring_enabled())
+  if (!FP8 && tile == 128 && a.ksteps % 4 == 0 && a.a_stages != 2)
     hipLaunchKernelGGL((ffn_big_kernel<128, NW, false, GEMM_A, PACKED, false, 0, true>), dim3(grid), dim3(64 * NW), 0,
                        s, a);
   else if (tile == 128) hipLaunchKernelGGL((ffn_big_kernel<128, NW, FP8, GEMM_A, PACKED>), dim3(grid), dim3(64 * NW), 0, s, a);
@@ -1547,7 +1538,7 @@ static int launch_big(int tile, const FfnArgs& a, int grid, hipStream_t s) {
 template <bool GEMM_A>
 static int launch_mx(int tile, int bn, bool packed, const FfnArgs& a, int grid, hipStream_t s) {
   if (bn != 512 || !packed || tile != 128) return MOE_ERR_UNSUPPORTED;
-  if (a.ksteps % 4 == 0 && ffn_ring_enabled())
+  if (a.ksteps % 4 == 0 && a.a_stages != 2)
     hipLaunchKernelGGL((ffn_big_kernel<128, kBigWaves, true, GEMM_A, true, true, 0, true>), dim3(grid),
                        dim3(64 * kBigWaves), 0, s, a);
   else
@@ -1643,6 +1634,7 @@ int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream
   a.epoch = f.epoch;
   a.err = reinterpret_cast<uint32_t*>(ws + L.err);
   a.timeout = f.timeout_ticks;
+  a.a_stages = f.a_stages;
   if (f.g_pool != nullptr) {
     a.g_save = static_cast<uint8_t*>(f.g_pool);
     a.g_ld = (int64_t)4 * I;
@@ -1747,7 +1739,7 @@ int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream
 // [H][2I], N = H, out = dx_pool.
 int launch_ffn_dgrad(const moe_plan_t& p, int32_t pool_rows, const void* A, const void* Bt, int32_t N, int32_t K,
                      void* out, void* g_pool, int32_t I, int epi, int32_t workgroups, int32_t unit_order,
-                     const WsLayout& L, char* ws, hipStream_t stream) {
+                     int32_t a_stages, const WsLayout& L, char* ws, hipStream_t stream) {
   const int tile = p.tile;
   FfnArgs a{};
   a.tile_shift = __builtin_ctz((unsigned)tile);
@@ -1778,7 +1770,7 @@ int launch_ffn_dgrad(const moe_plan_t& p, int32_t pool_rows, const void* A, cons
   const int ntiles_cap = std::min(p.rows_cap, pool_rows) / tile;
   grid = (int)std::max<int64_t>(1, std::min<int64_t>(grid, (int64_t)ntiles_cap * a.n_units));
   constexpr int NW = kBigWaves;
-  const bool ring = a.ksteps % 4 == 0 && ffn_ring_enabled();
+  const bool ring = a.ksteps % 4 == 0 && a_stages != 2;
   if (tile == 128 && ring) {
     if (epi == 1) hipLaunchKernelGGL((ffn_big_kernel<128, NW, false, false, true, false, 1, true>), dim3(grid), dim3(64 * NW), 0, stream, a);
     else hipLaunchKernelGGL((ffn_big_kernel<128, NW, false, false, true, false, 0, true>), dim3(grid), dim3(64 * NW), 0, stream, a);

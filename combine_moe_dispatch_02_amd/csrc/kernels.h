@@ -30,6 +30,7 @@ struct FfnLaunch {
   int32_t workgroups;
   int32_t unit_order;
   int32_t weight_layout;
+  int32_t a_stages;         // moe_tile_config.a_stages
   uint64_t timeout_ticks;   // s_memrealtime ticks (100 MHz)
   const float* topk_w;      // combine on completion: [T][K] weights (null = FFN only)
   void* comb_out;           // combine on completion: out [T][H] bf16 (null = FFN only)
@@ -51,7 +52,7 @@ int launch_pack_weights(const void* w, int32_t E, int32_t rows, int32_t K, int32
 
 int launch_ffn_dgrad(const moe_plan_t& p, int32_t pool_rows, const void* A, const void* Bt, int32_t N, int32_t K,
                      void* out, void* g_pool, int32_t I, int epi, int32_t workgroups, int32_t unit_order,
-                     const WsLayout& L, char* ws, hipStream_t stream);
+                     int32_t a_stages, const WsLayout& L, char* ws, hipStream_t stream);
 
 // backward.hip
 int launch_combine_backward(const void* dout, const float* topk_weights, const void* y_pool, int32_t pool_rows,

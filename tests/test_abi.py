@@ -155,6 +155,8 @@ def test_ffn_validation(lib):
     assert call(cfg=ctypes.byref(cfg)) == 1        # unit walks are 0..9
     cfg = _abi.TileConfig(0, -1, 0, 0, 0)
     assert call(cfg=ctypes.byref(cfg)) == 1        # negative grid
+    cfg = _abi.TileConfig(0, 0, 0, 0, 0, 3)
+    assert call(cfg=ctypes.byref(cfg)) == 1        # A pipeline depth is 0, 2 or 4
     mx = (v[5], v[6], v[7])
     assert call(dtype=2) == 1                      # mxfp4 without scales
     assert call(dtype=2, scales=mx) == 2           # mxfp4 runs on tiled weights only

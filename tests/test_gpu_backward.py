@@ -42,10 +42,10 @@ def test_pack_transposed_exact(shape):
     assert np.array_equal(got.cpu().view(torch.int16).numpy(), expected_t(w.numpy()))
 
 
-def _train_run(cfg, seed=None):
+def _train_run(cfg, seed=None, tile_cfg=None):
     inp = make_inputs(cfg) if seed is None else make_inputs(cfg, seed)
     d = dev_inputs(inp)
-    layer = make_layer(cfg, train=True)
+    layer = make_layer(cfg, train=True, cfg=tile_cfg)
     w1, w2, _, _ = layer.prepare_weights(d["w1"], d["w2"])
     w1t, w2t = layer.prepare_backward_weights(d["w1"], d["w2"])
     out = layer.forward(d["x"], d["idx"], d["w"], w1, w2).clone()
@@ -93,6 +93,17 @@ def test_backward_full_compare(cfg):
     none_local = ~((inp.topk_idx.numpy() >= cfg.expert_begin)
                    & (inp.topk_idx.numpy() < cfg.expert_begin + cfg.num_local_experts)).any(axis=1)
     assert (_bf(dx)[none_local] == 0).all() and (dw.cpu().numpy()[none_local] == 0).all()
+
+
+def test_backward_a_pipelines_agree():
+    # the data-gradient GEMMs give the same bits with the four-stage ring and with two stages
+    cfg = CASES[2]
+    say("backward A pipeline depth", cfg.name)
+    ring = _train_run(cfg, tile_cfg=moe.TileConfig(0, 0, 0, 0, 0, 4))
+    two = _train_run(cfg, tile_cfg=moe.TileConfig(0, 0, 0, 0, 0, 2))
+    for i in (6, 7, 8, 9):                        # dx, dw, dW1, dW2
+        assert torch.equal(ring[i].view(torch.int32 if ring[i].dtype == torch.float32 else torch.int16),
+                           two[i].view(torch.int32 if two[i].dtype == torch.float32 else torch.int16)), i
 
 
 def test_backward_full_size_skew_sampled():

@@ -140,3 +140,17 @@ def test_layer_unit_walks_agree(order):
     import combine_moe_dispatch_02_amd as moe
     got = run_layer(make_layer(cfg, cfg=moe.TileConfig(0, 0, 0, order, 0)), d)
     assert torch.equal(ref.view(torch.int16), got.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["big_both", "mx_big"])
+def test_layer_a_pipelines_agree(name):
+    # the four-stage pool-row ring and the two-stage pipeline feed the MFMAs the same
+    # operands in the same order: bitwise equal outputs
+    import combine_moe_dispatch_02_amd as moe
+    cfg = next(c for c in FULL_COMPARE if c.name == name)
+    inp = make_inputs(cfg)
+    d = dev_inputs(inp)
+    say("A pipeline depth", name)
+    ring = run_layer(make_layer(cfg, cfg=moe.TileConfig(0, 0, 0, 0, 0, 4)), d).clone()
+    two = run_layer(make_layer(cfg, cfg=moe.TileConfig(0, 0, 0, 0, 0, 2)), d)
+    assert torch.equal(ring.view(torch.int16), two.view(torch.int16))
