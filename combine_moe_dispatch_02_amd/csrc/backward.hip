@@ -327,9 +327,14 @@ __global__ __launch_bounds__(512, 1) void wgrad_kernel(WgradArgs a) {
     wait_vm0();
     __syncthreads();
 
-    // C[e][n1][n2]: lane holds n1 = t1*256 + wm*128 + tm*16 + l16, n2 = t2*256 + wn*64 + tn*16 + 4*lhi + (0..3)
-    uint8_t* cbase = a.C + ((int64_t)e * a.N1 + t1 * kWgTile + wm * 128 + l16) * a.N2 * 2 +
-                     (int64_t)(t2 * kWgTile + wn * 64 + 4 * lhi) * 2;
+    // Output through the idle ring: stored straight from the accumulators, a lane's 8-byte
+    // pieces of 16 rows would make every store instruction touch 16 rows. Each wave instead
+    // writes its 128 x 64 bf16 block into its own 16 KiB of the ring (128-byte rows, 16-byte
+    // chunks rotated by row & 7), reads it back row-contiguous (a wave's LDS accesses complete
+    // in order) and stores 8 whole 128-byte row segments per instruction.
+    // Accumulator (tm, tn) of a lane: block row tm*16 + l16, block columns tn*16 + 4*lhi + (0..3).
+    uint8_t* sw = wave < 2 ? &s_t0[wave & 1][0] : wave < 4 ? &s_t1[wave & 1][0]
+                : wave < 6 ? &s_t2[wave & 1][0] : &s_t3[wave & 1][0];
 #pragma unroll
     for (int tm = 0; tm < 8; ++tm)
 #pragma unroll
@@ -337,8 +342,27 @@ __global__ __launch_bounds__(512, 1) void wgrad_kernel(WgradArgs a) {
         u32x2 o;
         o.x = pack_bf16x2(acc[tm][tn][0], acc[tm][tn][1]);
         o.y = pack_bf16x2(acc[tm][tn][2], acc[tm][tn][3]);
-        *reinterpret_cast<u32x2*>(cbase + (int64_t)tm * 16 * a.N2 * 2 + tn * 32) = o;
+        const int row = tm * 16 + l16;
+        const int chunk = tn * 2 + (lhi >> 1);
+        *reinterpret_cast<u32x2*>(sw + row * 128 + ((chunk ^ (row & 7)) << 4) + (lhi & 1) * 8) = o;
       }
+    // C[e][n1][n2]: block row r is n1 = t1*256 + wm*128 + r, block column c is n2 = t2*256 + wn*64 + c
+    uint8_t* cbase = a.C + ((int64_t)e * a.N1 + t1 * kWgTile + wm * 128) * a.N2 * 2 +
+                     (int64_t)(t2 * kWgTile + wn * 64) * 2;
+    const int oc = lane & 7;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = i * 8 + (lane >> 3);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(sw + row * 128 + ((oc ^ (row & 7)) << 4));
+      *reinterpret_cast<u32x4*>(cbase + (int64_t)row * a.N2 * 2 + oc * 16) = v;
+    }
+    // every wave has read its block back (the stores consumed the reads) before the next
+    // unit's DMAs refill the ring; a bare barrier, since a __syncthreads would also wait
+    // for the stores to complete
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
