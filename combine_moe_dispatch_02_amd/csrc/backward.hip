@@ -291,13 +291,17 @@ __global__ __launch_bounds__(512, 1) void wgrad_kernel(WgradArgs a) {
       int fr = frow, fbt = fbyte;
       asm volatile("" : "+v"(fr), "+v"(fbt));
       __builtin_amdgcn_sched_barrier(0);
-      dma(s + 3, SN);
       const uint8_t* ta = &stage(ST)[0][0];
       const uint8_t* tb = &stage(ST)[1][0];
       wg_bf16x8 fb[4];
 #pragma unroll
       for (int tn = 0; tn < 4; ++tn) fb[tn] = frag(tb, wn * 64 + tn * 16, fr, fbt);
       wg_bf16x8 fa_cur = frag(ta, wm * 128, fr, fbt);
+      // the step's first fragment reads go out before its DMAs, whose issue then overlaps
+      // their latency (about 3% faster than the other way round)
+      __builtin_amdgcn_sched_barrier(0);
+      dma(s + 3, SN);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int tm = 0; tm < 8; ++tm) {
         wg_bf16x8 fa_next = fa_cur;
@@ -349,10 +353,13 @@ __global__ __launch_bounds__(512, 1) void wgrad_kernel(WgradArgs a) {
     // C[e][n1][n2]: block row r is n1 = t1*256 + wm*128 + r, block column c is n2 = t2*256 + wn*64 + c
     uint8_t* cbase = a.C + ((int64_t)e * a.N1 + t1 * kWgTile + wm * 128) * a.N2 * 2 +
                      (int64_t)(t2 * kWgTile + wn * 64) * 2;
-    const int oc = lane & 7;
+    // through an empty asm, so that the 16 row addresses are formed here rather than
+    // hoisted above the K loop, where they would hold 32 registers
+    int oc = lane & 7, orow = lane >> 3;
+    asm volatile("" : "+v"(oc), "+v"(orow));
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int row = i * 8 + (lane >> 3);
+      const int row = i * 8 + orow;
       const u32x4 v = *reinterpret_cast<const u32x4*>(sw + row * 128 + ((oc ^ (row & 7)) << 4));
       *reinterpret_cast<u32x4*>(cbase + (int64_t)row * a.N2 * 2 + oc * 16) = v;
     }
