@@ -1214,19 +1214,38 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
       };
       if constexpr (!FP8) {
         if (a.g_save != nullptr) {
-          // training: keep G (gate and up before the activation) for the backward pass
+          // training: keep G (gate and up before the activation) for the backward pass.
+          // It leaves through the same stage as h, gate columns then up columns, as whole
+          // 512-byte rows of the unit's 256 columns of each. Bare barriers: the stage is
+          // whole once every wave's LDS writes are done, and free again once every wave's
+          // reads are (a __syncthreads would also wait for the G stores to complete).
 #pragma unroll
-          for (int tm = 0; tm < TM; ++tm) {
-            uint8_t* grow = a.g_save + (int64_t)(m0 + tm * 16 + l16) * a.g_ld;
+          for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
-            for (int tn = 0; tn < TN; ++tn) {
-              const int half = tn < TN / 2 ? 0 : a.up_row0;
-              const int col = half + j * 256 + wn * HALF + (tn % (TN / 2)) * 16 + 4 * lhi;
-              u32x2 v;
-              v.x = pack_bf16x2(acc[tm][tn][0], acc[tm][tn][1]);
-              v.y = pack_bf16x2(acc[tm][tn][2], acc[tm][tn][3]);
-              *reinterpret_cast<u32x2*>(grow + (int64_t)col * 2) = v;
+            for (int tm = 0; tm < TM; ++tm) {
+              const int r = tm * 16 + l16;
+#pragma unroll
+              for (int tn = 0; tn < TN / 2; ++tn) {
+                u32x2 v;
+                v.x = pack_bf16x2(acc[tm][tn + hf * (TN / 2)][0], acc[tm][tn + hf * (TN / 2)][1]);
+                v.y = pack_bf16x2(acc[tm][tn + hf * (TN / 2)][2], acc[tm][tn + hf * (TN / 2)][3]);
+                *reinterpret_cast<u32x2*>(hst(r, hb0 + tn * 32)) = v;
+              }
             }
+            __builtin_amdgcn_s_waitcnt(kLgkm0);
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            uint8_t* gcol = a.g_save + (int64_t)(hf * a.up_row0 + j * 256) * 2;
+#pragma unroll
+            for (int q = 0; q < BM * 512 / 1024 / NW; ++q) {
+              const int r = (wn * (BM * 512 / 1024 / NW) + q) * 2 + lane / 32;
+              const int sl = lane % 32;
+              const u32x4 v = *reinterpret_cast<const u32x4*>(&s_hstage[r * 512 + sl * 16]);
+              *reinterpret_cast<u32x4*>(gcol + (int64_t)(m0 + r) * a.g_ld + ((sl ^ (r & 7)) << 4)) = v;
+            }
+            __builtin_amdgcn_s_waitcnt(kLgkm0);
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
 #pragma unroll
@@ -1317,46 +1336,78 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
       // backward GEMM Y: acc = dh for row tm*16+l16, h columns c..c+3 of tile tn with
       // c = j*512 + wn*64 + tn*16 + 4*lhi. g and u come from G (columns c and I + c), the
       // results replace them: dg = dh u silu'(g), du = dh silu(g), s = 1 / (1 + e^-g),
-      // silu'(g) = s (1 + g (1 - s)). The next row tile's G is loaded one ahead.
-      const int I = a.up_row0;
-      auto grow = [&](int tm) { return a.g_save + (int64_t)(m0 + tm * 16 + l16) * a.g_ld; };
-      auto col = [&](int tn) { return (int64_t)(j * 512 + wn * C::kWCols + tn * 16 + 4 * lhi) * 2; };
-      u32x2 gv[2][TN], uv[2][TN];
+      // silu'(g) = s (1 + g (1 - s)). G moves as whole 128-byte row segments (the wave's
+      // 64 columns) through the wave's own LDS region, 32 rows at a time: row-contiguous
+      // loads -> LDS -> fragment order -> results in place -> LDS -> row-contiguous stores.
+      // The next 32 rows' loads are issued before this group's LDS work. A wave's LDS
+      // accesses complete in order, and each staged value is read and rewritten by the
+      // lane that owns it: no barrier.
+      constexpr int SP = 32;                           // rows per group
+      const int I2 = a.up_row0 * 2;                    // bytes from g to u in a G row
+      uint8_t* st = &s_ystage[wn * 8192];              // g rows at 0, u rows at 4096
+      const int colb = (j * 512 + wn * C::kWCols) * 2;
+      const int lr = lane >> 3, sl = lane & 7;         // row-contiguous: row q*8 + lr, slot sl
+      auto gsrc = [&](int sp, int q) {
+        const int r = q * 8 + lr;
+        return a.g_save + (int64_t)(m0 + sp * SP + r) * a.g_ld + colb + ((sl ^ (r & 7)) << 4);
+      };
+      auto sfrag = [&](int r, int b) { return st + r * 128 + ((((b >> 4) ^ (r & 7))) << 4) + (b & 15); };
+      u32x4 gl[2][SP / 8], ul[2][SP / 8];
 #pragma unroll
-      for (int tn = 0; tn < TN; ++tn) {
-        gv[0][tn] = *reinterpret_cast<const u32x2*>(grow(0) + col(tn));
-        uv[0][tn] = *reinterpret_cast<const u32x2*>(grow(0) + (int64_t)I * 2 + col(tn));
+      for (int q = 0; q < SP / 8; ++q) {
+        gl[0][q] = *reinterpret_cast<const u32x4*>(gsrc(0, q));
+        ul[0][q] = *reinterpret_cast<const u32x4*>(gsrc(0, q) + I2);
       }
 #pragma unroll
-      for (int tm = 0; tm < TM; ++tm) {
-        const int cb = tm & 1;
-        if (tm + 1 < TM) {
+      for (int sp = 0; sp < BM / SP; ++sp) {
+        const int cb = sp & 1;
+        if (sp + 1 < BM / SP) {
 #pragma unroll
-          for (int tn = 0; tn < TN; ++tn) {
-            gv[cb ^ 1][tn] = *reinterpret_cast<const u32x2*>(grow(tm + 1) + col(tn));
-            uv[cb ^ 1][tn] = *reinterpret_cast<const u32x2*>(grow(tm + 1) + (int64_t)I * 2 + col(tn));
+          for (int q = 0; q < SP / 8; ++q) {
+            gl[cb ^ 1][q] = *reinterpret_cast<const u32x4*>(gsrc(sp + 1, q));
+            ul[cb ^ 1][q] = *reinterpret_cast<const u32x4*>(gsrc(sp + 1, q) + I2);
           }
         }
-        uint8_t* gr = grow(tm);
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-          const float g[4] = {bf16_lo(gv[cb][tn].x), bf16_hi(gv[cb][tn].x), bf16_lo(gv[cb][tn].y), bf16_hi(gv[cb][tn].y)};
-          const float u[4] = {bf16_lo(uv[cb][tn].x), bf16_hi(uv[cb][tn].x), bf16_lo(uv[cb][tn].y), bf16_hi(uv[cb][tn].y)};
-          float dg[4], du[4];
+        for (int q = 0; q < SP / 8; ++q) {
+          const int r = q * 8 + lr;
+          *reinterpret_cast<u32x4*>(st + r * 128 + sl * 16) = gl[cb][q];
+          *reinterpret_cast<u32x4*>(st + 4096 + r * 128 + sl * 16) = ul[cb][q];
+        }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g[i]));
-            const float dh = acc[tm][tn][i];
-            dg[i] = dh * u[i] * (sg * (1.0f + g[i] * (1.0f - sg)));
-            du[i] = dh * (g[i] * sg);
+        for (int t = 0; t < SP / 16; ++t) {
+          const int tm = sp * (SP / 16) + t;
+          const int r = t * 16 + l16;
+#pragma unroll
+          for (int tn = 0; tn < TN; ++tn) {
+            uint8_t* pg = sfrag(r, tn * 32 + 8 * lhi);
+            const u32x2 gv = *reinterpret_cast<const u32x2*>(pg);
+            const u32x2 uv = *reinterpret_cast<const u32x2*>(pg + 4096);
+            const float g[4] = {bf16_lo(gv.x), bf16_hi(gv.x), bf16_lo(gv.y), bf16_hi(gv.y)};
+            const float u[4] = {bf16_lo(uv.x), bf16_hi(uv.x), bf16_lo(uv.y), bf16_hi(uv.y)};
+            float dg[4], du[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g[i]));
+              const float dh = acc[tm][tn][i];
+              dg[i] = dh * u[i] * (sg * (1.0f + g[i] * (1.0f - sg)));
+              du[i] = dh * (g[i] * sg);
+            }
+            u32x2 o;
+            o.x = pack_bf16x2(dg[0], dg[1]);
+            o.y = pack_bf16x2(dg[2], dg[3]);
+            *reinterpret_cast<u32x2*>(pg) = o;
+            o.x = pack_bf16x2(du[0], du[1]);
+            o.y = pack_bf16x2(du[2], du[3]);
+            *reinterpret_cast<u32x2*>(pg + 4096) = o;
           }
-          u32x2 o;
-          o.x = pack_bf16x2(dg[0], dg[1]);
-          o.y = pack_bf16x2(dg[2], dg[3]);
-          *reinterpret_cast<u32x2*>(gr + col(tn)) = o;
-          o.x = pack_bf16x2(du[0], du[1]);
-          o.y = pack_bf16x2(du[2], du[3]);
-          *reinterpret_cast<u32x2*>(gr + (int64_t)I * 2 + col(tn)) = o;
+        }
+#pragma unroll
+        for (int q = 0; q < SP / 8; ++q) {
+          const int r = q * 8 + lr;
+          uint8_t* dst = const_cast<uint8_t*>(gsrc(sp, q));
+          *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(st + r * 128 + sl * 16);
+          *reinterpret_cast<u32x4*>(dst + I2) = *reinterpret_cast<const u32x4*>(st + 4096 + r * 128 + sl * 16);
         }
       }
     } else {
