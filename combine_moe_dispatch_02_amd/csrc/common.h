@@ -14,8 +14,11 @@ constexpr int kWave = 64;
 // workspace layout (shared by every entry point; offsets depend only on shape)
 // --------------------------------------------------------------------------
 constexpr int kPlanWaves = 4;            // waves per plan block
-constexpr int kPairsPerWave = 1024;      // pairs one plan wave ranks
-constexpr int kPairsPerBlock = kPlanWaves * kPairsPerWave;
+constexpr int kPairsPerWave = 1024;      // pairs one plan wave ranks (at most)
+// a batch that one plan block covers is split over all of its waves
+inline int32_t plan_pairs_per_wave(int64_t pairs) {
+  return pairs <= (int64_t)kPlanWaves * kPairsPerWave ? kPairsPerWave / 4 : kPairsPerWave;
+}
 
 struct WsLayout {
   size_t err = 0;        // uint32: first device error code (0 = none)
@@ -29,6 +32,7 @@ struct WsLayout {
   size_t plan_end = 0;   // end of what plan/dispatch need
   size_t total = 0;
   int32_t ncols = 0;
+  int32_t ppw = 0;       // pairs per plan column
   int32_t ntiles_cap = 0;
 };
 
@@ -43,7 +47,8 @@ inline WsLayout ws_layout(int32_t T, int32_t K, int32_t E, int32_t tile, int64_t
   WsLayout L;
   const int64_t pairs = (int64_t)T * K;
   const int64_t cap = pool_rows_bound(T, K, E, tile);
-  L.ncols = (int32_t)((pairs + kPairsPerWave - 1) / kPairsPerWave);
+  L.ppw = plan_pairs_per_wave(pairs);
+  L.ncols = (int32_t)((pairs + L.ppw - 1) / L.ppw);
   L.ntiles_cap = (int32_t)(cap / tile);
   L.fill = align_up(L.hist + (size_t)L.ncols * E * 4, 256);
   L.ydone = align_up(L.fill + (size_t)L.ntiles_cap * 4, 256);

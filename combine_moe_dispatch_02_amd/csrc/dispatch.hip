@@ -235,10 +235,13 @@ int launch_dispatch(const void* x, int32_t H, int32_t dtype, const moe_plan_t& p
   a.err = reinterpret_cast<uint32_t*>(ws + L.err);
   const int nch = H / 8;
   const int cpl = nch <= 64 ? 1 : nch <= 128 ? 2 : nch <= 256 ? 4 : 8;
-  a.tokens_per_wave = 64 / p.K;
+  const int cus = std::max(1, device_cu_count());
+  // tokens per wave: up to 64/K (one pos load per wave and token run), fewer when that
+  // leaves under two waves per CU -- a wave walks its tokens one after another, so a
+  // small batch wants one or two tokens per wave
+  a.tokens_per_wave = std::max(1, std::min(64 / p.K, p.T / (2 * cus)));
   const int waves = (p.T + a.tokens_per_wave - 1) / a.tokens_per_wave;
   // waves per block: the largest power of two up to 16 that leaves a block per CU
-  const int cus = std::max(1, device_cu_count());
   int wpb = 1;
   while (wpb < 16 && waves / (2 * wpb) >= cus) wpb *= 2;
   if (dtype == MOE_FP8_E4M3_G128)

@@ -7,7 +7,8 @@
 // ids outside [expert_begin, expert_begin + E_local) are not local.
 //
 // Scheme (no global atomics on counts, so every result is deterministic):
-//   column c = one wave's run of kPairsPerWave consecutive pairs.
+//   column c = one wave's run of ppw consecutive pairs (1024; 256 when one block
+//           covers the batch, so that its four waves share it).
 //   pass 1  each wave counts its column per expert: per 64 pairs, lanes with the
 //           same expert are matched with one ballot per key bit, the lowest lane
 //           of each group adds the group size to the wave's LDS counter row.
@@ -38,6 +39,7 @@ struct PlanArgs {
   int32_t ntiles_cap;     // entries of tile_expert / tile_ready (rows_cap / tile)
   int32_t nfill;          // entries of the workspace's fill counters
   int32_t ncols;
+  int32_t ppw;            // pairs per column
   int32_t* counts;
   int32_t* offsets;
   int32_t* pos;
@@ -55,12 +57,24 @@ struct PlanArgs {
 template <bool COUNT_ONLY>
 __device__ inline void rank_column(const PlanArgs& a, int col, int* run) {
   const int lane = lane_id();
-  const int begin = col * kPairsPerWave;
-  const int end = min(begin + kPairsPerWave, a.pairs);
-  for (int base = begin; base < end; base += kWave) {
+  const int begin = col * a.ppw;
+  const int end = min(begin + a.ppw, a.pairs);
+  // the column's ids are loaded up front: one memory round trip instead of one per
+  // 64 pairs (the walk below is serial through run[])
+  constexpr int kIters = kPairsPerWave / kWave;
+  int ids[kIters];
+#pragma unroll
+  for (int i = 0; i < kIters; ++i) {
+    const int q = begin + i * kWave + lane;
+    ids[i] = q < end ? a.topk_idx[q] : -1;
+  }
+#pragma unroll
+  for (int i = 0; i < kIters; ++i) {
+    const int base = begin + i * kWave;
+    if (base >= end) break;
     const int q = base + lane;
     const bool in = q < end;
-    const int id = in ? a.topk_idx[q] : -1;
+    const int id = ids[i];
     const int e = id - a.expert_begin;
     const bool local = in && id >= a.expert_begin && e < a.E;
     const uint64_t peers = match_key(local ? (uint32_t)e : 0u, local, a.key_bits);
@@ -195,14 +209,17 @@ __global__ __launch_bounds__(256) void plan_count_kernel(PlanArgs a) {
     for (int e = lane; e < a.E; e += kWave) a.hist[col * a.E + e] = run[e];
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const uint32_t prev = __hip_atomic_fetch_add(a.done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = prev == gridDim.x - 1;
+  if (gridDim.x > 1) {
+    // the last block to finish scans; a single block needs no device-scope handshake
+    if (threadIdx.x == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      const uint32_t prev = __hip_atomic_fetch_add(a.done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = prev == gridDim.x - 1;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
-  __syncthreads();
-  if (!s_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   // s_run doubles as the counts array of the scan (the waves' rows are done)
   int* s_cnt = &s_run[0][0];
   int* s_half = &s_run[1][0];
@@ -244,6 +261,7 @@ int launch_plan(const int32_t* topk_idx, const moe_plan_t& p, const WsLayout& L,
   a.ntiles_cap = p.rows_cap / p.tile;
   a.nfill = L.ntiles_cap;
   a.ncols = L.ncols;
+  a.ppw = L.ppw;
   a.counts = p.counts;
   a.offsets = p.offsets;
   a.pos = p.pos;
