@@ -109,8 +109,9 @@ def _short(name: str) -> str:
     return re.sub(r"moe::|\(moe::\w+\)|void |at::native::", "", name)[:70]
 
 
-def summarize_profiles(workload, trace_dir, fetch_dir, write_dir, out_dir, commands):
-    """rocprofv3 CSV output -> profiles/<kernel>_<workload>.txt and the FFN traffic JSON.
+def summarize_profiles(workload, trace_dir, fetch_dir, write_dir, out_dir, commands, train=False):
+    """rocprofv3 CSV output -> profiles/moe_layer_<workload>.txt and the FFN traffic JSON
+    (training runs: profiles/moe_train_<workload>.txt only).
 
     FETCH_SIZE / WRITE_SIZE (KiB per dispatch) are scaled by what they read for the
     three 1 GiB device-to-device copies of --copy-calibration."""
@@ -131,7 +132,8 @@ def summarize_profiles(workload, trace_dir, fetch_dir, write_dir, out_dir, comma
     ffn_ns = sum(float(r["AverageNs"]) for r in ffn)
     fetch = sum(v for k, v in per["FETCH_SIZE"][0].items() if "ffn_" in k)
     write = sum(v for k, v in per["WRITE_SIZE"][0].items() if "ffn_" in k)
-    lines = [f"# rocprofv3 summary: MoE layer, workload {workload}", "",
+    title = "MoE layer training step (forward keeping G + backward)" if train else "MoE layer"
+    lines = [f"# rocprofv3 summary: {title}, workload {workload}", "",
              "Commands (from the repository root on one MI355X):"]
     lines += [f"  {c}" for c in commands]
     lines += ["", f"{'kernel':70s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} "
@@ -144,10 +146,21 @@ def summarize_profiles(workload, trace_dir, fetch_dir, write_dir, out_dir, comma
                      f"{float(r['MinNs'])/1e3:10.1f} {float(r['MaxNs'])/1e3:10.1f} "
                      f"{(fv or 0)/1e6:10.1f} {(wv or 0)/1e6:10.1f}")
     lines += ["", f"FETCH_SIZE scale (1 GiB copy): x{per['FETCH_SIZE'][1]:.3f} of the KiB reading; "
-              f"WRITE_SIZE scale: x{per['WRITE_SIZE'][1]:.3f}",
-              f"expert FFN (all ffn_ kernels of one call): {ffn_ns/1e3:.1f} us, "
-              f"HBM fetch {fetch/1e9:.3f} GB + write {write/1e9:.3f} GB per call"]
+              f"WRITE_SIZE scale: x{per['WRITE_SIZE'][1]:.3f}"]
     os.makedirs(out_dir, exist_ok=True)
+    if train:
+        lines += ["The training step's kernels, by template: ffn_big_kernel<..., GEMM_A=true, ...> is the",
+                  "forward GEMM A keeping G; <..., GEMM_A=false, ..., EPI=1, ...> the backward GEMM Y (data,",
+                  "SwiGLU backward in its epilogue); <..., GEMM_A=false, ..., EPI=0, ...> both the forward",
+                  "GEMM Y and the backward GEMM A (data), averaged together; wgrad_kernel both weight-gradient",
+                  "GEMMs (dW2, then dW1), averaged together."]
+        txt = os.path.join(out_dir, f"moe_train_{workload}.txt")
+        with open(txt, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print(txt)
+        return
+    lines.append(f"expert FFN (all ffn_ kernels of one call): {ffn_ns/1e3:.1f} us, "
+                 f"HBM fetch {fetch/1e9:.3f} GB + write {write/1e9:.3f} GB per call")
     txt = os.path.join(out_dir, f"moe_layer_{workload}.txt")
     with open(txt, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -281,7 +294,7 @@ def main():
     args = ap.parse_args()
     if args.summarize_profiles:
         summarize_profiles(args.workload, *args.summarize_profiles, os.path.join(ROOT, "profiles"),
-                           [c.strip() for c in args.profile_commands.split(";") if c.strip()])
+                           [c.strip() for c in args.profile_commands.split(";") if c.strip()], train=args.train)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this single-GPU "
@@ -295,10 +308,6 @@ def main():
     from synth import config_by_name, make_inputs
 
     cfg = config_by_name(args.workload)
-    if args.train:
-        train_bench(args, cfg)
-        return
-    fp8 = cfg.dtype == "fp8"
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0").fill_(1)
         dst = torch.empty_like(src)
@@ -306,6 +315,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.train:
+        train_bench(args, cfg)
+        return
+    fp8 = cfg.dtype == "fp8"
     log(f"[bench] generating {cfg.name} inputs")
     inp = make_inputs(cfg, pin_memory=True)
     dev = torch.device("cuda:0")
