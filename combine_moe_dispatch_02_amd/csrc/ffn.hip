@@ -1564,10 +1564,8 @@ int ffn_supported(int32_t H, int32_t I, int32_t dtype, int32_t tile, int32_t blo
   return MOE_ERR_INVALID;
 }
 
-#ifndef MOE_BIG_WAVES
-#define MOE_BIG_WAVES 8
-#endif
-constexpr int kBigWaves = MOE_BIG_WAVES;
+// waves of a big-tile workgroup: each owns BM rows x 64 of the unit's 512 columns
+constexpr int kBigWaves = 8;
 
 template <int BM, int BN, int WM, int WN, bool FP8, bool GEMM_A>
 static void launch_one(const FfnArgs& a, int grid, hipStream_t s) {
