@@ -275,6 +275,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="zipf_skew")
     ap.add_argument("--streams", action="store_true", help="dispatch/combine and FFN on two streams")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of one step captured in a HIP graph (one stream)")
     ap.add_argument("--train", action="store_true",
                     help="time a training step: the forward (keeping G) plus the backward pass (bf16 workloads)")
     ap.add_argument("--combine-on-completion", action="store_true",
@@ -354,6 +356,19 @@ def main():
     rc = moe.moe_get_error(layer.ws)
     if rc != 0:
         raise RuntimeError(f"device error {rc} during warmup")
+    if args.graph:
+        # one step captured in a HIP graph (the same launches, replayed without the host)
+        if streams is not None:
+            raise SystemExit("--graph runs the one-stream step")
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+
+        def step():  # noqa: F811
+            graph.replay()
+
+        step()
+        torch.cuda.synchronize()
 
     # whole-step timing: K steps bracketed by synchronisation
     log(f"[bench] timing {args.steps} steps")
@@ -432,6 +447,7 @@ def main():
                    "tile": cfg.tile, "routing": cfg.routing, "pairs": work["pairs"],
                    "pool_rows": int(layer.plan.offsets[-1].item()),
                    "streams": "two (comm + compute)" if args.streams else "one",
+                   "launch": "HIP graph replay" if args.graph else "eager",
                    "combine": ("on completion, inside GEMM Y (stage 'ffn' includes it)"
                                if args.combine_on_completion else "kernel after the FFN"),
                    "weights": "MFMA-tiled (permuted once at load time)" if layer.tiled else "row-major"},
