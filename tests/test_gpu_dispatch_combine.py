@@ -10,7 +10,7 @@ import torch
 
 import combine_moe_dispatch_02_amd as moe
 import oracle
-from synth import CONFIGS, MoEConfig, config_by_name, make_inputs
+from synth import MoEConfig, config_by_name, make_inputs
 
 from _gpu import say
 
@@ -43,8 +43,8 @@ def plan_and_dispatch(inp, epoch=5, fp8=False, dtype=None):
 
 
 SMALL = [
-    CONFIGS[0],
-    CONFIGS[1],
+    config_by_name("tiny"),
+    config_by_name("decode"),
     MoEConfig("ragged", 333, 392, 64, 11, 3, 6, 3, 32),      # H not a multiple of 512 chunks
     MoEConfig("ep_small", 700, 7168, 64, 64, 0, 8, 8, 128),   # two row segments per lane
 ]
@@ -154,7 +154,7 @@ def test_dispatch_mxfp8_full_size_sampled_rows():
     assert np.array_equal(pool_s.cpu().numpy()[rows], scales)
 
 
-@pytest.mark.parametrize("cfg", [CONFIGS[0], MoEConfig("ident", 515, 256, 64, 12, 4, 5, 4, 16)],
+@pytest.mark.parametrize("cfg", [config_by_name("tiny"), MoEConfig("ident", 515, 256, 64, 12, 4, 5, 4, 16)],
                          ids=["tiny", "ident_nonlocal"])
 def test_identity_expert_combine(cfg):
     inp = make_inputs(cfg, weights=False)

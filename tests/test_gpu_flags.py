@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import combine_moe_dispatch_02_amd as moe
-from synth import CONFIGS, MoEConfig, make_inputs
+from synth import config_by_name, MoEConfig, make_inputs
 
 from _gpu import dev_inputs, make_layer, run_layer, say
 
@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 
 
 def test_epoch_rollover():
-    cfg = CONFIGS[0]
+    cfg = config_by_name("tiny")
     d = dev_inputs(make_inputs(cfg))
     layer = make_layer(cfg)
     say("epoch rollover")
@@ -57,7 +57,7 @@ def test_pool_too_small_is_reported():
     assert moe.moe_get_error(layer.ws) == moe.layer._abi.MOE_ERR_INVALID
 
 
-@pytest.mark.parametrize("cfg", [CONFIGS[1], CONFIGS[4].with_(name="fp8_4k", T=4096)],
+@pytest.mark.parametrize("cfg", [config_by_name("decode"), config_by_name("fp8_weights").with_(name="fp8_4k", T=4096)],
                          ids=["decode", "fp8_4k"])
 def test_two_streams_match_one(cfg):
     inp = make_inputs(cfg)

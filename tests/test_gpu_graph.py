@@ -7,14 +7,14 @@ import pytest
 import torch
 
 import combine_moe_dispatch_02_amd as moe
-from synth import CONFIGS, MoEConfig, make_inputs
+from synth import config_by_name, MoEConfig, make_inputs
 
 from _gpu import dev_inputs, make_layer, say
 
 pytestmark = pytest.mark.gpu
 
 GRAPH_CASES = [
-    CONFIGS[0],                                                         # tiny
+    config_by_name("tiny"),
     MoEConfig("graph_big", 600, 1024, 512, 8, 0, 8, 4, 128),           # big-tile kernels, ring
     MoEConfig("graph_fp8", 300, 512, 256, 6, 0, 6, 2, 64, "fp8"),
 ]

@@ -9,15 +9,15 @@ import pytest
 import torch
 
 import oracle
-from synth import CONFIGS, MoEConfig, config_by_name, make_inputs
+from synth import MoEConfig, config_by_name, make_inputs
 
 from _gpu import TOL, assert_plan_equal, dev_inputs, make_layer, out_rows_f64, rel_err, run_layer, say
 
 pytestmark = pytest.mark.gpu
 
 FULL_COMPARE = [
-    CONFIGS[0],                                                      # tiny
-    CONFIGS[1],                                                      # decode
+    config_by_name("tiny"),
+    config_by_name("decode"),
     MoEConfig("ragged_t32", 333, 384, 192, 9, 0, 9, 3, 32),
     MoEConfig("ragged_t64", 517, 512, 320, 7, 2, 4, 2, 64),         # experts 2..5 local
     MoEConfig("t128_bn128", 1500, 640, 192, 5, 0, 5, 2, 128),       # H % 256 != 0, I % 128 != 0
@@ -86,7 +86,7 @@ def test_layer_full_size_sampled(name):
 
 
 def test_layer_repeat_is_bitwise_identical():
-    cfg = CONFIGS[4].with_(name="fp8_repeat", T=2048)
+    cfg = config_by_name("fp8_weights").with_(name="fp8_repeat", T=2048)
     inp = make_inputs(cfg)
     d = dev_inputs(inp)
     layer = make_layer(cfg)
@@ -116,7 +116,7 @@ def test_layer_polled_pool_size_matches_bound():
 def test_layer_row_major_weights_on_big_tiles(name):
     # the big-tile kernel also reads row-major weights (fp8: row-major weights take the
     # general kernel); same tolerance as the tiled path
-    cfg = CONFIGS[1] if name == "decode" else next(c for c in FULL_COMPARE if c.name == name)
+    cfg = config_by_name("decode") if name == "decode" else next(c for c in FULL_COMPARE if c.name == name)
     inp = make_inputs(cfg)
     d = dev_inputs(inp)
     layer = make_layer(cfg, weight_layout="row_major")

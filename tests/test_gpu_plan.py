@@ -6,7 +6,7 @@ import torch
 
 import combine_moe_dispatch_02_amd as moe
 import oracle
-from synth import CONFIGS, make_inputs
+from synth import CONFIGS, config_by_name, make_inputs
 
 from _gpu import assert_plan_equal, say
 
@@ -73,7 +73,7 @@ def test_plan_all_to_one_expert():
 
 def test_plan_reuses_workspace():
     # the last-block counter resets itself: a second plan on the same buffers agrees
-    cfg = CONFIGS[3]
+    cfg = config_by_name("zipf_skew")
     inp = make_inputs(cfg, weights=False)
     say("plan twice on one workspace")
     plan, ws = gpu_plan(inp.topk_idx, 0, cfg.num_local_experts, cfg.tile)
