@@ -31,9 +31,13 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
-    """Hash of the FFN kernel source: counter readings in profiles/ are valid only for it."""
+    """Hash of the FFN kernel source, comments and blank lines left out: counter readings
+    in profiles/ are valid only for the code they were taken on."""
+    import re
+
     p = os.path.join(ROOT, "combine_moe_dispatch_02_amd", "csrc", "ffn.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    code = [re.sub(r"//.*$", "", ln).rstrip() for ln in open(p).read().splitlines()]
+    return hashlib.sha256("\n".join(ln for ln in code if ln).encode()).hexdigest()[:16]
 
 
 def read_traffic(workload: str, src_hash: str):

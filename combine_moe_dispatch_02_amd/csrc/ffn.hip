@@ -13,16 +13,26 @@
 // the units; GEMM A waits (acquire) until its tile's ready flag equals the
 // epoch of the dispatch call.
 //
-// Main loop per 128-byte K step (64 bf16 or 128 e4m3 per row):
-//   global -> registers (16-byte lanes) for step k+1 while step k runs on MFMA
-//   from LDS; registers -> the other LDS buffer; one barrier per step.
+// Two kernels, one K step = 128 bytes of each row (64 bf16 or 128 e4m3 / e2m1 pairs):
+//  * ffn_gemm_kernel (4 waves, any BN of 128/256, row-major weights): A and B tiles
+//    through a double-buffered LDS, loaded one step ahead via registers; one
+//    barrier per step. fp8 there: each block's product leaves the MFMA on its own
+//    (zero accumulator input), then acc += product * a_scale[row] * b_scale[block].
+//  * ffn_big_kernel (8 waves, BM x 512 units, each wave BM x 64): the weights
+//    stream straight into registers one step ahead (the MFMA-tiled layout of
+//    moe_pack_weights makes each 16-byte lane load part of 1 KiB of contiguous
+//    memory); the pool rows come through LDS, either two stages loaded through
+//    registers (bf16) or by LDS-DMA (fp8), or a four-stage LDS-DMA ring three steps
+//    ahead (bf16, mxfp4); the output leaves through LDS in whole row segments. fp8
+//    there keeps acc in units of the current block's scales and rescales it by
+//    old / new before each block's MFMAs.
 // LDS rows are 128 bytes, 16-byte chunks XOR-swizzled by (row & 7), so the 8
 // lanes that read one chunk column from 8 consecutive rows hit 8 different
 // bank groups.
 // bf16: v_mfma_f32_16x16x32_bf16, A/B fragments = 8 consecutive K values of one
 // row per lane (lane l: row l%16, K chunk l/16).
 // fp8: v_mfma_scale_f32_16x16x128_f8f6f4 with unit scales (E8M0 127), one per
-// 128-wide K block, then acc += partial * a_scale[row] * b_scale[block] in fp32.
+// 128-wide K block.
 // mxfp4: the same instruction with e2m1 weights (format 4) and e4m3 activations,
 // its per-lane E8M0 operands carrying the 1x32 block scales of both sides.
 #include <algorithm>
