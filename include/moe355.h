@@ -187,7 +187,8 @@ MOE355_API int moe_dispatch(const void* x, int32_t H, int32_t act_dtype, const m
  * are never read by moe_combine. Only the first pool_rows/tile tiles are
  * computed; a plan that needs more records MOE_ERR_INVALID.
  * Errors: MOE_ERR_INVALID (null pointers, bad dtype, epoch 0, small workspace,
- * pool_rows not a multiple of tile), MOE_ERR_UNSUPPORTED (bf16: H % 128 or
+ * pool_rows not a multiple of tile, a moe_tile_config field out of its range),
+ * MOE_ERR_UNSUPPORTED (bf16: H % 128 or
  * I % 64 nonzero; fp8: H % 256 or I % 128 nonzero, or tile < 64; tiled weights:
  * bf16 with tile 64 or 128, H % 512 == 0 and I % 256 == 0 only; mxfp4: tiled
  * weights, tile 128, H % 512 == 0 and I % 256 == 0 only).
