@@ -154,3 +154,23 @@ def test_layer_a_pipelines_agree(name):
     ring = run_layer(make_layer(cfg, cfg=moe.TileConfig(0, 0, 0, 0, 0, 4)), d).clone()
     two = run_layer(make_layer(cfg, cfg=moe.TileConfig(0, 0, 0, 0, 0, 2)), d)
     assert torch.equal(ring.view(torch.int16), two.view(torch.int16))
+
+
+def test_layer_large_batch_sampled():
+    # four times the skew workload's pairs (524 288; a pool of about 540 k rows, 4.4 GB of bf16
+    # pool rows and as much y): every 64-bit row offset and every per-tile buffer range at a
+    # size past 2^32 bytes, on sampled tokens
+    cfg = config_by_name("zipf_skew").with_(name="large_batch", T=65536, routing="uniform")
+    inp = make_inputs(cfg, pin_memory=True)
+    d = dev_inputs(inp)
+    layer = make_layer(cfg)
+    say("layer large batch", cfg.T)
+    out = run_layer(layer, d)
+    p = oracle.plan(inp.topk_idx, cfg.expert_begin, cfg.num_local_experts, cfg.tile)
+    assert_plan_equal(layer.plan, p)
+    assert p.P * cfg.H * 2 > (1 << 32)
+    toks = _sample_tokens(cfg, inp, n=12)
+    ref = oracle.moe_layer(inp, tokens=toks, p=p)
+    err = rel_err(out_rows_f64(out, toks), ref.out)
+    print(f"large batch: {len(toks)} sampled tokens, max-norm rel err {err:.3e}")
+    assert err <= TOL[cfg.dtype]
