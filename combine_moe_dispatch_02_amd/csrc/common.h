@@ -28,7 +28,7 @@ struct WsLayout {
   size_t ydone = 0;      // uint32 [ntiles_cap]: GEMM Y units finished per tile (combine on completion)
   size_t cq = 0;         // uint32: combine items claimed (combine on completion)
   size_t h = 0;          // h [pool_rows][I]: bf16, or e4m3 codes
-  size_t hs = 0;         // fp8: float [pool_rows][I/128]; mxfp4: E8M0 bytes [pool_rows][I/32]
+  size_t hs = 0;         // h's scale words (pool_rows x ceil(I/128), tile-major as scale_word())
   size_t plan_end = 0;   // end of what plan/dispatch need
   size_t total = 0;
   int32_t ncols = 0;
@@ -37,6 +37,16 @@ struct WsLayout {
 };
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Scales of quantised activations (the pool in fp8 and mxfp4 mode, and h) are kept
+// tile-major, one 4-byte word per (pool row, 128-column K group): the fp32 group scale,
+// or the group's four E8M0 block bytes in block order. Row p's word for group g is
+// word ((p / tile) * groups + g) * tile + p % tile, so the words one K step of a tile
+// needs are tile consecutive words (a row-major [rows][groups] array would make that
+// step a gather of one word from each of tile rows).
+__host__ __device__ inline int64_t scale_word(int64_t row, int32_t g, int32_t groups, int32_t tile_shift) {
+  return (((row >> tile_shift) * groups + g) << tile_shift) + (row & ((1 << tile_shift) - 1));
+}
 
 inline int64_t pool_rows_bound(int64_t T, int64_t K, int64_t E, int64_t tile) {
   return (T * K + E * (tile - 1)) / tile * tile;
@@ -60,12 +70,9 @@ inline WsLayout ws_layout(int32_t T, int32_t K, int32_t E, int32_t tile, int64_t
     const size_t elem = dtype == MOE_BF16 ? 2 : 1;
     L.h = off;
     off = align_up(off + (size_t)pool_rows * I * elem, 256);
-    if (dtype == MOE_FP8_E4M3_G128) {
+    if (dtype == MOE_FP8_E4M3_G128 || dtype == MOE_MXFP4) {
       L.hs = off;
-      off = align_up(off + (size_t)pool_rows * (I / 128) * 4, 256);
-    } else if (dtype == MOE_MXFP4) {
-      L.hs = off;
-      off = align_up(off + (size_t)pool_rows * (I / 32), 256);
+      off = align_up(off + (size_t)pool_rows * ((I + 127) / 128) * 4, 256);
     }
   }
   L.total = off;

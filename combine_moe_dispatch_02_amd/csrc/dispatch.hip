@@ -12,7 +12,8 @@
 // scale) with IEEE division, round to nearest even, saturating. In mxfp4 mode
 // the activations become MXFP8 (OCP MX): each 1x32 block (4 lanes x 8 values)
 // gets the E8M0 scale 2^e, e = floor(log2(amax)) - 8, and codes e4m3(x * 2^-e),
-// exact scaling then the same rounding. A wave handles
+// exact scaling then the same rounding. Scales go to their tile-major words
+// (scale_word: one K step of a pool tile reads them as consecutive words). A wave handles
 // a run of 64/K tokens; a workgroup's runs are published with a single
 // device-scope release (an L2 write-back on this chip, so it is paid per
 // workgroup, not per row or per wave); each stored pair then bumps its tile's
@@ -34,7 +35,7 @@ struct DispatchArgs {
   const int32_t* offsets;
   const int32_t* counts;
   uint8_t* pool;
-  void* pool_s;                // fp8: float [rows][H/128]; mxfp4: E8M0 bytes [rows][H/32]
+  void* pool_s;                // scale words, tile-major (scale_word): fp8 float, mxfp4 4 E8M0 bytes
   int32_t pool_rows;
   uint32_t* tile_fill;
   uint32_t* tile_ready;
@@ -91,19 +92,19 @@ __device__ inline void dispatch_token(const DispatchArgs& a, int t, int p, uint6
         q[i].x = pack_e4m3x4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
         q[i].y = pack_e4m3x4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
       }
-      const int blocks = H >> 5;
+      const int words = (H + 127) >> 7;
       for (int k = 0; k < a.K; ++k) {
         if (!((dest >> k) & 1ull)) continue;
         const int pk = readlane(p, k);
         const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.pool + (int64_t)pk * out_row_bytes, (uint32_t)out_row_bytes);
-        const __amdgpu_buffer_rsrc_t sr =
-            make_rsrc(static_cast<uint8_t*>(a.pool_s) + (int64_t)pk * blocks, (uint32_t)blocks);
+        // byte (c >> 2) & 3 of the row's scale word for group c >> 4 (chunk c: 8 elements)
+        uint8_t* srow = static_cast<uint8_t*>(a.pool_s) + scale_word(pk, 0, words, a.tile_shift) * 4;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
           const int c = c0 + i * kWave + lane;
           buf_store8(q[i], pr, (uint32_t)c * 8u);
-          if ((lane & 3) == 0)   // chunks past the row end fall outside the buffer: dropped
-            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sb[i], sr, (uint32_t)(c >> 2), 0, 0);
+          if ((lane & 3) == 0 && c < nch)
+            srow[((int64_t)(c >> 4) << a.tile_shift) * 4 + ((c >> 2) & 3)] = (uint8_t)sb[i];
         }
       }
     } else {
@@ -130,12 +131,12 @@ __device__ inline void dispatch_token(const DispatchArgs& a, int t, int p, uint6
         if (!((dest >> k) & 1ull)) continue;
         const int pk = readlane(p, k);
         const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.pool + (int64_t)pk * out_row_bytes, (uint32_t)out_row_bytes);
-        float* srow = static_cast<float*>(a.pool_s) + (int64_t)pk * groups;
+        float* srow = static_cast<float*>(a.pool_s) + scale_word(pk, 0, groups, a.tile_shift);
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
           const int c = c0 + i * kWave + lane;
           buf_store8(q[i], pr, (uint32_t)c * 8u);
-          if ((lane & 15) == 0 && c < nch) srow[c >> 4] = s[i];
+          if ((lane & 15) == 0 && c < nch) srow[(int64_t)(c >> 4) << a.tile_shift] = s[i];
         }
       }
     }

@@ -51,11 +51,11 @@ typedef uint32_t u32x8_t __attribute__((ext_vector_type(8)));
 
 struct FfnArgs {
   const uint8_t* A;          // pool (GEMM A) or h (GEMM Y): [rows][Kdim] elements
-  const float* A_s;          // fp8: activation group scales [rows][Kdim/128]
+  const float* A_s;          // fp8: activation group scales, tile-major words (scale_word)
   const uint8_t* B;          // w1 or w2, expert-major
   const float* B_s;          // fp8: weight block scales, expert-major
   uint8_t* out;              // h (GEMM A) or y_pool (GEMM Y)
-  float* out_s;              // fp8 GEMM A: h group scales [rows][I/128]
+  float* out_s;              // fp8 GEMM A: h group scales, tile-major words
   int32_t ksteps;            // K steps of 128 bytes
   int64_t lda;               // bytes per A row
   int64_t b_expert;          // bytes per expert of B
@@ -63,7 +63,7 @@ struct FfnArgs {
   int32_t up_row0;           // GEMM A: first up row of w1 (= I)
   int64_t ldo;               // bytes per out row
   int32_t n_units;           // N blocks per tile
-  int32_t s_kblocks;         // fp8: Kdim / 128
+  int32_t s_kblocks;         // fp8, mxfp4: Kdim / 128 (scale words per row)
   int32_t bs_ld;             // fp8: B scale row stride (= Kdim / 128)
   int64_t bs_expert;         // fp8: B scale entries per expert
   int32_t out_groups;        // fp8 GEMM A: I / 128
@@ -80,12 +80,10 @@ struct FfnArgs {
   uint32_t* err;
   uint64_t timeout;
   int32_t wait_ready;
-  const uint8_t* A_e8;       // mxfp4: activation E8M0 scales [rows][Kdim/32]
+  const uint8_t* A_e8;       // mxfp4: activation E8M0 scales, tile-major 4-byte words
   const uint8_t* B_e8;       // mxfp4: weight E8M0 scales in tile order, expert-major
-  uint8_t* out_e8;           // mxfp4 GEMM A: h E8M0 scales [rows][I/32]
-  int32_t e8_lda;            // mxfp4: bytes per row of A_e8 (Kdim/32)
+  uint8_t* out_e8;           // mxfp4 GEMM A: h E8M0 scales, tile-major 4-byte words
   int64_t b_e8_expert;       // mxfp4: bytes per expert of B_e8
-  int32_t e8_ldo;            // mxfp4 GEMM A: bytes per row of out_e8 (I/32)
   // combine on completion (GEMM Y on the big-tile kernel; null ydone = off)
   uint32_t* ydone;           // per tile: GEMM Y units finished (GEMM A zeroes them)
   uint32_t* cq;              // next combine item to claim (GEMM A zeroes it)
@@ -261,7 +259,7 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(FfnArgs a) {
         rb[i] = *reinterpret_cast<const u32x4*>(Bexp + b_global_row(r) * a.ldb + kt * 128 + ch * 16);
       }
       if constexpr (FP8) {
-        if (tid < BM) ras = a.A_s[(int64_t)(m0 + tid) * a.s_kblocks + kt];
+        if (tid < BM) ras = a.A_s[((int64_t)m * a.s_kblocks + kt) * BM + tid];
       }
     };
     auto store_stage = [&](int buf) {
@@ -410,7 +408,7 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(FfnArgs a) {
               const int col = hcol0 + tn * 16 + l16;
               a.out[(int64_t)row * a.ldo + col] = (uint8_t)e4m3_from_f32(hv[tm][tn][i] * inv);
             }
-            if (wn == 0 && l16 == 0) a.out_s[(int64_t)row * a.out_groups + ((j * (BN / 2)) >> 7)] = sc;
+            if (wn == 0 && l16 == 0) a.out_s[((int64_t)m * a.out_groups + ((j * (BN / 2)) >> 7)) * BM + rl] = sc;
           }
         __syncthreads();
       }
@@ -658,7 +656,7 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
           ra[st][i] = __builtin_amdgcn_raw_buffer_load_b128(ar, aoff[i], kofs, 0);
       }
       if constexpr (FP8) {
-        if (tid < BM) ras[st] = a.A_s[(int64_t)(m0 + tid) * a.s_kblocks + ks];
+        if (tid < BM) ras[st] = a.A_s[((int64_t)m * a.s_kblocks + ks) * BM + tid];
       }
     };
     auto store_a = [&](auto SET, int stage) {
@@ -748,9 +746,9 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
     // tile's rows read, and later store, the last row's scale again
     auto load_ascale = [&](int ks) {
       if constexpr (MX)
-        rax = *reinterpret_cast<const uint32_t*>(a.A_e8 + (int64_t)(m0 + min(tid, BM - 1)) * a.e8_lda + 4 * ks);
+        rax = reinterpret_cast<const uint32_t*>(a.A_e8)[((int64_t)m * a.s_kblocks + ks) * BM + min(tid, BM - 1)];
       else
-        ras[0] = a.A_s[(int64_t)(m0 + min(tid, BM - 1)) * a.s_kblocks + ks];
+        ras[0] = a.A_s[((int64_t)m * a.s_kblocks + ks) * BM + min(tid, BM - 1)];
     };
     auto dma_a = [&](auto STAGE, int ks) {
       dma_rows(STAGE, ks);
@@ -1298,8 +1296,9 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
             for (int tn = 2 * bi; tn < 2 * bi + 2; ++tn)
               *reinterpret_cast<uint32_t*>(hst(rl, hb0 + tn * 16)) =
                   pack_e4m3x4(acc[tm][tn][0] * inv, acc[tm][tn][1] * inv, acc[tm][tn][2] * inv, acc[tm][tn][3] * inv);
+            const int blk = ((j * 256 + wn * HALF) >> 5) + bi;   // h's 32-column block
             if (lhi == 0)
-              a.out_e8[(int64_t)(m0 + rl) * a.e8_ldo + ((j * 256 + wn * HALF) >> 5) + bi] = (uint8_t)(ex + 127);
+              a.out_e8[(((int64_t)m * a.out_groups + (blk >> 2)) * BM + rl) * 4 + (blk & 3)] = (uint8_t)(ex + 127);
           }
         }
         __syncthreads();
@@ -1337,7 +1336,7 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
             *reinterpret_cast<uint32_t*>(hst(rl, hb0 + tn * 16)) =
                 pack_e4m3x4(acc[tm][tn][0] * inv, acc[tm][tn][1] * inv, acc[tm][tn][2] * inv, acc[tm][tn][3] * inv);
           if (wn % GW == 0 && lhi == 0)
-            a.out_s[(int64_t)(m0 + rl) * a.out_groups + ((j * 256 + wn * HALF) >> 7)] = sc;
+            a.out_s[((int64_t)m * a.out_groups + ((j * 256 + wn * HALF) >> 7)) * BM + rl] = sc;
         }
         __syncthreads();  // (also: every s_red read is done before the next unit writes it)
         hstore();
@@ -1719,9 +1718,7 @@ int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream
   a.A_e8 = mx ? static_cast<const uint8_t*>(f.pool_s) : nullptr;
   a.B_e8 = mx ? static_cast<const uint8_t*>(f.w1_s) : nullptr;
   a.out_e8 = hs8;
-  a.e8_lda = H / 32;
   a.b_e8_expert = (int64_t)2 * I * (H / 32);
-  a.e8_ldo = I / 32;
   a.ksteps = H * eb / 128;
   a.lda = (int64_t)H * eb;
   a.b_expert = mx ? (int64_t)2 * I * (H / 2) : (int64_t)2 * I * H * eb;
@@ -1758,7 +1755,6 @@ int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream
   a.A_e8 = hs8;
   a.B_e8 = mx ? static_cast<const uint8_t*>(f.w2_s) : nullptr;
   a.out_e8 = nullptr;
-  a.e8_lda = I / 32;
   a.b_e8_expert = (int64_t)H * (I / 32);
   a.ksteps = I * eb / 128;
   a.lda = (int64_t)I * eb;

@@ -370,10 +370,10 @@ class StreamMoE:
             self.pool_s = None
         elif self.dtype == "fp8":
             self.pool = torch.empty(rows, H, dtype=torch.uint8, device=device)
-            self.pool_s = torch.empty(rows, H // 128, dtype=torch.float32, device=device)
+            self.pool_s = torch.empty(rows, H // 128, dtype=torch.float32, device=device)   # tile-major words
         else:
             self.pool = torch.empty(rows, H, dtype=torch.uint8, device=device)
-            self.pool_s = torch.empty(rows, H // 32, dtype=torch.uint8, device=device)
+            self.pool_s = torch.empty(rows, (H + 127) // 128 * 4, dtype=torch.uint8, device=device)
         self.y_pool = torch.empty(rows, H, dtype=torch.bfloat16, device=device)
         self.out = torch.empty(T, H, dtype=torch.bfloat16, device=device)
         self.epoch = 0

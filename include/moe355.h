@@ -31,7 +31,8 @@
  *     y_pool[rows][H], out[T][H].
  *   - Types: bf16 is IEEE binary32's upper half; fp8 is OCP E4M3 ("fn": bias 7,
  *     max 448, no infinities). fp8 scales are fp32: activations one per 1x128
- *     group of the contraction dim ([rows][H/128] for the pool), weights one per
+ *     group of the contraction dim (tile-major words for the pool, see
+ *     moe_dispatch), weights one per
  *     128x128 block (w1_s[E_local][2I/128][H/128], w2_s[E_local][H/128][I/128]).
  */
 #ifndef MOE355_H
@@ -150,14 +151,20 @@ MOE355_API int moe_query_pool_rows(const moe_plan_t* plan, int32_t* host_P, void
 /*
  * A2. Dispatch: pool[pos[t,k]] = x[t] for every local pair (device x bf16 [T][H]).
  * bf16: pool is bf16 [pool_rows][H] and pool_s must be NULL.
- * fp8:  pool is e4m3 [pool_rows][H] and pool_s fp32 [pool_rows][H/128]; each
- *       1x128 group g of x[t] is stored as codes e4m3(x/s) with s = amax/448
- *       (s = 1 for an all-zero group), rounded to nearest even and saturated.
- * mxfp4: pool is e4m3 [pool_rows][H] and pool_s E8M0 bytes [pool_rows][H/32]
- *       (MXFP8, OCP MX specification): per 1x32 block, e = floor(log2(amax)) - 8
- *       clamped to [-127, 127] (-127 for an all-zero block), pool_s = e + 127,
- *       codes e4m3(x * 2^-e) rounded to nearest even and saturated. The scaling is
- *       exact, so the codes depend on x alone.
+ * fp8:  pool is e4m3 [pool_rows][H] and pool_s holds pool_rows * H/128 fp32
+ *       scale words; each 1x128 group g of x[t] is stored as codes e4m3(x/s) with
+ *       s = amax/448 (s = 1 for an all-zero group), rounded to nearest even and
+ *       saturated.
+ * mxfp4: pool is e4m3 [pool_rows][H] and pool_s holds pool_rows * ceil(H/128)
+ *       4-byte words of E8M0 scales (MXFP8, OCP MX specification): per 1x32
+ *       block, e = floor(log2(amax)) - 8 clamped to [-127, 127] (-127 for an
+ *       all-zero block), scale byte e + 127, codes e4m3(x * 2^-e) rounded to
+ *       nearest even and saturated. The scaling is exact, so the codes depend on
+ *       x alone. Byte b of a row's word for group g is the scale of its block 4g+b.
+ * Scale words are tile-major (tile = plan->tile): pool row p's word for its
+ * 128-column group g is word ((p / tile) * groups + g) * tile + p % tile, with
+ * groups = H/128 (fp8) or ceil(H/128) (mxfp4), so that one K step of a pool
+ * tile reads tile consecutive words.
  * Padding rows are not written. After a tile's real rows are stored the tile's
  * tile_ready entry is set to `epoch` with release ordering (device scope).
  * epoch must be nonzero and should change from one layer call to the next.
@@ -177,7 +184,8 @@ MOE355_API int moe_dispatch(const void* x, int32_t H, int32_t act_dtype, const m
  *           the pool (mxfp4 mode) in the workspace;
  *   GEMM Y: y_pool_tile = h . w2[e]^T (fp32 accumulate), stored bf16.
  * fp8 mode applies activation and weight scales per 128-wide K block in fp32.
- * mxfp4 mode: pool_s is E8M0 [pool_rows][H/32]; w1 / w2 are MXFP4 codes in the
+ * pool_s holds the scale words moe_dispatch writes (fp8 and mxfp4, tile-major).
+ * mxfp4 mode: w1 / w2 are MXFP4 codes in the
  * tiled layout of moe_pack_weights and w1_s / w2_s their E8M0 scales in the
  * layout of moe_pack_mx_scales; the scales are applied per 32-wide K block by
  * the matrix cores (scaled MFMA), so no rescaling happens in fp32.

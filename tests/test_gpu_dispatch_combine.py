@@ -1,7 +1,8 @@
 """A2 and A5 on the GPU, without the FFN:
 * dispatch writes exactly the oracle's pool rows (bf16 bits; e4m3 codes and fp32 group
-  scales; MXFP8 e4m3 codes and E8M0 block scales),
-  leaves poisoned padding rows alone, and raises every tile's ready flag;
+  scales; MXFP8 e4m3 codes and E8M0 block scales; the scales read back from the
+  tile-major words the ABI documents), leaves poisoned padding rows alone, and raises
+  every tile's ready flag;
 * with identity experts (y_pool = pool) combine returns sum_k w_k x_t, and with
   K = 1, w = 1 the dispatch -> combine round trip is bit-exact."""
 import numpy as np
@@ -19,7 +20,19 @@ pytestmark = pytest.mark.gpu
 POISON = 0x7FC1  # a bf16 NaN pattern
 
 
+def scale_rows(words, rows, tile, per_row):
+    """Scale words stored tile-major (row p's word for group g at word
+    (p // tile * groups + g) * tile + p % tile, 4 bytes each) -> [rows][per_row] in row
+    order: fp32 words for fp8, the 4 E8M0 bytes of each word for mxfp4."""
+    w = words.cpu().numpy().reshape(-1)
+    unit = 1 if w.dtype == np.float32 else 4
+    groups = per_row // unit
+    w = w[: rows * per_row].reshape(rows // tile, groups, tile, unit)
+    return w.transpose(0, 2, 1, 3).reshape(rows, per_row)
+
+
 def plan_and_dispatch(inp, epoch=5, fp8=False, dtype=None):
+    """Plan and dispatch; pool_s comes back in row order (see scale_rows)."""
     c = inp.cfg
     dtype = dtype or ("fp8" if fp8 else "bf16")
     plan = moe.Plan.allocate(c.T, c.K, c.expert_begin, c.num_local_experts, c.tile)
@@ -30,7 +43,7 @@ def plan_and_dispatch(inp, epoch=5, fp8=False, dtype=None):
         pool_s = torch.full((rows, c.H // 128), -1.0, dtype=torch.float32, device="cuda")
     elif dtype == "mxfp4":
         pool = torch.full((rows, c.H), 0x7F, dtype=torch.uint8, device="cuda")
-        pool_s = torch.full((rows, c.H // 32), 0xFF, dtype=torch.uint8, device="cuda")
+        pool_s = torch.full((rows, (c.H + 127) // 128 * 4), 0xFF, dtype=torch.uint8, device="cuda")
     else:
         pool = torch.full((rows, c.H), POISON, dtype=torch.int16, device="cuda").view(torch.bfloat16)
         pool_s = None
@@ -39,6 +52,8 @@ def plan_and_dispatch(inp, epoch=5, fp8=False, dtype=None):
     moe.moe_dispatch(x, plan, pool, pool_s, epoch, ws, dtype)
     torch.cuda.synchronize()
     assert moe.moe_get_error(ws) == 0
+    if pool_s is not None:
+        pool_s = scale_rows(pool_s, rows, c.tile, pool_s.shape[1])
     return plan, ws, pool, pool_s
 
 
@@ -100,7 +115,7 @@ def test_dispatch_fp8_codes_and_scales_exact(cfg):
     op = oracle.plan(inp.topk_idx, cfg.expert_begin, cfg.num_local_experts, cfg.tile)
     rows, (codes, scales) = oracle.dispatch(inp.x, op, fp8=True)
     assert np.array_equal(pool.cpu().numpy()[rows], codes)
-    assert np.array_equal(pool_s.cpu().numpy()[rows], scales)
+    assert np.array_equal(pool_s[rows, : scales.shape[1]], scales)
 
 
 def test_dispatch_fp8_full_size_sampled_rows():
@@ -113,7 +128,7 @@ def test_dispatch_fp8_full_size_sampled_rows():
     rows = np.sort(rng.choice(np.nonzero(src >= 0)[0], 256, replace=False))
     codes, scales = oracle.token_rows(inp.x, True, src[rows] // cfg.K)
     assert np.array_equal(pool.cpu().numpy()[rows], codes)
-    assert np.array_equal(pool_s.cpu().numpy()[rows], scales)
+    assert np.array_equal(pool_s[rows, : scales.shape[1]], scales)
 
 
 MX = [
@@ -136,9 +151,10 @@ def test_dispatch_mxfp8_codes_and_scales_exact(cfg):
     op = oracle.plan(inp.topk_idx, cfg.expert_begin, cfg.num_local_experts, cfg.tile)
     rows, (codes, scales) = oracle.dispatch(inp.x, op, "mxfp4")
     assert np.array_equal(pool.cpu().numpy()[rows], codes)
-    assert np.array_equal(pool_s.cpu().numpy()[rows], scales)
+    assert np.array_equal(pool_s[rows, : scales.shape[1]], scales)
     pad = np.setdiff1d(np.arange(op.P_cap), rows)
-    assert (pool_s.cpu().numpy()[pad] == 0xFF).all()
+    assert (pool_s[pad] == 0xFF).all()
+    assert (pool_s[rows, scales.shape[1]:] == 0xFF).all()       # the last word's bytes past H/32
 
 
 def test_dispatch_mxfp8_full_size_sampled_rows():
@@ -151,7 +167,7 @@ def test_dispatch_mxfp8_full_size_sampled_rows():
     rows = np.sort(rng.choice(np.nonzero(src >= 0)[0], 256, replace=False))
     codes, scales = oracle.token_rows(inp.x, "mxfp4", src[rows] // cfg.K)
     assert np.array_equal(pool.cpu().numpy()[rows], codes)
-    assert np.array_equal(pool_s.cpu().numpy()[rows], scales)
+    assert np.array_equal(pool_s[rows, : scales.shape[1]], scales)
 
 
 @pytest.mark.parametrize("cfg", [config_by_name("tiny"), MoEConfig("ident", 515, 256, 64, 12, 4, 5, 4, 16)],
