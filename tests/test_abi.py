@@ -66,6 +66,10 @@ def test_workspace_bytes(lib):
     assert full_fp8 - plan_only >= rows * 1536 + rows * 12 * 4
     full_mx = lib.moe_workspace_bytes(16384, 8, 128, 128, 0, 1536, 2)
     assert full_mx - plan_only >= rows * 1536 + rows * 48
+    # mxfp4 h scales are ceil(I/128) 4-byte words per row (tile-major): I = 160 needs 8 bytes a row
+    r16 = oracle.pool_rows_bound(16, 2, 4, 16)
+    assert lib.moe_workspace_bytes(16, 2, 4, 16, 0, 160, 2) - lib.moe_workspace_bytes(16, 2, 4, 16, 0, 0, 0) >= \
+        r16 * 160 + r16 * 8
     assert lib.moe_workspace_bytes(16, 2, 4, 16, 0, 100, 1) == 0     # fp8 needs I % 128 == 0
     assert lib.moe_workspace_bytes(16, 2, 4, 16, 0, 48, 2) == 0      # mxfp4 needs I % 32 == 0
     assert lib.moe_workspace_bytes(16, 2, 4, 16, 0, 64, 7) == 0      # unknown dtype
