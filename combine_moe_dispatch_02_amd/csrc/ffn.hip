@@ -1731,7 +1731,7 @@ int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream
   a.bs_expert = (int64_t)(2 * I / 128) * (H / 128);
   a.out_groups = I / 128;
   a.wait_ready = 1;
-  a.unit_order = bn_a == 512 ? (f.unit_order ? f.unit_order : 3) : 1;
+  a.unit_order = bn_a == 512 ? (f.unit_order ? f.unit_order : mx ? 1 : 3) : 1;   // mxfp4: tiles then N blocks measured 1% faster
   int grid = f.workgroups > 0 ? f.workgroups : device_cu_count();
   if (grid <= 0) return MOE_ERR_HIP;
   int ga = (int)std::min<int64_t>(grid, (int64_t)ntiles_cap * a.n_units);
@@ -1767,7 +1767,7 @@ int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream
   a.bs_ld = I / 128;
   a.bs_expert = (int64_t)(H / 128) * (I / 128);
   a.wait_ready = 0;
-  a.unit_order = bn_y == 512 ? (f.unit_order ? f.unit_order : 3) : 1;
+  a.unit_order = bn_y == 512 ? (f.unit_order ? f.unit_order : mx ? 1 : 3) : 1;
   int gy = (int)std::min<int64_t>(grid, (int64_t)ntiles_cap * a.n_units);
   if (gy < 1) gy = 1;
   if (fuse) {

@@ -108,7 +108,8 @@ typedef struct moe_tile_config {
   int32_t gemm_workgroups;  /* persistent GEMM grid size (0 = one per CU) */
   uint32_t spin_timeout_us; /* bound on one ready-flag wait (0 = 2 000 000 us) */
   int32_t unit_order;       /* work-unit walk: 1 = pool tile major, 2 = expert, N block, tile,
-                               k = 3..9: expert, group of k-1 N blocks, tile (0 = auto) */
+                               k = 3..9: expert, group of k-1 N blocks, tile (0 = auto: 3 on
+                               the big-tile kernel, 1 for mxfp4 and on the general kernel) */
   int32_t weight_layout;    /* MOE_WEIGHTS_ROW_MAJOR or MOE_WEIGHTS_MFMA_TILED (w1 and w2) */
   int32_t a_stages;         /* pool-row pipeline of the big-tile GEMMs: 4 = a ring of four LDS
                                stages three K steps ahead (bf16 and mxfp4, K steps % 4 == 0),
