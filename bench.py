@@ -30,13 +30,18 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+FFN_SOURCES = ("ffn.hip", "ffn_sq.hip")
+
+
 def kernel_source_hash() -> str:
-    """Hash of the FFN kernel source, comments and blank lines left out: counter readings
+    """Hash of the FFN kernel sources, comments and blank lines left out: counter readings
     in profiles/ are valid only for the code they were taken on."""
     import re
 
-    p = os.path.join(ROOT, "combine_moe_dispatch_02_amd", "csrc", "ffn.hip")
-    code = [re.sub(r"//.*$", "", ln).rstrip() for ln in open(p).read().splitlines()]
+    code = []
+    for name in FFN_SOURCES:
+        p = os.path.join(ROOT, "combine_moe_dispatch_02_amd", "csrc", name)
+        code += [re.sub(r"//.*$", "", ln).rstrip() for ln in open(p).read().splitlines()]
     return hashlib.sha256("\n".join(ln for ln in code if ln).encode()).hexdigest()[:16]
 
 
@@ -288,6 +293,10 @@ def main():
     ap.add_argument("--block-n", type=int, default=0, help="tile config override: N block (0 = auto)")
     ap.add_argument("--gemm-wgs", type=int, default=0, help="tile config override: GEMM grid (0 = auto)")
     ap.add_argument("--unit-order", type=int, default=0, help="tile config override: unit walk (0 = auto)")
+    ap.add_argument("--unit-rows", type=int, default=0,
+                    help="tile config override: rows per GEMM work unit (0 = auto, 128, 256)")
+    ap.add_argument("--dispatch-cus", type=int, default=0,
+                    help="tile config override: CUs GEMM A leaves to a concurrent dispatch (0 = auto)")
     ap.add_argument("--a-stages", type=int, default=0,
                     help="tile config override: pool-row pipeline depth of the big-tile GEMMs (0 = auto, 2, 4)")
     ap.add_argument("--cpu-sample", type=int, default=512, help="tokens of the oracle CPU baseline (0 = skip)")
@@ -339,8 +348,9 @@ def main():
         w1, w2, w1s, w2s = inp.w1.to(dev), inp.w2.to(dev), None, None
     torch.cuda.synchronize()
     tcfg = None
-    if args.block_n or args.gemm_wgs or args.unit_order or args.a_stages:
-        tcfg = moe.TileConfig(args.block_n, args.gemm_wgs, 0, args.unit_order, 0, args.a_stages)
+    if args.block_n or args.gemm_wgs or args.unit_order or args.a_stages or args.unit_rows or args.dispatch_cus:
+        tcfg = moe.TileConfig(args.block_n, args.gemm_wgs, 0, args.unit_order, 0, args.a_stages,
+                              args.dispatch_cus, args.unit_rows)
     layer = moe.StreamMoE(cfg.T, cfg.H, cfg.I, cfg.K, cfg.num_local_experts,
                           expert_begin=cfg.expert_begin, tile=cfg.tile, dtype=cfg.dtype, cfg=tcfg,
                           combine_on_completion=args.combine_on_completion)

@@ -61,6 +61,8 @@ class TileConfig(ctypes.Structure):
         ("unit_order", ctypes.c_int32),
         ("weight_layout", ctypes.c_int32),
         ("a_stages", ctypes.c_int32),
+        ("dispatch_cus", ctypes.c_int32),
+        ("unit_rows", ctypes.c_int32),
     ]
 
 

@@ -93,6 +93,9 @@ MOE355_API int moe_dispatch(const void* x, int32_t H, int32_t act_dtype, const m
   } else {
     return MOE_ERR_INVALID;
   }
+  // scale words are tile-major: a row of a partial last tile would address a word past
+  // pool_rows * groups, so a scaled pool must hold whole tiles
+  if (pool_s && pool_rows % plan->tile != 0) return MOE_ERR_INVALID;
   if (H % 8 != 0) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)H * 2 > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
   const WsLayout L = ws_layout(plan->T, plan->K, plan->E_local, plan->tile, 0, 0, MOE_BF16);
@@ -121,7 +124,8 @@ static int expert_ffn(const moe_plan_t* plan, int32_t pool_rows, const void* poo
   const int32_t block_n = cfg ? cfg->block_n : 0;
   const int32_t layout = cfg ? cfg->weight_layout : MOE_WEIGHTS_ROW_MAJOR;
   if (layout != MOE_WEIGHTS_ROW_MAJOR && layout != MOE_WEIGHTS_MFMA_TILED) return MOE_ERR_INVALID;
-  rc = ffn_supported(H, I, dtype, plan->tile, block_n, layout);
+  const int32_t unit_rows = cfg ? cfg->unit_rows : 0;
+  rc = ffn_supported(H, I, dtype, plan->tile, block_n, layout, unit_rows, out != nullptr);
   if (rc != MOE_OK) return rc;
   if ((int64_t)pool_rows * H * 2 > ((int64_t)1 << 40)) return MOE_ERR_UNSUPPORTED;
   const WsLayout L = ws_layout(plan->T, plan->K, plan->E_local, plan->tile, pool_rows, I, dtype);
@@ -151,6 +155,9 @@ static int expert_ffn(const moe_plan_t* plan, int32_t pool_rows, const void* poo
   f.weight_layout = layout;
   f.a_stages = cfg ? cfg->a_stages : 0;
   if (f.a_stages != 0 && f.a_stages != 2 && f.a_stages != 4) return MOE_ERR_INVALID;
+  f.dispatch_cus = cfg ? cfg->dispatch_cus : 0;
+  if (f.dispatch_cus < 0) return MOE_ERR_INVALID;
+  f.unit_rows = unit_rows;
   if (f.unit_order < 0 || f.unit_order > 9) return MOE_ERR_INVALID;
   const uint64_t us = (cfg && cfg->spin_timeout_us) ? cfg->spin_timeout_us : 2000000u;
   f.timeout_ticks = us * 100u;  // s_memrealtime counts at 100 MHz

@@ -171,7 +171,6 @@ typedef float wg_f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) wg_bf16x4 wg_lds_bf16x4;
 
 // byte of (row, byte b of the row) in a step's operand tile (512-byte rows)
-__device__ inline void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0) only
 
 // A transposing read touches 16 rows (8g + q and, for the second half, 8g + 4 + q; g, q
 // = 0..3) at one 32-byte column segment; rows are 512 bytes apart, so the segment is moved

@@ -23,6 +23,8 @@ inline int32_t plan_pairs_per_wave(int64_t pairs) {
 struct WsLayout {
   size_t err = 0;        // uint32: first device error code (0 = none)
   size_t done = 64;      // uint32: plan blocks finished (reset by the last one)
+  size_t abort = 128;    // uint32: epoch of the last FFN call whose ready-flag wait timed out
+  size_t tiles_done = 192;  // uint32: tiles whose ready flag dispatch has raised (plan zeroes it)
   size_t hist = 256;     // int32 [ncols][E_local]: per-wave expert counts, then bases
   size_t fill = 0;       // uint32 [ntiles_cap]: rows stored per tile by dispatch
   size_t ydone = 0;      // uint32 [ntiles_cap]: GEMM Y units finished per tile (combine on completion)
@@ -191,6 +193,22 @@ __device__ inline int mx_e4m3_shared_exp(float amax) {
 // 2^-e for a shared exponent of mx_e4m3_shared_exp (-e <= 127, and e <= 119 keeps it
 // normal): multiplying by it is exact, so the codes equal those of x / 2^e
 __device__ inline float mx_inv_scale(int e) { return __builtin_amdgcn_ldexpf(1.0f, -e); }
+
+// --------------------------------------------------------------------------
+// persistent grids and wait counters
+// --------------------------------------------------------------------------
+// Workgroup g of a persistent grid of G runs on XCD g % 8 (the dispatcher deals
+// workgroups to the XCDs round-robin); slot(g) gives each XCD a contiguous run of
+// G/8 work units per round, so units that share operands share that XCD's L2.
+__device__ inline int unit_slot(int g, int G) { return (G & 7) == 0 ? (g & 7) * (G >> 3) + (g >> 3) : g; }
+
+// s_waitcnt vmcnt(0), the other counters left alone (LDS-DMA loads have no
+// register result for the compiler to wait on)
+__device__ inline void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(n) (n < 64), the other counters left alone
+constexpr int vmcnt_enc(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+// s_waitcnt lgkmcnt(0), the other counters left alone
+constexpr int kLgkm0 = 0xC07F;
 
 // --------------------------------------------------------------------------
 // buffer resources: hardware range checks (out-of-range loads read 0, stores drop)

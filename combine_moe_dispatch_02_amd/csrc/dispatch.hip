@@ -39,6 +39,7 @@ struct DispatchArgs {
   int32_t pool_rows;
   uint32_t* tile_fill;
   uint32_t* tile_ready;
+  uint32_t* tiles_done;     // count of raised flags: equal to num_tiles once every tile is in
   uint32_t epoch;
   uint32_t* err;
   int32_t tokens_per_wave;  // tokens_per_wave * K <= 64
@@ -186,6 +187,7 @@ __global__ __launch_bounds__(64 * WPB) void dispatch_kernel(DispatchArgs a) {
       if ((int)old + 1 == real) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         __hip_atomic_store(&a.tile_ready[ti], a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(a.tiles_done, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
@@ -232,6 +234,7 @@ int launch_dispatch(const void* x, int32_t H, int32_t dtype, const moe_plan_t& p
   a.pool_rows = pool_rows;
   a.tile_fill = reinterpret_cast<uint32_t*>(ws + L.fill);
   a.tile_ready = p.tile_ready;
+  a.tiles_done = reinterpret_cast<uint32_t*>(ws + L.tiles_done);
   a.epoch = epoch;
   a.err = reinterpret_cast<uint32_t*>(ws + L.err);
   const int nch = H / 8;

@@ -78,6 +78,7 @@ struct FfnArgs {
   const uint32_t* tile_ready;
   uint32_t epoch;
   uint32_t* err;
+  uint32_t* abort_epoch;     // epoch of a call whose ready-flag wait timed out (its other waits end)
   uint64_t timeout;
   int32_t wait_ready;
   const uint8_t* A_e8;       // mxfp4: activation E8M0 scales, tile-major 4-byte words
@@ -145,17 +146,23 @@ __device__ inline void unit_coords(const FfnArgs& a, int u, int order, int& m, i
   }
 }
 
-__device__ inline int unit_slot(int g, int G) { return (G & 7) == 0 ? (g & 7) * (G >> 3) + (g >> 3) : g; }
 
-// wait until tile m's ready flag equals the epoch; false when the unit is skipped
+// wait until tile m's ready flag equals the epoch; false when the unit is skipped.
+// A wait that times out records MOE_ERR_TIMEOUT and marks this call's epoch aborted,
+// which ends the other waits of the same call at once; a later call (another epoch)
+// is not affected by it, whether or not the error word has been read since.
 __device__ inline bool wait_tile_ready(const FfnArgs& a, int m, int* s_go) {
   if (threadIdx.x == 0) {
     int go = 1;
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     while (__hip_atomic_load(&a.tile_ready[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.epoch) {
-      if (load_error(a.err) != 0) { go = 0; break; }
+      if (__hip_atomic_load(a.abort_epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch) {
+        go = 0;
+        break;
+      }
       if (__builtin_amdgcn_s_memrealtime() - t0 > a.timeout) {
         record_error(a.err, MOE_ERR_TIMEOUT);
+        __hip_atomic_store(a.abort_epoch, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         go = 0;
         break;
       }
@@ -517,13 +524,6 @@ __device__ inline void combine_tail(const FfnArgs& a, int* s_item) {
   }
 }
 
-// s_waitcnt vmcnt(0), the other counters left alone (LDS-DMA loads have no
-// register result for the compiler to wait on)
-__device__ inline void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-// s_waitcnt vmcnt(n) (n < 64), the other counters left alone
-constexpr int vmcnt_enc(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
-// s_waitcnt lgkmcnt(0), the other counters left alone
-constexpr int kLgkm0 = 0xC07F;
 
 __device__ inline uint32_t swz_a(int r, int c) {
   // 8 consecutive rows reading one chunk column hit 8 distinct 16-byte bank groups
@@ -1544,8 +1544,24 @@ bool ffn_train_ok(int32_t H, int32_t I, int32_t dtype, int32_t tile, int32_t blo
          H % 512 == 0 && (block_n == 0 || block_n == 512);
 }
 
-int ffn_supported(int32_t H, int32_t I, int32_t dtype, int32_t tile, int32_t block_n, int32_t weight_layout) {
+// 256 x 256 units (ffn_sq.hip): bf16 with tiled weights at tile 128; K stages of 32 in
+// whole rounds of four (H, I % 128) and whole 256-column N blocks (2I, H % 256); 32-bit
+// buffer offsets over a unit's rows and an expert's weights
+bool ffn_sq_ok(int32_t H, int32_t I, int32_t dtype, int32_t tile, int32_t block_n, int32_t weight_layout,
+               bool combine) {
+  return dtype == MOE_BF16 && tile == 128 && weight_layout == MOE_WEIGHTS_MFMA_TILED && !combine &&
+         (block_n == 0 || block_n == 512) && H % 256 == 0 && I % 128 == 0 &&
+         (int64_t)2 * I * H * 2 < ((int64_t)1 << 32) && (int64_t)256 * std::max(H, I) * 2 < ((int64_t)1 << 31);
+}
+
+int ffn_supported(int32_t H, int32_t I, int32_t dtype, int32_t tile, int32_t block_n, int32_t weight_layout,
+                  int32_t unit_rows, bool combine) {
   if (block_n != 0 && block_n != 128 && block_n != 256 && block_n != 512) return MOE_ERR_INVALID;
+  if (unit_rows != 0 && unit_rows != 128 && unit_rows != 256) return MOE_ERR_INVALID;
+  const bool sq = ffn_sq_ok(H, I, dtype, tile, block_n, weight_layout, combine);
+  if (unit_rows == 256 && !sq) return MOE_ERR_UNSUPPORTED;
+  // tiled bf16 weights on shapes only the 256 x 256 kernel takes
+  if (sq && unit_rows != 128) return MOE_OK;
   const bool big_a = big_a_ok(H, I, dtype, tile);
   const bool big_y = big_y_ok(H, I, dtype, tile);
   // fp8 on the big-tile kernel needs tiled weights
@@ -1691,6 +1707,7 @@ int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream
   a.tile_ready = p.tile_ready;
   a.epoch = f.epoch;
   a.err = reinterpret_cast<uint32_t*>(ws + L.err);
+  a.abort_epoch = reinterpret_cast<uint32_t*>(ws + L.abort);
   a.timeout = f.timeout_ticks;
   a.a_stages = f.a_stages;
   if (f.g_pool != nullptr) {
@@ -1706,6 +1723,63 @@ int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream
     a.T = p.T;
     a.K = p.K;
     a.pool_rows = f.pool_rows;
+  }
+
+  // 256-row units when asked for, or when only they take the shape (tiled weights with
+  // I % 256 != 0); the 128 x 512 units otherwise
+  const bool sq_shape = ffn_sq_ok(H, I, f.dtype, tile, f.block_n, f.weight_layout, f.comb_out != nullptr);
+  const bool sq = sq_shape && (f.unit_rows == 256 || (f.unit_rows == 0 && !(big_a_ok(H, I, f.dtype, tile) &&
+                                                                           big_y_ok(H, I, f.dtype, tile))));
+  if (sq) {
+    int grid = f.workgroups > 0 ? f.workgroups : device_cu_count();
+    if (grid <= 0) return MOE_ERR_HIP;
+    SqArgs q{};
+    q.n_experts = p.E_local;
+    q.max_tiles = f.pool_rows / 128;
+    q.group = f.unit_order > 0 ? f.unit_order : 4;
+    q.offsets = p.offsets;
+    q.num_tiles = p.num_tiles;
+    q.tile_ready = p.tile_ready;
+    q.tiles_done = reinterpret_cast<const uint32_t*>(ws + L.tiles_done);
+    q.epoch = f.epoch;
+    q.err = reinterpret_cast<uint32_t*>(ws + L.err);
+    q.abort_epoch = reinterpret_cast<uint32_t*>(ws + L.abort);
+    q.timeout = f.timeout_ticks;
+    // at most this many tile pairs (the tiles plus one odd tile per expert)
+    const int64_t pairs_cap = (int64_t)ntiles_cap / 2 + p.E_local;
+    // GEMM A: pool x w1^T -> SwiGLU -> h (and G when training)
+    q.A = static_cast<const uint8_t*>(f.pool);
+    q.lda = (int64_t)H * 2;
+    q.B = static_cast<const uint8_t*>(f.w1);
+    q.b_expert = (int64_t)2 * I * H * 2;
+    q.ktiles = H / 32;
+    q.out = h;
+    q.ldo = (int64_t)I * 2;
+    q.g_save = static_cast<uint8_t*>(f.g_pool);
+    q.g_ld = (int64_t)4 * I;
+    q.g_up = 2 * I;
+    q.KS = H / 32;
+    q.NB = 2 * I / 256;
+    q.up_rb = I / 16;
+    q.wait_ready = 1;
+    int ga = (int)std::min<int64_t>(std::max(1, grid - f.dispatch_cus), pairs_cap * q.NB);
+    int rc = launch_ffn_sq(q, std::max(1, ga), true, f.g_pool != nullptr, stream);
+    if (rc != MOE_OK) return rc;
+    // GEMM Y: h x w2^T -> y_pool (same stream, so every h row is complete)
+    q.A = h;
+    q.lda = (int64_t)I * 2;
+    q.B = static_cast<const uint8_t*>(f.w2);
+    q.b_expert = (int64_t)H * I * 2;
+    q.ktiles = I / 32;
+    q.out = static_cast<uint8_t*>(f.y_pool);
+    q.ldo = (int64_t)H * 2;
+    q.g_save = nullptr;
+    q.KS = I / 32;
+    q.NB = H / 256;
+    q.up_rb = 0;
+    q.wait_ready = 0;
+    int gy = (int)std::min<int64_t>(grid, pairs_cap * q.NB);
+    return launch_ffn_sq(q, std::max(1, gy), false, false, stream);
   }
 
   // GEMM A: pool x w1^T -> SwiGLU -> h
@@ -1734,7 +1808,9 @@ int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream
   a.unit_order = bn_a == 512 ? (f.unit_order ? f.unit_order : mx ? 1 : 3) : 1;   // mxfp4: tiles then N blocks measured 1% faster
   int grid = f.workgroups > 0 ? f.workgroups : device_cu_count();
   if (grid <= 0) return MOE_ERR_HIP;
-  int ga = (int)std::min<int64_t>(grid, (int64_t)ntiles_cap * a.n_units);
+  // GEMM A waits on flags that a concurrent dispatch raises: its persistent grid leaves
+  // dispatch_cus CUs free (one workgroup fills a CU), so that dispatch can always run
+  int ga = (int)std::min<int64_t>(std::max(1, grid - f.dispatch_cus), (int64_t)ntiles_cap * a.n_units);
   if (ga < 1) ga = 1;
   const bool packed = f.weight_layout == MOE_WEIGHTS_MFMA_TILED;
   a.ktiles = H / (fp8 || mx ? 128 : 32);
@@ -1805,6 +1881,7 @@ int launch_ffn_dgrad(const moe_plan_t& p, int32_t pool_rows, const void* A, cons
   a.tile_expert = p.tile_expert;
   a.tile_ready = p.tile_ready;
   a.err = reinterpret_cast<uint32_t*>(ws + L.err);
+  a.abort_epoch = reinterpret_cast<uint32_t*>(ws + L.abort);
   a.A = static_cast<const uint8_t*>(A);
   a.B = static_cast<const uint8_t*>(Bt);
   a.out = static_cast<uint8_t*>(out);

@@ -50,6 +50,7 @@ struct PlanArgs {
   uint32_t* tile_fill;
   int32_t* hist;
   uint32_t* done;
+  uint32_t* tiles_done;   // dispatch's count of raised ready flags
 };
 
 // One wave's walk over its column. COUNT_ONLY: accumulate counts in run[];
@@ -192,6 +193,7 @@ __device__ void plan_scan(const PlanArgs& a, int* s_cnt, int* s_off, int* s_half
   // a fresh start for the dispatch that follows
   for (int t = tid; t < a.ntiles_cap; t += 256) a.tile_ready[t] = 0u;
   for (int t = tid; t < a.nfill; t += 256) a.tile_fill[t] = 0u;
+  if (tid == 0) *a.tiles_done = 0u;
 }
 
 __global__ __launch_bounds__(256) void plan_count_kernel(PlanArgs a) {
@@ -272,6 +274,7 @@ int launch_plan(const int32_t* topk_idx, const moe_plan_t& p, const WsLayout& L,
   a.tile_fill = reinterpret_cast<uint32_t*>(ws + L.fill);
   a.hist = reinterpret_cast<int32_t*>(ws + L.hist);
   a.done = reinterpret_cast<uint32_t*>(ws + L.done);
+  a.tiles_done = reinterpret_cast<uint32_t*>(ws + L.tiles_done);
   const int blocks = (L.ncols + kPlanWaves - 1) / kPlanWaves;
   hipLaunchKernelGGL(plan_count_kernel, dim3(blocks), dim3(256), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;

@@ -350,15 +350,19 @@ class StreamMoE:
         # tiled weights feed the big-tile kernel, which needs whole 512-column blocks
         # (bf16: tile 64 or 128; fp8, mxfp4: tile 128); mxfp4 runs there only
         tiles_ok = tile in (64, 128) if self.dtype == "bf16" else tile == 128
-        tiled_ok = (tiles_ok and I % 256 == 0 and H % 512 == 0
-                    and (cfg is None or cfg.block_n in (0, 512)))
+        block_ok = cfg is None or cfg.block_n in (0, 512)
+        tiled_ok = tiles_ok and I % 256 == 0 and H % 512 == 0 and block_ok
+        # the 256 x 256 units take tiled bf16 weights at tile 128 for H % 256, I % 128
+        if (self.dtype == "bf16" and tile == 128 and H % 256 == 0 and I % 128 == 0 and block_ok
+                and not combine_on_completion and (cfg is None or cfg.unit_rows != 128)):
+            tiled_ok = True
         if (weight_layout == "tiled" or self.dtype == "mxfp4") and not tiled_ok:
             raise MoeError("StreamMoE", _abi.MOE_ERR_UNSUPPORTED)
         if self.dtype == "mxfp4" and weight_layout == "row_major":
             raise MoeError("StreamMoE", _abi.MOE_ERR_UNSUPPORTED)
         self.tiled = weight_layout == "tiled" or (weight_layout == "auto" and tiled_ok)
         if cfg is None:
-            cfg = TileConfig(0, 0, 0, 0, 0)
+            cfg = TileConfig(0, 0, 0, 0, 0, 0, 0)
         cfg.weight_layout = MOE_WEIGHTS_MFMA_TILED if self.tiled else MOE_WEIGHTS_ROW_MAJOR
         self.cfg = cfg
         self.plan = Plan.allocate(T, K, expert_begin, num_local_experts, tile, device)
@@ -416,6 +420,28 @@ class StreamMoE:
         moe_dispatch_backward(self.dx_pool, self.plan, self.dx, s)
         return self.dx, self.dw, dw1, dw2
 
+    def check_errors(self, stream=None) -> None:
+        """Wait for ``stream`` and raise MoeError if the device recorded an error since the last
+        check (a ready-flag wait that timed out, a pool too small for the plan). forward() is
+        asynchronous and does not synchronise, so device errors surface only here (or through
+        moe_get_error); the error word is cleared by reading it."""
+        rc = moe_get_error(self.ws, stream)
+        if rc != 0:
+            raise MoeError("device", rc)
+
+    def _concurrent_cfg(self) -> TileConfig:
+        """The tile config of an FFN that runs while dispatch may still be running on another
+        stream: GEMM A's persistent grid leaves CUs free for dispatch (one GEMM workgroup fills a
+        CU), so that GEMM A's waits for tiles always end. One eighth of the CUs unless the
+        caller's config sets dispatch_cus."""
+        c = self.cfg
+        if c.dispatch_cus > 0:
+            return c
+        if getattr(self, "_ccfg", None) is None:
+            self._ccfg = TileConfig(c.block_n, c.gemm_workgroups, c.spin_timeout_us, c.unit_order,
+                                    c.weight_layout, c.a_stages, max(1, device_cu_count() // 8))
+        return self._ccfg
+
     def next_epoch(self) -> int:
         self.epoch = (self.epoch % 0xFFFFFFFF) + 1      # 1 .. 2^32-1; 0 is never a valid epoch
         return self.epoch
@@ -423,8 +449,10 @@ class StreamMoE:
     def forward(self, x, topk_idx, topk_weights, w1, w2, w1_scale=None, w2_scale=None,
                 streams=None) -> torch.Tensor:
         """One layer. Weights and scales come from prepare_weights(). ``streams=(compute, comm)`` runs
-        plan/dispatch/combine on comm and the FFN on compute, ordered by events; None runs
-        everything on the current stream."""
+        plan/dispatch/combine on comm and the FFN on compute, ordered by events, with GEMM A
+        claiming pool tiles as dispatch raises their flags (its grid then leaves CUs free for
+        dispatch); None runs everything on the current stream. Asynchronous: device errors are
+        reported by check_errors()."""
         if topk_idx.dtype != torch.int32:
             topk_idx = topk_idx.to(torch.int32)
         epoch = self.next_epoch()
@@ -452,19 +480,20 @@ class StreamMoE:
         planned.record(comm)
         moe_dispatch(x, self.plan, self.pool, self.pool_s, epoch, self.ws, self.dtype, comm)
         compute.wait_event(planned)
+        ccfg = self._concurrent_cfg()
         if self.combine_on_completion:
             compute.wait_stream(cur)       # topk_weights and out belong to the caller's stream
             moe_expert_ffn_combine(self.plan, self.pool, self.pool_s, w1, w1_scale, w2, w2_scale, epoch,
-                                   self.ws, self.y_pool, topk_weights, self.out, self.dtype, self.cfg, compute)
+                                   self.ws, self.y_pool, topk_weights, self.out, self.dtype, ccfg, compute)
             cur.wait_stream(compute)
             cur.wait_stream(comm)
             return self.out
         if self.train:
             moe_expert_ffn_train(self.plan, self.pool, w1, w2, epoch, self.ws, self.y_pool, self.g_pool,
-                                 self.cfg, compute)
+                                 ccfg, compute)
         else:
             moe_expert_ffn(self.plan, self.pool, self.pool_s, w1, w1_scale, w2, w2_scale, epoch,
-                           self.ws, self.y_pool, self.dtype, self.cfg, compute)
+                           self.ws, self.y_pool, self.dtype, ccfg, compute)
         done = torch.cuda.Event()
         done.record(compute)
         comm.wait_event(done)

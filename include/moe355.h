@@ -114,6 +114,19 @@ typedef struct moe_tile_config {
   int32_t a_stages;         /* pool-row pipeline of the big-tile GEMMs: 4 = a ring of four LDS
                                stages three K steps ahead (bf16 and mxfp4, K steps % 4 == 0),
                                2 = two stages; 0 = auto (4 where available). Same results. */
+  int32_t dispatch_cus;     /* CUs that GEMM A's persistent grid leaves free, so that a
+                               moe_dispatch running at the same time on another stream always
+                               has CUs to run on while GEMM A waits for its tiles (0 = none:
+                               right when dispatch has finished before the FFN starts, e.g. on
+                               the same stream). GEMM A's grid is then the grid size minus this
+                               (at least 1); GEMM Y is not affected. Same results. */
+  int32_t unit_rows;        /* rows of a GEMM work unit: 128 = one pool tile (128 x 512 units),
+                               256 = two pool tiles of one expert (256 x 256 units, both operands
+                               by LDS-DMA; bf16, tiled weights, tile 128, H % 256 == 0,
+                               I % 128 == 0, not with combine on completion); 0 = auto (128
+                               where the 128 x 512 kernel takes the shape, else 256). With 256,
+                               unit_order k >= 1 walks each expert in groups of k tile pairs
+                               (0 = auto). Same results. */
 } moe_tile_config;
 
 /* Host-only size helpers (no device access). */
@@ -170,7 +183,8 @@ MOE355_API int moe_query_pool_rows(const moe_plan_t* plan, int32_t* host_P, void
  * tile_ready entry is set to `epoch` with release ordering (device scope).
  * epoch must be nonzero and should change from one layer call to the next.
  * A pair whose row is >= pool_rows is not written and records MOE_ERR_INVALID.
- * Errors: MOE_ERR_INVALID (null pointers, H < 8, epoch 0, bad dtype),
+ * Errors: MOE_ERR_INVALID (null pointers, H < 8, epoch 0, bad dtype; fp8 and
+ * mxfp4 with pool_rows % tile != 0, since a row of a partial tile has no scale word),
  * MOE_ERR_UNSUPPORTED (H % 8 != 0; fp8 with H % 128 != 0; mxfp4 with H % 32 != 0).
  */
 MOE355_API int moe_dispatch(const void* x, int32_t H, int32_t act_dtype, const moe_plan_t* plan,

@@ -33,14 +33,23 @@ E2M1_EMAX = 2
 E4M3_EMAX = 8
 
 
-def e2m1_decode(codes) -> np.ndarray:
-    """FP4 E2M1 codes (low 4 bits of each entry) -> float64, from the bit fields."""
-    c = np.asarray(codes).astype(np.int64) & 0xF
+def _e2m1_from_fields(c: np.ndarray) -> np.ndarray:
+    """FP4 E2M1 codes 0..15 -> float64, from the bit fields."""
     s = (c >> 3) & 1
     e = (c >> 1) & 3
     m = c & 1
     mag = np.where(e == 0, m * 0.5, (1.0 + 0.5 * m) * np.exp2(e - 1.0))
     return np.where(s == 1, -mag, mag)
+
+
+# the 16 values, each decoded once from its bit fields
+_E2M1_VALUES = _e2m1_from_fields(np.arange(16, dtype=np.int64))
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    """FP4 E2M1 codes (low 4 bits of each entry) -> float64: the bit-field decoding of
+    each of the 16 codes, looked up per element."""
+    return _E2M1_VALUES[np.asarray(codes).astype(np.intp) & 0xF]
 
 
 def e8m0_decode(b) -> np.ndarray:

@@ -68,3 +68,24 @@ def out_rows_f64(out, rows=None):
 
 def rel_err(got, ref):
     return oracle.max_norm_rel_err(got, ref)
+
+
+def tile_covering_tokens(cfg, inp, p, extra=()):
+    """Tokens to compare at full size: for every pool tile, the token of its last real row
+    (so every tile, and with it every work unit of both GEMMs, has a compared pair), plus the
+    first and last token, a token with no local pair and any ``extra``."""
+    src = np.asarray(p.src[:p.P]).reshape(-1, cfg.tile)
+    pick = set(int(t) for t in extra) | {0, cfg.T - 1}
+    for row in src:
+        real = row[row >= 0]
+        if real.size:
+            pick.add(int(real[-1]) // cfg.K)
+    idx = inp.topk_idx.numpy()
+    local = (idx >= cfg.expert_begin) & (idx < cfg.expert_begin + cfg.num_local_experts)
+    if (~local.any(axis=1)).any():
+        pick.add(int(np.nonzero(~local.any(axis=1))[0][0]))
+    pick.add(int(local.sum(axis=1).argmax()))
+    toks = np.array(sorted(pick))
+    covered = {int(q) // cfg.tile for t in toks for q in p.pos.reshape(cfg.T, cfg.K)[t] if q >= 0}
+    assert covered == set(range(p.num_tiles)), "sample misses a tile"
+    return toks

@@ -127,6 +127,13 @@ def test_dispatch_validation(lib):
     # mxfp4: needs its E8M0 buffer and whole 32-wide blocks
     assert lib.moe_dispatch(X, 128, 2, ctypes.byref(p), 248, POOL, None, 1, WS, big, None) == 1
     assert lib.moe_dispatch(X, 136, 2, ctypes.byref(p), 248, POOL, ctypes.c_void_p(8), 1, WS, big, None) == 2
+    # scaled pools hold whole tiles (tile 16 here): their scale words are tile-major, and a row
+    # of a partial last tile would address a word past the buffer
+    for dt in (1, 2):
+        assert lib.moe_dispatch(X, 128, dt, ctypes.byref(p), 200, POOL, ctypes.c_void_p(8), 1, WS, big,
+                                None) == _abi.MOE_ERR_INVALID
+    # a bf16 pool of any row count is fine for the checks (it has no scale words)
+    assert lib.moe_dispatch(X, 100, 0, ctypes.byref(p), 200, POOL, None, 1, WS, big, None) == 2
 
 
 def test_ffn_validation(lib):
@@ -166,6 +173,33 @@ def test_ffn_validation(lib):
     assert call(dtype=2, scales=mx) == 2           # mxfp4 runs on tiled weights only
     tiled = _abi.TileConfig(0, 0, 0, 0, 1)
     assert call(H=512, I=256, dtype=2, scales=mx, cfg=ctypes.byref(tiled)) == 2   # tile 128 only
+    cfg = _abi.TileConfig(0, 0, 0, 0, 0, 0, -1)
+    assert call(cfg=ctypes.byref(cfg)) == 1        # negative dispatch_cus
+    cfg = _abi.TileConfig(0, 0, 0, 0, 0, 0, 0, 64)
+    assert call(cfg=ctypes.byref(cfg)) == 1        # unit rows are 128 or 256
+    cfg = _abi.TileConfig(0, 0, 0, 0, 1, 0, 0, 256)
+    assert call(cfg=ctypes.byref(cfg)) == 2        # 256-row units: tile 128 only (this plan has 16)
+
+
+def test_ffn_unit_rows_validation(lib):
+    # the 256 x 256 units: bf16, tiled weights, tile 128, H % 256, I % 128, no combine on completion
+    p = _fake_plan(T=64, K=2, E_local=8, tile=128, rows_cap=oracle.pool_rows_bound(64, 2, 8, 128))
+    v = [ctypes.c_void_p(a) for a in range(0x10000, 0x10000 * 9, 0x10000)]
+    POOL, W1, W2, WS, Y = v[:5]
+
+    def call(H, I, rows, layout):
+        cfg = _abi.TileConfig(0, 0, 0, 0, layout, 0, 0, rows)
+        return lib.moe_expert_ffn(ctypes.byref(p), 1152, POOL, None, W1, None, W2, None, H, I, 0, 1, WS, 1 << 40,
+                                  Y, ctypes.byref(cfg), None)
+
+    assert call(640, 384, 256, 1) == 2             # H % 256
+    assert call(1024, 448, 256, 1) == 2            # I % 128
+    assert call(1024, 384, 256, 0) == 2            # row-major weights
+    # I = 384 with tiled weights has no 128 x 512 kernel (I % 256): only the 256-row units take it
+    assert call(1024, 384, 128, 1) == 2
+    cfg = _abi.TileConfig(0, 0, 0, 0, 1, 0, 0, 256)
+    assert lib.moe_expert_ffn_combine(ctypes.byref(p), 1152, POOL, None, W1, None, W2, None, 1024, 512, 0, 1, WS,
+                                      1 << 40, Y, v[5], v[6], ctypes.byref(cfg), None) == 2   # not with combine
 
 
 def test_ffn_combine_validation(lib):

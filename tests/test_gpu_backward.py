@@ -62,10 +62,21 @@ def test_pack_transposed_exact(shape):
     assert np.array_equal(got.cpu().view(torch.int16).numpy(), expected_t(w.numpy()))
 
 
-def _train_run(cfg, seed=None, tile_cfg=None):
+def _poison(t):
+    t.view(torch.uint8).fill_(0xFF)          # NaN as bf16 and fp32
+
+
+def _train_run(cfg, seed=None, tile_cfg=None, poison=False):
     inp = make_inputs(cfg) if seed is None else make_inputs(cfg, seed)
     d = dev_inputs(inp)
     layer = make_layer(cfg, train=True, cfg=tile_cfg)
+    if poison:
+        # padding rows of every pool-shaped buffer (pool, y / dy, G / dG, dx_pool) and of h hold
+        # NaN; the real rows are all written before they are read
+        for t in (layer.pool, layer.y_pool, layer.g_pool, layer.dx_pool):
+            _poison(t)
+        plan_end = moe.workspace_bytes(cfg.T, cfg.K, cfg.num_local_experts, cfg.tile, layer.pool_rows, 0, "bf16")
+        layer.ws.buf[plan_end:].fill_(0xFF)
     w1, w2, _, _ = layer.prepare_weights(d["w1"], d["w2"])
     w1t, w2t = layer.prepare_backward_weights(d["w1"], d["w2"])
     out = layer.forward(d["x"], d["idx"], d["w"], w1, w2).clone()
@@ -81,10 +92,16 @@ def _bf(t):
     return oracle.bf16_to_f64(t.cpu())
 
 
-@pytest.mark.parametrize("cfg", CASES, ids=[c.name for c in CASES])
-def test_backward_full_compare(cfg):
-    say("backward", cfg.name)
-    inp, d, layer, out, g_saved, dout, dx, dw, dW1, dW2 = _train_run(cfg)
+@pytest.mark.parametrize("cfg,poison", [(c, False) for c in CASES] + [(CASES[1], True), (CASES[2], True)],
+                         ids=[c.name for c in CASES] + [CASES[1].name + "_poisoned", CASES[2].name + "_poisoned"])
+def test_backward_full_compare(cfg, poison):
+    # poisoned: the padding rows of the pool, y (then dy), G (then dG), dx_pool and h start as
+    # NaN; the weight gradients sum over real rows only, so every result stays finite
+    say("backward", cfg.name, "poisoned" if poison else "")
+    inp, d, layer, out, g_saved, dout, dx, dw, dW1, dW2 = _train_run(cfg, poison=poison)
+    if poison:
+        for t in (out, dx, dw, dW1, dW2):
+            assert bool(torch.isfinite(t.float()).all())
     # the training forward computes the same out as the inference one
     ref_layer = make_layer(cfg)
     ref_out = run_layer(ref_layer, d)

@@ -107,3 +107,47 @@ def test_layer_one_expert_takes_every_pair(dtype):
     err = rel_err(out_rows_f64(out), ref.out)
     print(f"{cfg.name}: max-norm rel err {err:.3e}")
     assert err <= TOL[dtype]
+
+
+POISON = [
+    MoEConfig("poison_bf16", 700, 1024, 512, 9, 1, 6, 4, 128),            # big-tile kernels, EP slice
+    MoEConfig("poison_bf16_t32", 333, 384, 192, 9, 0, 9, 3, 32),          # general kernel
+    MoEConfig("poison_fp8", 700, 1024, 512, 10, 1, 8, 4, 128, "fp8"),
+    MoEConfig("poison_mx", 700, 1024, 768, 10, 1, 8, 4, 128, "mxfp4"),
+]
+
+
+def poison_(t):
+    """Fill with all-ones bytes: NaN as bf16, e4m3 and fp32."""
+    t.view(torch.uint8).fill_(0xFF)
+
+
+def poison_workspace_h(layer):
+    """NaN bytes over h and its scales (the workspace past what plan and dispatch use)."""
+    plan_end = moe.workspace_bytes(layer.T, layer.K, layer.E_local, layer.tile, layer.pool_rows, 0, layer.dtype)
+    layer.ws.buf[plan_end:].fill_(0xFF)
+
+
+@pytest.mark.parametrize("cfg", POISON, ids=[c.name for c in POISON])
+def test_padding_rows_never_reach_the_output(cfg):
+    # padding rows of the pool, of h and of y_pool hold NaN before the call: no output element
+    # may see one (every GEMM output row depends only on its own input row, combine reads real
+    # rows only)
+    inp = make_inputs(cfg)
+    d = dev_inputs(inp)
+    layer = make_layer(cfg)
+    for t in (layer.pool, layer.y_pool) + ((layer.pool_s,) if layer.pool_s is not None else ()):
+        poison_(t)
+    poison_workspace_h(layer)
+    say("poisoned padding", cfg.name)
+    out = run_layer(layer, d)
+    ref = oracle.moe_layer(inp)
+    assert_plan_equal(layer.plan, ref.plan)
+    got = out_rows_f64(out)
+    assert np.isfinite(got).all()
+    assert (layer.plan.offsets[-1].item() % cfg.tile == 0)
+    src = layer.plan.src.cpu().numpy()[: layer.plan.offsets[-1].item()]
+    assert (src < 0).any(), "the case has padding rows"
+    err = rel_err(got, ref.out)
+    print(f"{cfg.name} (poisoned padding): max-norm rel err {err:.3e}")
+    assert err <= TOL[cfg.dtype]

@@ -1,16 +1,22 @@
-"""Per-tile ready flags (StreamEP README, "How it works": dispatch signals each pool
-tile as it fills and the compute kernels claim ready tiles):
+"""Per-tile ready flags (StreamEP README, "How it works", per-tile streaming: dispatch
+marks each pool tile once its rows are in, and GEMM A starts on a tile as soon as it is
+marked):
 * epochs compare by equality, so the counter's wrap from 2^32-1 to 1 is harmless;
 * an FFN whose tiles never become ready ends with MOE_ERR_TIMEOUT instead of hanging
-  (forced from the host: the dispatch that would raise the flags is never enqueued);
-* running dispatch and the FFN on two streams gives the same bits as one stream."""
+  (forced from the host: the dispatch that would raise the flags is never enqueued), and
+  such a timeout does not touch a later call even while its error is still unread;
+* running dispatch and the FFN on two streams, at the default tile config, gives the same
+  bits as one stream, and at full size matches the oracle on every pool tile."""
+import numpy as np
 import pytest
 import torch
 
 import combine_moe_dispatch_02_amd as moe
+import oracle
 from synth import config_by_name, MoEConfig, make_inputs
 
-from _gpu import dev_inputs, make_layer, run_layer, say
+from _gpu import (TOL, assert_plan_equal, dev_inputs, make_layer, out_rows_f64, rel_err, run_layer, say,
+                  tile_covering_tokens)
 
 pytestmark = pytest.mark.gpu
 
@@ -57,16 +63,54 @@ def test_pool_too_small_is_reported():
     assert moe.moe_get_error(layer.ws) == moe.layer._abi.MOE_ERR_INVALID
 
 
+def test_stale_timeout_does_not_touch_a_later_call():
+    # a timed-out call whose error word is not read yet: the next call (a new epoch) must
+    # still compute every unit
+    cfg = MoEConfig("stale", 256, 256, 128, 8, 0, 8, 2, 64)
+    d = dev_inputs(make_inputs(cfg))
+    layer = make_layer(cfg, cfg=moe.TileConfig(0, 0, 2000, 0))
+    say("stale timeout")
+    ref = run_layer(layer, d).clone()
+    moe.moe_plan(d["idx"], layer.plan, layer.ws)
+    moe.moe_expert_ffn(layer.plan, layer.pool, None, d["w1"], None, d["w2"], None, layer.next_epoch(),
+                       layer.ws, layer.y_pool, "bf16", layer.cfg)
+    out = layer.forward(d["x"], d["idx"], d["w"], d["w1"], d["w2"])
+    torch.cuda.synchronize()
+    assert torch.equal(ref.view(torch.int16), out.view(torch.int16))
+    with pytest.raises(moe.MoeError):
+        layer.check_errors()               # the first call's timeout, reported once
+    layer.check_errors()
+
+
 @pytest.mark.parametrize("cfg", [config_by_name("decode"), config_by_name("fp8_weights").with_(name="fp8_4k", T=4096)],
                          ids=["decode", "fp8_4k"])
 def test_two_streams_match_one(cfg):
+    # default tile config: with streams, GEMM A's grid leaves CUs for the concurrent dispatch
     inp = make_inputs(cfg)
     d = dev_inputs(inp)
-    # leave CUs free for the dispatch kernel while the persistent FFN waits on flags
-    cus = moe.device_cu_count()
-    layer = make_layer(cfg, cfg=moe.TileConfig(0, max(1, cus - 32), 0, 0))
+    layer = make_layer(cfg)
     say("streams", cfg.name)
     one = run_layer(layer, d).clone()
     streams = moe.make_streams()
     two = run_layer(layer, d, streams=streams).clone()
     assert torch.equal(one.view(torch.int16), two.view(torch.int16))
+
+
+def test_two_streams_full_size_skew():
+    # the skew workload on two streams at the default config: bitwise the one-stream result,
+    # and within tolerance of the oracle on a pair of every pool tile
+    cfg = config_by_name("zipf_skew")
+    inp = make_inputs(cfg, pin_memory=True)
+    d = dev_inputs(inp)
+    layer = make_layer(cfg)
+    say("streams full size", cfg.name)
+    one = run_layer(layer, d).clone()
+    two = run_layer(layer, d, streams=moe.make_streams()).clone()
+    assert torch.equal(one.view(torch.int16), two.view(torch.int16))
+    p = oracle.plan(inp.topk_idx, cfg.expert_begin, cfg.num_local_experts, cfg.tile)
+    assert_plan_equal(layer.plan, p)
+    toks = tile_covering_tokens(cfg, inp, p)
+    ref = oracle.moe_layer(inp, tokens=toks, p=p)
+    err = rel_err(out_rows_f64(two, toks), ref.out)
+    print(f"two streams, {cfg.name}: {len(toks)} tokens over all {p.num_tiles} tiles, err {err:.3e}")
+    assert err <= TOL[cfg.dtype]
