@@ -1758,7 +1758,7 @@ int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream
     q.g_save = static_cast<uint8_t*>(f.g_pool);
     q.g_ld = (int64_t)4 * I;
     q.g_up = 2 * I;
-    q.KS = H / 32;
+    q.KS = H / 64;
     q.NB = 2 * I / 256;
     q.up_rb = I / 16;
     q.wait_ready = 1;
@@ -1774,7 +1774,7 @@ int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream
     q.out = static_cast<uint8_t*>(f.y_pool);
     q.ldo = (int64_t)H * 2;
     q.g_save = nullptr;
-    q.KS = I / 32;
+    q.KS = I / 64;
     q.NB = H / 256;
     q.up_rb = 0;
     q.wait_ready = 0;

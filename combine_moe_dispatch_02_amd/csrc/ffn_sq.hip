@@ -15,24 +15,26 @@
 // 8 waves: wave w computes rows 128 (w / 4) .. +128 and 64 of the 256 columns
 // (w % 4), i.e. 8 x 4 MFMA tiles, 128 accumulators per lane.
 //
-// Operands. A K stage is 32 values (64 bytes) of every row: 256 pool (or h) rows and
-// 256 weight rows, each block of 16 rows stored in LDS as one 1 KiB MFMA fragment
-// (lane l's 16 bytes = row l % 16, K values 8 (l / 16) .. +8 of the stage). The
-// tiled weight layout already holds exactly these 1 KiB blocks contiguously; the
-// pool rows are gathered into them by the DMA's per-lane source addresses. Each
-// wave moves 4 of the stage's 32 blocks by LDS-DMA (buffer_load ... lds), so no
-// register holds a load in flight, and every fragment read is a contiguous,
-// conflict-free 1 KiB ds_read_b128.
+// Operands. A K stage is 64 values (128 bytes, one cache line) of every row: 256 pool
+// (or h) rows and 256 weight rows, 64 KiB of LDS. The pool rows are stored row by row,
+// their eight 16-byte chunks XOR-permuted by row % 8: the eight lanes of a DMA that
+// fill one row fetch its whole line, and the eight lanes of a fragment read that share
+// a chunk index (eight rows) land on eight distinct 16-byte slots of a 128-byte bank
+// row. The tiled weight layout already holds MFMA fragments as contiguous 1 KiB blocks
+// (lane l's 16 bytes = row l % 16, K values 8 (l / 16) .. +8 of a 32-wide K tile), two
+// per 16 rows and stage, which the DMA copies as they are. Each wave moves 8 of the
+// stage's 64 KiB by LDS-DMA (buffer_load ... lds), so no register holds a load in
+// flight, and every request covers whole cache lines.
 //
-// Pipeline. A ring of four 32 KiB stages, three stages ahead. Step ks: wait for this
-// wave's DMAs of stage ks (vmcnt), barrier (every wave's are in; stage ks-1's slot is
-// free), DMA stage ks+3 into that slot, then the MFMAs of stage ks. The ring runs on
-// across units: the last three steps of a unit load the next unit's first three
-// stages, so a unit's epilogue overlaps the next unit's loads. The last MFMA group
-// of each stage is issued after the next barrier, while that stage's first fragment
-// reads are in flight. The ring stages are separate LDS objects used with constant
-// indices (the K loop runs four steps per round), so the compiler can tell a step's
-// reads from the DMA writes in flight to the other stages and adds no wait of its own.
+// Pipeline. Two 64 KiB stages. Step ks: wait for this wave's DMAs of stage ks (vmcnt),
+// barrier (every wave's are in; stage ks-1's slot is free), DMA stage ks+1 into that
+// slot, then the MFMAs of stage ks. The stages run on across units: a unit's last step
+// loads the next unit's first stage, so a unit's epilogue overlaps that load. The last
+// MFMA group of each stage is issued after the next barrier, while the next stage's
+// first fragment reads are in flight. The two stages are separate LDS objects used
+// with constant indices (the K loop runs two steps per round), so the compiler can
+// tell a step's reads from the DMA writes in flight to the other stage and adds no
+// wait of its own.
 //
 // Output. Each wave stages one 16-row MFMA tile row at a time in its own 2 KiB of LDS
 // (no barrier: a wave's LDS accesses complete in order) and stores whole row segments:
@@ -58,8 +60,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kSqWaves = 8;
-constexpr int kStageBytes = 32768;   // 16 A blocks + 16 B blocks of 1 KiB
-constexpr int kBHalf = 16384;        // B blocks start here
+constexpr int kStageBytes = 65536;   // 256 A rows x 128 bytes, then 16 B row blocks x 2 K tiles x 1 KiB
+constexpr int kBHalf = 32768;        // B blocks start here
 constexpr int kMaxExpertsSq = 1024;
 
 __device__ inline float sq_silu_mul(float g, float u) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u; }
@@ -143,21 +145,14 @@ __global__ __launch_bounds__(64 * kSqWaves, 1) void ffn_sq_kernel(SqArgs a) {
   static_assert(!GSAVE || GEMM_A, "G is kept by GEMM A");
   __shared__ __attribute__((aligned(16))) uint8_t s_r0[kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_r1[kStageBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t s_r2[kStageBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t s_r3[kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_out[kSqWaves * 2048];
   __shared__ int32_t s_ru[kMaxExpertsSq + 1];
   auto ring = [&](auto ST) -> uint8_t* {
-    constexpr int k = decltype(ST)::value;
-    if constexpr (k == 0) return s_r0;
-    else if constexpr (k == 1) return s_r1;
-    else if constexpr (k == 2) return s_r2;
-    else return s_r3;
+    if constexpr (decltype(ST)::value == 0) return s_r0;
+    else return s_r1;
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  using I3 = std::integral_constant<int, 3>;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -209,30 +204,36 @@ __global__ __launch_bounds__(64 * kSqWaves, 1) void ffn_sq_kernel(SqArgs a) {
   }
 
   const int KS = a.KS;
-  // this wave's DMA lanes: A blocks 2w, 2w + 1 are rows 32w .. 32w + 31 of the unit
+  // this wave's DMA lanes: pool rows 32w .. 32w + 31 of the unit, 8 rows per DMA; lane i fills
+  // LDS bytes 16i .. 16i + 15 of a DMA's 1 KiB, i.e. row i / 8, chunk slot i % 8, which holds
+  // the row's chunk (i % 8) ^ (row % 8)
   const uint32_t lda = (uint32_t)a.lda;
-  const uint32_t a_vo0 = (uint32_t)(32 * w + (lane & 15)) * lda + 16u * (uint32_t)(lane >> 4);
-  const uint32_t a_vo1 = a_vo0 + 16u * lda;
+  const uint32_t a_vo = (uint32_t)(32 * w + (lane >> 3)) * lda + 16u * (uint32_t)((lane & 7) ^ ((lane >> 3) & 7));
   const uint32_t b_vo = 16u * (uint32_t)lane;
+  // fragment read of pool rows: lane l takes row l % 16, chunk 4 kk + l / 16 of the stage
+  const int a_frag0 = (lane & 15) * 128 + ((((lane >> 4)) ^ (lane & 7)) << 4);
+  const int a_frag1 = (lane & 15) * 128 + (((4 + (lane >> 4)) ^ (lane & 7)) << 4);
   auto dma = [&](auto ST, const SqSrc& s, int ks) {
     uint8_t* base = ring(ST);
-    const uint32_t ka = (uint32_t)ks * 64u, kb = (uint32_t)ks * 1024u;
+    const uint32_t ka = (uint32_t)ks * 128u, kb = (uint32_t)ks * 2048u;
     typedef __attribute__((address_space(3))) void* lds_t;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(s.ar, (lds_t)(base + (2 * w) * 1024), 16, a_vo0, ka, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(s.ar, (lds_t)(base + (2 * w + 1) * 1024), 16, a_vo1, ka, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(s.br, (lds_t)(base + kBHalf + (2 * w) * 1024), 16, b_vo, s.b0 + kb, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(s.br, (lds_t)(base + kBHalf + (2 * w + 1) * 1024), 16, b_vo, s.b1 + kb,
-                                             0, 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(s.ar, (lds_t)(base + (4 * w + q) * 1024), 16, a_vo + 8u * q * lda, ka,
+                                               0, 0);
+    // B row blocks 2w, 2w + 1, K tiles 2ks, 2ks + 1 each
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(s.br, (lds_t)(base + kBHalf + (4 * w + q) * 1024), 16, b_vo,
+                                               (q < 2 ? s.b0 : s.b1) + kb + (q & 1) * 1024u, 0, 0);
   };
-  // B blocks of this wave's MFMA column tiles: GEMM A gate 2cg, 2cg + 1, up 8 + 2cg, 8 + 2cg + 1
+  // B row blocks of this wave's MFMA column tiles: GEMM A gate 2cg, 2cg + 1, up 8 + 2cg, 8 + 2cg + 1
   auto bblk = [&](int tn) { return GEMM_A ? (tn < 2 ? 2 * cg + tn : 8 + 2 * cg + (tn - 2)) : 4 * cg + tn; };
 
   SqUnit cur = sq_unit(a, s_ru, u);
   if (poll_each) sq_wait_tiles(a, cur);
   SqSrc cs = sq_src<GEMM_A>(a, cur, w);
   dma(I0{}, cs, 0);
-  dma(I1{}, cs, 1);
-  dma(I2{}, cs, 2);
 
   f32x4_t acc[8][4];
   bf16x8_t fbp[4], fap;   // the previous stage's last MFMA group, issued after the next barrier
@@ -252,27 +253,24 @@ __global__ __launch_bounds__(64 * kSqWaves, 1) void ffn_sq_kernel(SqArgs a) {
     fap = bf16x8_t{};   // zero operands: the first step's deferred group adds exactly 0
 
     auto step = [&](auto ST, int ks) {
-      constexpr int st = decltype(ST)::value;
-      using SN = std::integral_constant<int, (st + 3) & 3>;
+      using SN = std::integral_constant<int, decltype(ST)::value ^ 1>;
       __builtin_amdgcn_sched_barrier(0);
-      // this wave's DMAs of stage ks are in (those of ks + 1, ks + 2 may be in flight); its
-      // reads of stage ks - 1 are done
-      __builtin_amdgcn_s_waitcnt(vmcnt_enc(8));
+      // this wave's DMAs of stage ks are in, and its reads of stage ks - 1 are done
+      wait_vm0();
       __builtin_amdgcn_s_waitcnt(kLgkm0);
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      // stage ks + 3 into the slot of stage ks - 1: this unit's, the next unit's first
-      // three, or (last unit) a reload of this unit's last stage that nobody reads, so
-      // that every step issues four DMAs
+      // stage ks + 1 into the slot of stage ks - 1: this unit's, the next unit's first, or
+      // (last unit) a reload of this unit's last stage that nobody reads, so that every step
+      // issues the same DMAs
       {
-        const int kd = ks + 3;
         SqSrc s = cs;
-        int kk = kd;
-        if (kd >= KS) {
+        int kk = ks + 1;
+        if (kk >= KS) {
           if (has_next) {
             s = ns;
-            kk = kd - KS;
-            if (kk == 0 && poll_each) sq_wait_tiles(a, nx);
+            kk = 0;
+            if (poll_each) sq_wait_tiles(a, nx);
           } else {
             kk = KS - 1;
           }
@@ -281,37 +279,46 @@ __global__ __launch_bounds__(64 * kSqWaves, 1) void ffn_sq_kernel(SqArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
       if (compute) {
-        const uint8_t* sa = ring(ST) + (rg * 8) * 1024 + 16 * lane;
+        const uint8_t* sa = ring(ST) + (rg * 128) * 128;
         const uint8_t* sb = ring(ST) + kBHalf + 16 * lane;
         bf16x8_t fb[4];
 #pragma unroll
-        for (int tn = 0; tn < 4; ++tn) fb[tn] = *reinterpret_cast<const bf16x8_t*>(sb + bblk(tn) * 1024);
-        bf16x8_t fa = *reinterpret_cast<const bf16x8_t*>(sa);
+        for (int tn = 0; tn < 4; ++tn) fb[tn] = *reinterpret_cast<const bf16x8_t*>(sb + (bblk(tn) * 2) * 1024);
+        bf16x8_t fa = *reinterpret_cast<const bf16x8_t*>(sa + a_frag0);
         // the previous stage's last group
 #pragma unroll
         for (int tn = 0; tn < 4; ++tn)
           acc[7][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fbp[tn], fap, acc[7][tn], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
+        // 16 groups: K half kk, row tile tm; A fragments read one group ahead, the second K
+        // half's B fragments during the first half
+        bf16x8_t fb1[4];
 #pragma unroll
-        for (int tm = 0; tm < 7; ++tm) {
-          const bf16x8_t fn = *reinterpret_cast<const bf16x8_t*>(sa + (tm + 1) * 1024);
+        for (int g = 0; g < 15; ++g) {
+          const int kk = g >> 3, tm = g & 7;
+          const int g1 = g + 1;
+          const bf16x8_t fn =
+              *reinterpret_cast<const bf16x8_t*>(sa + ((g1 & 7) * 16) * 128 + ((g1 >> 3) ? a_frag1 : a_frag0));
+          if (g == 3) {
+#pragma unroll
+            for (int tn = 0; tn < 4; ++tn)
+              fb1[tn] = *reinterpret_cast<const bf16x8_t*>(sb + (bblk(tn) * 2 + 1) * 1024);
+          }
 #pragma unroll
           for (int tn = 0; tn < 4; ++tn)
-            acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[tn], fa, acc[tm][tn], 0, 0, 0);
+            acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk ? fb1[tn] : fb[tn], fa, acc[tm][tn], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
           fa = fn;
         }
         fap = fa;
 #pragma unroll
-        for (int tn = 0; tn < 4; ++tn) fbp[tn] = fb[tn];
+        for (int tn = 0; tn < 4; ++tn) fbp[tn] = fb1[tn];
       }
     };
 
-    for (int ks = 0; ks < KS; ks += 4) {
+    for (int ks = 0; ks < KS; ks += 2) {
       step(I0{}, ks);
       step(I1{}, ks + 1);
-      step(I2{}, ks + 2);
-      step(I3{}, ks + 3);
     }
 
     if (compute) {
