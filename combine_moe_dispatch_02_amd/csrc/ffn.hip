@@ -1725,19 +1725,19 @@ int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream
     a.pool_rows = f.pool_rows;
   }
 
-  // 256-row units when asked for, or when only they take the shape (tiled weights with
-  // I % 256 != 0); the 128 x 512 units otherwise
-  const bool sq_shape = ffn_sq_ok(H, I, f.dtype, tile, f.block_n, f.weight_layout, f.comb_out != nullptr);
-  const bool sq = sq_shape && (f.unit_rows == 256 || (f.unit_rows == 0 && !(big_a_ok(H, I, f.dtype, tile) &&
-                                                                           big_y_ok(H, I, f.dtype, tile))));
+  // 256-row units wherever they take the shape (unless 128 is asked for); the 128 x 512
+  // units otherwise
+  const bool sq = f.unit_rows != 128 && ffn_sq_ok(H, I, f.dtype, tile, f.block_n, f.weight_layout,
+                                                  f.comb_out != nullptr);
   if (sq) {
     int grid = f.workgroups > 0 ? f.workgroups : device_cu_count();
     if (grid <= 0) return MOE_ERR_HIP;
     SqArgs q{};
     q.n_experts = p.E_local;
     q.max_tiles = f.pool_rows / 128;
-    q.group = f.unit_order > 0 ? f.unit_order : 4;
+    q.group = f.unit_order > 0 ? f.unit_order : 6;
     q.offsets = p.offsets;
+    q.counts = p.counts;
     q.num_tiles = p.num_tiles;
     q.tile_ready = p.tile_ready;
     q.tiles_done = reinterpret_cast<const uint32_t*>(ws + L.tiles_done);
@@ -1758,7 +1758,7 @@ int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream
     q.g_save = static_cast<uint8_t*>(f.g_pool);
     q.g_ld = (int64_t)4 * I;
     q.g_up = 2 * I;
-    q.KS = H / 64;
+    q.KS = H / 32;
     q.NB = 2 * I / 256;
     q.up_rb = I / 16;
     q.wait_ready = 1;
@@ -1774,7 +1774,7 @@ int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream
     q.out = static_cast<uint8_t*>(f.y_pool);
     q.ldo = (int64_t)H * 2;
     q.g_save = nullptr;
-    q.KS = I / 64;
+    q.KS = I / 32;
     q.NB = H / 256;
     q.up_rb = 0;
     q.wait_ready = 0;

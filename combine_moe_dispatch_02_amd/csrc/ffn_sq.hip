@@ -10,31 +10,36 @@
 //
 // Work unit = (expert e, two consecutive pool tiles m, m+1 of e, N block j of 256
 // columns); an expert with an odd tile count ends with a one-tile unit, whose second
-// row half is neither computed nor stored. GEMM A's N block is 128 gate columns and
+// row half (rows of the next segment, outside the DMA range) is computed from zeros and
+// not stored. GEMM A's N block is 128 gate columns and
 // the matching 128 up columns of w1, so SwiGLU stays in the lane that holds both.
 // 8 waves: wave w computes rows 128 (w / 4) .. +128 and 64 of the 256 columns
 // (w % 4), i.e. 8 x 4 MFMA tiles, 128 accumulators per lane.
 //
-// Operands. A K stage is 64 values (128 bytes, one cache line) of every row: 256 pool
-// (or h) rows and 256 weight rows, 64 KiB of LDS. The pool rows are stored row by row,
-// their eight 16-byte chunks XOR-permuted by row % 8: the eight lanes of a DMA that
-// fill one row fetch its whole line, and the eight lanes of a fragment read that share
-// a chunk index (eight rows) land on eight distinct 16-byte slots of a 128-byte bank
-// row. The tiled weight layout already holds MFMA fragments as contiguous 1 KiB blocks
-// (lane l's 16 bytes = row l % 16, K values 8 (l / 16) .. +8 of a 32-wide K tile), two
-// per 16 rows and stage, which the DMA copies as they are. Each wave moves 8 of the
-// stage's 64 KiB by LDS-DMA (buffer_load ... lds), so no register holds a load in
-// flight, and every request covers whole cache lines.
+// Operands. The pool (or h) rows move in K stages of 64 values, 128 bytes a row (one
+// cache line): 256 rows, 32 KiB. They are stored row by row, their eight 16-byte chunks
+// XOR-permuted by row % 8: the eight lanes of a DMA that fill one row fetch its whole
+// line, and the eight lanes of a fragment read that share a chunk index (eight rows)
+// land on eight distinct 16-byte slots of a 128-byte bank row. The weights move in K
+// stages of 32 values: the tiled layout already holds MFMA fragments as contiguous 1 KiB
+// blocks (lane l's 16 bytes = row l % 16, K values 8 (l / 16) .. +8 of a 32-wide K tile),
+// 16 of them per stage (16 KiB), which the DMA copies as they are. Rows past the unit's
+// real rows (a segment's padding) lie outside the DMA's buffer range: they are not
+// fetched and land as zeros. Each wave issues its share by LDS-DMA (buffer_load ... lds),
+// so no register holds a load in flight, and every request covers whole cache lines.
 //
-// Pipeline. Two 64 KiB stages. Step ks: wait for this wave's DMAs of stage ks (vmcnt),
-// barrier (every wave's are in; stage ks-1's slot is free), DMA stage ks+1 into that
-// slot, then the MFMAs of stage ks. The stages run on across units: a unit's last step
-// loads the next unit's first stage, so a unit's epilogue overlaps that load. The last
-// MFMA group of each stage is issued after the next barrier, while the next stage's
-// first fragment reads are in flight. The two stages are separate LDS objects used
-// with constant indices (the K loop runs two steps per round), so the compiler can
-// tell a step's reads from the DMA writes in flight to the other stage and adds no
-// wait of its own.
+// Pipeline, in steps of 32 K values. Weights: a ring of four 16 KiB stages, three steps
+// ahead. Pool rows: two 32 KiB stages of 64 K values, the next one loaded during the
+// current one (issued at its first step, used two steps later). About 80 KiB per CU are
+// in flight. Step s: wait for this wave's DMAs that step s reads (vmcnt), barrier (every
+// wave's are in; the stages step s - 1 read are free), issue the DMAs of weight stage
+// s + 3 and, on even steps, of pool-row stage s / 2 + 1, then the MFMAs of step s. The
+// stages run on across units: the last steps of a unit load the next unit's first
+// stages, so a unit's epilogue overlaps them. The last MFMA group of each step is
+// issued after the next barrier, while the next step's first fragment reads are in
+// flight. The stages are separate LDS objects used with constant indices (the K loop
+// runs four steps per round), so the compiler can tell a step's reads from the DMA
+// writes in flight to the other stages and adds no wait of its own.
 //
 // Output. Each wave stages one 16-row MFMA tile row at a time in its own 2 KiB of LDS
 // (no barrier: a wave's LDS accesses complete in order) and stores whole row segments:
@@ -60,8 +65,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kSqWaves = 8;
-constexpr int kStageBytes = 65536;   // 256 A rows x 128 bytes, then 16 B row blocks x 2 K tiles x 1 KiB
-constexpr int kBHalf = 32768;        // B blocks start here
+constexpr int kAStage = 32768;   // 256 pool rows x 128 bytes (64 K values)
+constexpr int kBStage = 16384;   // 16 weight row blocks x 1 KiB (32 K values)
 constexpr int kMaxExpertsSq = 1024;
 
 __device__ inline float sq_silu_mul(float g, float u) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u; }
@@ -77,7 +82,7 @@ struct SqUnit {
 // before e. Within expert e, units go in groups of `group` row units; inside a group,
 // N block by N block, the group's row units back to back: units that run together
 // share weight panels and pool rows.
-__device__ inline SqUnit sq_unit(const SqArgs& a, const int32_t* s_ru, int u) {
+__device__ __attribute__((always_inline)) inline SqUnit sq_unit(const SqArgs& a, const int32_t* s_ru, int u) {
   int lo = 0, hi = a.n_experts - 1;
   while (lo < hi) {  // the last expert whose first unit is <= u (empty experts share a start)
     const int mid = (lo + hi + 1) >> 1;
@@ -97,6 +102,12 @@ __device__ inline SqUnit sq_unit(const SqArgs& a, const int32_t* s_ru, int u) {
   const int t1 = min(a.offsets[lo + 1] >> 7, a.max_tiles);
   r.m = t0 + 2 * ru;
   r.two = r.m + 1 < t1;
+  // uniform over the wave (all lanes read the same LDS words): keep the unit in scalar
+  // registers, so that its buffer resources stay scalar too
+  r.e = __builtin_amdgcn_readfirstlane(r.e);
+  r.m = __builtin_amdgcn_readfirstlane(r.m);
+  r.two = __builtin_amdgcn_readfirstlane(r.two);
+  r.j = __builtin_amdgcn_readfirstlane(r.j);
   return r;
 }
 
@@ -108,9 +119,11 @@ struct SqSrc {
 };
 
 template <bool GEMM_A>
-__device__ inline SqSrc sq_src(const SqArgs& a, const SqUnit& U, int w) {
+__device__ __attribute__((always_inline)) inline SqSrc sq_src(const SqArgs& a, const SqUnit& U, int w) {
   SqSrc s;
-  s.ar = make_rsrc(a.A + (int64_t)U.m * 128 * a.lda, (uint32_t)((U.two ? 256 : 128) * a.lda));
+  // the unit's real rows only: padding rows are not fetched
+  const int real = __builtin_amdgcn_readfirstlane(min(U.two ? 256 : 128, a.offsets[U.e] + a.counts[U.e] - U.m * 128));
+  s.ar = make_rsrc(a.A + (int64_t)U.m * 128 * a.lda, (uint32_t)(max(real, 0) * a.lda));
   s.br = make_rsrc(a.B + (int64_t)U.e * a.b_expert, (uint32_t)a.b_expert);
   // B blocks 2w, 2w + 1 of the unit's 16: GEMM A gate blocks 0..7, up blocks 8..15
   const int rb = GEMM_A ? (w < 4 ? U.j * 8 + 2 * w : a.up_rb + U.j * 8 + 2 * (w - 4)) : U.j * 16 + 2 * w;
@@ -120,7 +133,7 @@ __device__ inline SqSrc sq_src(const SqArgs& a, const SqUnit& U, int w) {
 }
 
 // Wait until the unit's tiles carry this call's epoch (see the file comment).
-__device__ inline void sq_wait_tiles(const SqArgs& a, const SqUnit& U) {
+__device__ __attribute__((always_inline)) inline void sq_wait_tiles(const SqArgs& a, const SqUnit& U) {
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   for (;;) {
     const bool r0 = __hip_atomic_load(&a.tile_ready[U.m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch;
@@ -143,16 +156,29 @@ __device__ inline void sq_wait_tiles(const SqArgs& a, const SqUnit& U) {
 template <bool GEMM_A, bool GSAVE>
 __global__ __launch_bounds__(64 * kSqWaves, 1) void ffn_sq_kernel(SqArgs a) {
   static_assert(!GSAVE || GEMM_A, "G is kept by GEMM A");
-  __shared__ __attribute__((aligned(16))) uint8_t s_r0[kStageBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t s_r1[kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_a0[kAStage];
+  __shared__ __attribute__((aligned(16))) uint8_t s_a1[kAStage];
+  __shared__ __attribute__((aligned(16))) uint8_t s_b0[kBStage];
+  __shared__ __attribute__((aligned(16))) uint8_t s_b1[kBStage];
+  __shared__ __attribute__((aligned(16))) uint8_t s_b2[kBStage];
+  __shared__ __attribute__((aligned(16))) uint8_t s_b3[kBStage];
   __shared__ __attribute__((aligned(16))) uint8_t s_out[kSqWaves * 2048];
   __shared__ int32_t s_ru[kMaxExpertsSq + 1];
-  auto ring = [&](auto ST) -> uint8_t* {
-    if constexpr (decltype(ST)::value == 0) return s_r0;
-    else return s_r1;
+  auto aring = [&](auto ST) __attribute__((always_inline)) -> uint8_t* {
+    if constexpr (decltype(ST)::value == 0) return s_a0;
+    else return s_a1;
+  };
+  auto bring = [&](auto ST) __attribute__((always_inline)) -> uint8_t* {
+    constexpr int k = decltype(ST)::value;
+    if constexpr (k == 0) return s_b0;
+    else if constexpr (k == 1) return s_b1;
+    else if constexpr (k == 2) return s_b2;
+    else return s_b3;
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -190,7 +216,7 @@ __global__ __launch_bounds__(64 * kSqWaves, 1) void ffn_sq_kernel(SqArgs a) {
     if (lane == 63) s_ru[E] = incl;
   }
   __syncthreads();
-  const int total = s_ru[a.n_experts] * a.NB;
+  const int total = __builtin_amdgcn_readfirstlane(s_ru[a.n_experts] * a.NB);
   const int G = gridDim.x;
   int u = unit_slot(blockIdx.x, G);
   if (u >= total) return;
@@ -213,27 +239,37 @@ __global__ __launch_bounds__(64 * kSqWaves, 1) void ffn_sq_kernel(SqArgs a) {
   // fragment read of pool rows: lane l takes row l % 16, chunk 4 kk + l / 16 of the stage
   const int a_frag0 = (lane & 15) * 128 + ((((lane >> 4)) ^ (lane & 7)) << 4);
   const int a_frag1 = (lane & 15) * 128 + (((4 + (lane >> 4)) ^ (lane & 7)) << 4);
-  auto dma = [&](auto ST, const SqSrc& s, int ks) {
-    uint8_t* base = ring(ST);
-    const uint32_t ka = (uint32_t)ks * 128u, kb = (uint32_t)ks * 2048u;
-    typedef __attribute__((address_space(3))) void* lds_t;
+  typedef __attribute__((address_space(3))) void* lds_t;
+  // one DMA of pool-row stage kd (64 K values): rows 32w + 8q .. +8
+  auto dma_a1 = [&](auto ST, const SqSrc& s, int kd, int q) __attribute__((always_inline)) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(s.ar, (lds_t)(aring(ST) + (4 * w + q) * 1024), 16, a_vo + 8u * q * lda,
+                                             (uint32_t)kd * 128u, 0, 0);
+  };
+  // one DMA of weight stage kb (32 K values): this wave's row block 2w + q
+  auto dma_b1 = [&](auto ST, const SqSrc& s, int kb, int q) __attribute__((always_inline)) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(s.br, (lds_t)(bring(ST) + (2 * w + q) * 1024), 16, b_vo,
+                                             (q ? s.b1 : s.b0) + (uint32_t)kb * 1024u, 0, 0);
+  };
+  auto dma_a = [&](auto ST, const SqSrc& s, int kd) __attribute__((always_inline)) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(s.ar, (lds_t)(base + (4 * w + q) * 1024), 16, a_vo + 8u * q * lda, ka,
-                                               0, 0);
-    // B row blocks 2w, 2w + 1, K tiles 2ks, 2ks + 1 each
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(s.br, (lds_t)(base + kBHalf + (4 * w + q) * 1024), 16, b_vo,
-                                               (q < 2 ? s.b0 : s.b1) + kb + (q & 1) * 1024u, 0, 0);
+    for (int q = 0; q < 4; ++q) dma_a1(ST, s, kd, q);
+  };
+  auto dma_b = [&](auto ST, const SqSrc& s, int kb) __attribute__((always_inline)) {
+    dma_b1(ST, s, kb, 0);
+    dma_b1(ST, s, kb, 1);
   };
   // B row blocks of this wave's MFMA column tiles: GEMM A gate 2cg, 2cg + 1, up 8 + 2cg, 8 + 2cg + 1
-  auto bblk = [&](int tn) { return GEMM_A ? (tn < 2 ? 2 * cg + tn : 8 + 2 * cg + (tn - 2)) : 4 * cg + tn; };
+  auto bblk = [&](int tn) __attribute__((always_inline)) { return GEMM_A ? (tn < 2 ? 2 * cg + tn : 8 + 2 * cg + (tn - 2)) : 4 * cg + tn; };
 
   SqUnit cur = sq_unit(a, s_ru, u);
   if (poll_each) sq_wait_tiles(a, cur);
   SqSrc cs = sq_src<GEMM_A>(a, cur, w);
-  dma(I0{}, cs, 0);
+  // the first unit's stages in the order the steady state issues them: weights 0, pool rows
+  // 0 and weights 1 (as at step -2), weights 2 (step -1)
+  dma_b(I0{}, cs, 0);
+  dma_a(I0{}, cs, 0);
+  dma_b(I1{}, cs, 1);
+  dma_b(I2{}, cs, 2);
 
   f32x4_t acc[8][4];
   bf16x8_t fbp[4], fap;   // the previous stage's last MFMA group, issued after the next barrier
@@ -243,7 +279,7 @@ __global__ __launch_bounds__(64 * kSqWaves, 1) void ffn_sq_kernel(SqArgs a) {
     const bool has_next = un < total;
     const SqUnit nx = has_next ? sq_unit(a, s_ru, un) : cur;
     const SqSrc ns = sq_src<GEMM_A>(a, nx, w);
-    const bool compute = rg == 0 || cur.two;
+    const bool store = rg == 0 || cur.two;   // a one-tile unit's second row half is not stored
 #pragma unroll
     for (int tm = 0; tm < 8; ++tm)
 #pragma unroll
@@ -252,79 +288,95 @@ __global__ __launch_bounds__(64 * kSqWaves, 1) void ffn_sq_kernel(SqArgs a) {
     for (int tn = 0; tn < 4; ++tn) fbp[tn] = bf16x8_t{};
     fap = bf16x8_t{};   // zero operands: the first step's deferred group adds exactly 0
 
-    auto step = [&](auto ST, int ks) {
-      using SN = std::integral_constant<int, decltype(ST)::value ^ 1>;
+    // step ks (32 K values), ks % 4 = ST: weights from stage ST, pool rows from stage ST / 2,
+    // K half ST % 2 of it
+    auto step = [&](auto ST, int ks) __attribute__((always_inline)) {
+      constexpr int st = decltype(ST)::value;
+      using AS = std::integral_constant<int, st / 2>;          // pool-row stage read
+      using AN = std::integral_constant<int, (st / 2) ^ 1>;    // pool-row stage loaded (even steps)
+      using BN = std::integral_constant<int, (st + 3) & 3>;    // weight stage loaded
+      constexpr bool EVEN = (st & 1) == 0;
       __builtin_amdgcn_sched_barrier(0);
-      // this wave's DMAs of stage ks are in, and its reads of stage ks - 1 are done
-      wait_vm0();
+      // this wave's DMAs that step ks reads are in (even steps: pool rows ks / 2 and weights
+      // ks, with weights ks + 1, ks + 2 in flight behind them; odd steps: weights ks, with
+      // weights ks + 1, pool rows ks / 2 + 1 and weights ks + 2 behind them); its reads of
+      // step ks - 1 are done
+      __builtin_amdgcn_s_waitcnt(vmcnt_enc(EVEN ? 4 : 8));
       __builtin_amdgcn_s_waitcnt(kLgkm0);
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      // stage ks + 1 into the slot of stage ks - 1: this unit's, the next unit's first, or
-      // (last unit) a reload of this unit's last stage that nobody reads, so that every step
-      // issues the same DMAs
-      {
-        SqSrc s = cs;
-        int kk = ks + 1;
-        if (kk >= KS) {
-          if (has_next) {
-            s = ns;
-            kk = 0;
-            if (poll_each) sq_wait_tiles(a, nx);
-          } else {
-            kk = KS - 1;
-          }
-        }
-        dma(SN{}, s, kk);
+      // even steps: pool-row stage ks / 2 + 1 (this unit's, the next unit's first, or a reload
+      // nobody reads when there is no next unit); every step: weight stage ks + 3, likewise.
+      // The DMAs go out one per MFMA group, pool rows first (the wait counts above rely on
+      // that order), so that issuing them never holds the wave off its MFMAs for long.
+      const int kd0 = (ks >> 1) + 1;
+      const bool a_next = kd0 >= (KS >> 1);
+      if constexpr (EVEN) {
+        if (a_next && has_next && poll_each) sq_wait_tiles(a, nx);
       }
+      const bool an = a_next && has_next;
+      __amdgpu_buffer_rsrc_t d_ar = cs.ar;
+      if (an) d_ar = ns.ar;
+      const uint32_t d_ak = (uint32_t)(a_next ? (has_next ? 0 : (KS >> 1) - 1) : kd0) * 128u;
+      const int kb0 = ks + 3;
+      const bool b_next = kb0 >= KS;
+      const bool bn = b_next && has_next;
+      __amdgpu_buffer_rsrc_t d_br = cs.br;
+      if (bn) d_br = ns.br;
+      const uint32_t d_bk = (uint32_t)(b_next ? (has_next ? kb0 - KS : KS - 1) : kb0) * 1024u;
+      const uint32_t d_b0 = (bn ? ns.b0 : cs.b0) + d_bk, d_b1 = (bn ? ns.b1 : cs.b1) + d_bk;
+      // the DMA of group g (0 .. 5 on even steps, 0 .. 1 on odd ones)
+      auto dma_g = [&](int g) __attribute__((always_inline)) {
+        if (EVEN && g < 4) {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(d_ar, (lds_t)(aring(AN{}) + (4 * w + g) * 1024), 16,
+                                                   a_vo + 8u * (uint32_t)g * lda, d_ak, 0, 0);
+        } else {
+          const int q = EVEN ? g - 4 : g;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(d_br, (lds_t)(bring(BN{}) + (2 * w + q) * 1024), 16, b_vo,
+                                                   q ? d_b1 : d_b0, 0, 0);
+        }
+      };
+      constexpr int NDMA = EVEN ? 6 : 2;
       __builtin_amdgcn_sched_barrier(0);
-      if (compute) {
-        const uint8_t* sa = ring(ST) + (rg * 128) * 128;
-        const uint8_t* sb = ring(ST) + kBHalf + 16 * lane;
+      {
+        const uint8_t* sa = aring(AS{}) + (rg * 128) * 128 + (EVEN ? a_frag0 : a_frag1);
+        const uint8_t* sb = bring(ST) + 16 * lane;
         bf16x8_t fb[4];
 #pragma unroll
-        for (int tn = 0; tn < 4; ++tn) fb[tn] = *reinterpret_cast<const bf16x8_t*>(sb + (bblk(tn) * 2) * 1024);
-        bf16x8_t fa = *reinterpret_cast<const bf16x8_t*>(sa + a_frag0);
-        // the previous stage's last group
+        for (int tn = 0; tn < 4; ++tn) fb[tn] = *reinterpret_cast<const bf16x8_t*>(sb + bblk(tn) * 1024);
+        bf16x8_t fa = *reinterpret_cast<const bf16x8_t*>(sa);
+        // the previous step's last group
 #pragma unroll
         for (int tn = 0; tn < 4; ++tn)
           acc[7][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fbp[tn], fap, acc[7][tn], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        // 16 groups: K half kk, row tile tm; A fragments read one group ahead, the second K
-        // half's B fragments during the first half
-        bf16x8_t fb1[4];
-#pragma unroll
-        for (int g = 0; g < 15; ++g) {
-          const int kk = g >> 3, tm = g & 7;
-          const int g1 = g + 1;
-          const bf16x8_t fn =
-              *reinterpret_cast<const bf16x8_t*>(sa + ((g1 & 7) * 16) * 128 + ((g1 >> 3) ? a_frag1 : a_frag0));
-          if (g == 3) {
-#pragma unroll
-            for (int tn = 0; tn < 4; ++tn)
-              fb1[tn] = *reinterpret_cast<const bf16x8_t*>(sb + (bblk(tn) * 2 + 1) * 1024);
-          }
+#pragma clang loop unroll(full)
+        for (int tm = 0; tm < 7; ++tm) {
+          if (tm < NDMA) dma_g(tm);
+          const bf16x8_t fn = *reinterpret_cast<const bf16x8_t*>(sa + ((tm + 1) * 16) * 128);
 #pragma unroll
           for (int tn = 0; tn < 4; ++tn)
-            acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk ? fb1[tn] : fb[tn], fa, acc[tm][tn], 0, 0, 0);
+            acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[tn], fa, acc[tm][tn], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
           fa = fn;
         }
         fap = fa;
 #pragma unroll
-        for (int tn = 0; tn < 4; ++tn) fbp[tn] = fb1[tn];
+        for (int tn = 0; tn < 4; ++tn) fbp[tn] = fb[tn];
       }
     };
 
-    for (int ks = 0; ks < KS; ks += 2) {
+    for (int ks = 0; ks < KS; ks += 4) {
       step(I0{}, ks);
       step(I1{}, ks + 1);
+      step(I2{}, ks + 2);
+      step(I3{}, ks + 3);
     }
 
-    if (compute) {
 #pragma unroll
-      for (int tn = 0; tn < 4; ++tn)
-        acc[7][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fbp[tn], fap, acc[7][tn], 0, 0, 0);
+    for (int tn = 0; tn < 4; ++tn)
+      acc[7][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fbp[tn], fap, acc[7][tn], 0, 0, 0);
+    if (store) {
       // ---- epilogue: lane holds row tm*16 + (lane & 15), columns 4 (lane >> 4) + (0..3) of each tile
       uint8_t* so = s_out + w * 2048;
       const int64_t row0 = (int64_t)cur.m * 128 + rg * 128;

@@ -53,13 +53,14 @@ struct SqArgs {
   uint8_t* g_save;           // training GEMM A: G = [gate | up] bf16 [rows][2I]
   int64_t g_ld;              // bytes per G row
   int32_t g_up;              // bytes from a G row's gate columns to its up columns (2I / 2 * 2)
-  int32_t KS;                // K / 64 stages (even)
+  int32_t KS;                // K / 32 steps (a multiple of 4)
   int32_t NB;                // N blocks of 256 columns
   int32_t up_rb;             // GEMM A: first 16-row block of w1's up rows (I / 16)
   int32_t n_experts;
   int32_t max_tiles;         // pool_rows / 128
   int32_t group;             // row units per walk group
   const int32_t* offsets;
+  const int32_t* counts;
   const int32_t* num_tiles;
   const uint32_t* tile_ready;
   const uint32_t* tiles_done;

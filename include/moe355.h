@@ -123,10 +123,10 @@ typedef struct moe_tile_config {
   int32_t unit_rows;        /* rows of a GEMM work unit: 128 = one pool tile (128 x 512 units),
                                256 = two pool tiles of one expert (256 x 256 units, both operands
                                by LDS-DMA; bf16, tiled weights, tile 128, H % 256 == 0,
-                               I % 128 == 0, not with combine on completion); 0 = auto (128
-                               where the 128 x 512 kernel takes the shape, else 256). With 256,
-                               unit_order k >= 1 walks each expert in groups of k tile pairs
-                               (0 = auto). Same results. */
+                               I % 128 == 0, not with combine on completion); 0 = auto (256
+                               where it applies, else 128). With 256, unit_order k >= 1 walks
+                               each expert in groups of k tile pairs (0 = auto: 6). Same
+                               results. */
 } moe_tile_config;
 
 /* Host-only size helpers (no device access). */
