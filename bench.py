@@ -82,8 +82,11 @@ def algorithmic_work(cfg, idx_np):
     }
 
 
-def cpu_baseline(inp, sample_tokens: int):
-    """The oracle as it stands, on tokens [0, sample_tokens) of the same workload."""
+def cpu_baseline(inp, max_tokens: int, target_s: float = 15.0, gpu_out=None):
+    """The oracle as it stands, timed on the first tokens of the same workload: a probe on 64
+    tokens sizes the sample to about ``target_s`` seconds of CPU work (at most ``max_tokens``).
+    With ``gpu_out`` (the layer's output on the GPU), also the max-normwise relative error of
+    those tokens against the oracle."""
     import numpy as np
 
     import oracle
@@ -92,13 +95,80 @@ def cpu_baseline(inp, sample_tokens: int):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = 1
-    toks = np.arange(sample_tokens)
     t0 = time.perf_counter()
-    oracle.moe_layer(inp, tokens=toks)
+    oracle.moe_layer(inp, tokens=np.arange(min(64, max_tokens)))
+    probe = time.perf_counter() - t0
+    n = int(max(64, min(max_tokens, 64 * target_s / max(probe, 1e-3))))
+    toks = np.arange(n)
+    t0 = time.perf_counter()
+    ref = oracle.moe_layer(inp, tokens=toks)
     dt = time.perf_counter() - t0
-    return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"tokens 0..{sample_tokens - 1} of the workload (all their pairs), "
-                      f"float64 NumPy oracle incl. weight dequantisation, {dt:.1f} s"}
+    out = {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"tokens 0..{n - 1} of the workload (all their pairs), float64 NumPy oracle incl. "
+                     f"weight dequantisation, {dt:.1f} s (sized by a 64-token probe of {probe:.1f} s)"}
+    if gpu_out is not None:
+        got = oracle.bf16_to_f64(gpu_out[:n].cpu())
+        out["gpu_max_norm_rel_err"] = float(oracle.max_norm_rel_err(got, ref.out))
+    return out
+
+
+def measured_peaks(dev):
+    """The device's own rates beside the spec peaks: a bf16 MFMA loop and streaming read /
+    write / copy kernels of the library (moe_calibrate_*), timed with HIP events."""
+    import ctypes
+
+    import torch
+
+    import combine_moe_dispatch_02_amd as moe
+    from combine_moe_dispatch_02_amd import _abi
+
+    lib = _abi.load()
+    cus = moe.device_cu_count()
+    s = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(s.cuda_stream)
+    sink = torch.empty(cus * 8 * 512, dtype=torch.float32, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps=3):
+        fn()
+        best = 1e9
+        for _ in range(reps):
+            e0.record(s)
+            fn()
+            e1.record(s)
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e-3)
+        return best
+
+    iters = 20000
+    t = timed(lambda: _abi.check("moe_calibrate_mfma", lib.moe_calibrate_mfma(
+        iters, ctypes.c_void_p(sink.data_ptr()), cus, sp)))
+    mfma = cus * 8 * iters * 16 * 16384 / t / 1e12
+    nbytes = 2 << 30
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    b = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    a.fill_(1)
+    rates = {}
+    for mode, name, factor in ((0, "read", 1), (1, "write", 1), (2, "copy", 2)):
+        t = timed(lambda: _abi.check("moe_calibrate_stream", lib.moe_calibrate_stream(
+            ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(b.data_ptr()), nbytes, mode,
+            ctypes.c_void_p(sink.data_ptr()), cus * 8, sp)))
+        rates[name] = factor * nbytes / t / 1e9
+    del a, b
+    return {"mfma_bf16_loop_TFLOPs": round(mfma, 1), "spec_bf16_TFLOPs": PEAK_BF16_TFLOPS,
+            "hbm_read_GBps": round(rates["read"], 1), "hbm_write_GBps": round(rates["write"], 1),
+            "hbm_copy_GBps": round(rates["copy"], 1), "spec_hbm_GBps": PEAK_HBM_GBS,
+            "method": f"bf16 MFMA loop on {cus} CUs x 8 waves; one grid-stride pass over 2 GiB "
+                      f"(copy counts read + write bytes); best of 3, HIP events"}
+
+
+def routing_stats(layer, cfg):
+    """Realised routing of the step: pairs per local expert and the pool it makes."""
+    c = layer.plan.counts.cpu().numpy().astype(float)
+    return {"max_count": int(c.max()), "mean_count": round(float(c.mean()), 1),
+            "max_over_mean": round(float(c.max() / max(c.mean(), 1e-9)), 2),
+            "empty_experts": int((c == 0).sum()), "tiles": int(layer.plan.num_tiles.item()),
+            "pool_rows": int(layer.plan.offsets[-1].item())}
 
 
 def _read_csv(path):
@@ -299,7 +369,12 @@ def main():
                     help="tile config override: CUs GEMM A leaves to a concurrent dispatch (0 = auto)")
     ap.add_argument("--a-stages", type=int, default=0,
                     help="tile config override: pool-row pipeline depth of the big-tile GEMMs (0 = auto, 2, 4)")
-    ap.add_argument("--cpu-sample", type=int, default=512, help="tokens of the oracle CPU baseline (0 = skip)")
+    ap.add_argument("--cpu-sample", type=int, default=16384,
+                    help="most tokens of the oracle CPU baseline, sized to about 15 s of CPU work (0 = skip)")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured MFMA / HBM peaks")
+    ap.add_argument("--flush-steps", type=int, default=5,
+                    help="steps also timed one by one after a 512 MiB write (the last-level cache "
+                         "flushed); 0 = skip")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run three 1 GiB device-to-device copies (a known-size reference for "
                          "the FETCH_SIZE / WRITE_SIZE counters)")
@@ -430,6 +505,30 @@ def main():
         for i, k in enumerate(stage_ms):
             stage_ms[k] += ev[i].elapsed_time(ev[i + 1]) / len(evs)
 
+    # the same steps with the last-level cache (256 MB) flushed before each: a 512 MiB write
+    flushed = None
+    if args.flush_steps > 0 and not args.graph:
+        import ctypes
+
+        from combine_moe_dispatch_02_amd import _abi
+        junk = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        lib = _abi.load()
+        f_ms = []
+        for _ in range(args.flush_steps):
+            _abi.check("moe_calibrate_stream", lib.moe_calibrate_stream(
+                None, ctypes.c_void_p(junk.data_ptr()), junk.numel(), 1, None, 2048,
+                ctypes.c_void_p(s.cuda_stream)))
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(s)
+            step()
+            a1.record(s)
+            torch.cuda.synchronize()
+            f_ms.append(a0.elapsed_time(a1))
+        del junk
+        f = sorted(f_ms)[len(f_ms) // 2]
+        flushed = {"ms_per_step": round(f, 4), "value": round(cfg.T / (f * 1e-3), 1),
+                   "steps": args.flush_steps, "how": "median of single steps, each after a 512 MiB write"}
+
     tokens_s = cfg.T / (ms_step * 1e-3)
     ffn_tflops = work["ffn_flops"] / (stage_ms["ffn"] * 1e-3) / 1e12
     ffn_gbs = work["ffn_bytes"] / (stage_ms["ffn"] * 1e-3) / 1e9
@@ -482,10 +581,27 @@ def main():
             / ((stage_ms["dispatch"] + stage_ms["combine"]) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
         if not args.combine_on_completion else None,
         "wall_s_timed": round(wall, 3),
+        "mall_flushed": flushed,
+        "routing": routing_stats(layer, cfg),
     }
+    if not args.no_peaks:
+        log("[bench] measured peaks")
+        pk = measured_peaks(dev)
+        result["measured_peaks"] = pk
+        r = result["roofline"]
+        if r["unit"] == "TFLOP/s" and cfg.dtype == "bf16":
+            r["frac_of_measured_mfma_loop"] = round(r["achieved"] / pk["mfma_bf16_loop_TFLOPs"], 4)
+        dc_rate = result["dispatch_combine_frac_hbm"]
+        if dc_rate is not None:
+            # dispatch writes about eight times what it reads, combine the reverse: the copy
+            # rate is the streaming limit for that mix
+            result["dispatch_combine_frac_of_measured_copy"] = round(
+                dc_rate * PEAK_HBM_GBS / pk["hbm_copy_GBps"], 4)
     if args.cpu_sample > 0:
-        log(f"[bench] oracle CPU baseline on {args.cpu_sample} tokens")
-        result["cpu_baseline"] = cpu_baseline(inp, min(args.cpu_sample, cfg.T))
+        log(f"[bench] oracle CPU baseline (at most {args.cpu_sample} tokens)")
+        torch.cuda.synchronize()
+        result["cpu_baseline"] = cpu_baseline(inp, min(args.cpu_sample, cfg.T), gpu_out=layer.out)
+        result["oracle_max_norm_rel_err"] = result["cpu_baseline"].pop("gpu_max_norm_rel_err", None)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

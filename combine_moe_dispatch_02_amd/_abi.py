@@ -91,6 +91,8 @@ SIGNATURES = [
     ("moe_combine", ctypes.c_int, [_VP, _I32, _VP, _PP, _I32, _VP, _VP]),
     ("moe_pack_weights", ctypes.c_int, [_VP, _I32, _I32, _I32, _I32, _VP, _VP]),
     ("moe_pack_mx_scales", ctypes.c_int, [_VP, _I32, _I32, _I32, _VP, _VP]),
+    ("moe_calibrate_mfma", ctypes.c_int, [_I32, _VP, _I32, _VP]),
+    ("moe_calibrate_stream", ctypes.c_int, [_VP, _VP, ctypes.c_int64, _I32, _VP, _I32, _VP]),
     ("moe_get_error", ctypes.c_int, [_VP, _SZ, _VP]),
     ("moe_status_string", ctypes.c_char_p, [ctypes.c_int]),
     ("moe_device_cu_count", ctypes.c_int, []),

@@ -1,6 +1,7 @@
 // C ABI of libmoe355: argument validation, workspace layout, launches.
 // The contract of each entry point is stated in include/moe355.h.
 #include <hip/hip_runtime.h>
+#include <rocprofiler-sdk-roctx/roctx.h>
 
 #include <algorithm>
 #include <cstring>
@@ -18,10 +19,16 @@ int device_cu_count() {
   return n;
 }
 
+// a named roctx range around one entry point's launches (seen by rocprofv3 --marker-trace)
+struct TraceRange {
+  explicit TraceRange(const char* name) { roctxRangePushA(name); }
+  ~TraceRange() { roctxRangePop(); }
+};
+
 static bool valid_tile(int32_t tile) { return tile == 16 || tile == 32 || tile == 64 || tile == 128; }
 
 // shape checks common to every call that takes a plan
-static int check_plan(const moe_plan_t* p) {
+int check_plan(const moe_plan_t* p) {
   if (!p) return MOE_ERR_INVALID;
   if (p->T < 1 || p->K < 1 || p->K > 16 || p->E_local < 1 || p->E_local > 1024 || p->expert_begin < 0)
     return MOE_ERR_INVALID;
@@ -57,6 +64,7 @@ MOE355_API size_t moe_workspace_bytes(int32_t T, int32_t K, int32_t E_local, int
 
 MOE355_API int moe_plan(const int32_t* topk_idx, const moe_plan_t* plan, void* ws, size_t ws_bytes,
                         void* stream) {
+  TraceRange trace("moe_plan");
   int rc = check_plan(plan);
   if (rc != MOE_OK) return rc;
   if (!topk_idx || !ws) return MOE_ERR_INVALID;
@@ -79,6 +87,7 @@ MOE355_API int moe_query_pool_rows(const moe_plan_t* plan, int32_t* host_P, void
 MOE355_API int moe_dispatch(const void* x, int32_t H, int32_t act_dtype, const moe_plan_t* plan,
                             int32_t pool_rows, void* pool, void* pool_s, uint32_t epoch, void* ws,
                             size_t ws_bytes, void* stream) {
+  TraceRange trace("moe_dispatch");
   int rc = check_plan(plan);
   if (rc != MOE_OK) return rc;
   if (!x || !pool || !ws || epoch == 0 || H < 8 || pool_rows < 0) return MOE_ERR_INVALID;
@@ -170,6 +179,7 @@ MOE355_API int moe_expert_ffn(const moe_plan_t* plan, int32_t pool_rows, const v
                               const void* w1, const void* w1_s, const void* w2, const void* w2_s, int32_t H,
                               int32_t I, int32_t dtype, uint32_t epoch, void* ws, size_t ws_bytes, void* y_pool,
                               const moe_tile_config* cfg, void* stream) {
+  TraceRange trace("moe_expert_ffn");
   return expert_ffn(plan, pool_rows, pool, pool_s, w1, w1_s, w2, w2_s, H, I, dtype, epoch, ws, ws_bytes, y_pool,
                     nullptr, nullptr, nullptr, cfg, stream);
 }
@@ -179,6 +189,7 @@ MOE355_API int moe_expert_ffn_combine(const moe_plan_t* plan, int32_t pool_rows,
                                       const void* w2_s, int32_t H, int32_t I, int32_t dtype, uint32_t epoch,
                                       void* ws, size_t ws_bytes, void* y_pool, const float* topk_weights, void* out,
                                       const moe_tile_config* cfg, void* stream) {
+  TraceRange trace("moe_expert_ffn_combine");
   if (!topk_weights || !out) return MOE_ERR_INVALID;
   if (H % 8 != 0) return MOE_ERR_UNSUPPORTED;
   return expert_ffn(plan, pool_rows, pool, pool_s, w1, w1_s, w2, w2_s, H, I, dtype, epoch, ws, ws_bytes, y_pool,
@@ -188,6 +199,7 @@ MOE355_API int moe_expert_ffn_combine(const moe_plan_t* plan, int32_t pool_rows,
 MOE355_API int moe_expert_ffn_train(const moe_plan_t* plan, int32_t pool_rows, const void* pool, const void* w1,
                                     const void* w2, int32_t H, int32_t I, uint32_t epoch, void* ws, size_t ws_bytes,
                                     void* y_pool, void* g_pool, const moe_tile_config* cfg, void* stream) {
+  TraceRange trace("moe_expert_ffn_train");
   if (!g_pool) return MOE_ERR_INVALID;
   return expert_ffn(plan, pool_rows, pool, nullptr, w1, nullptr, w2, nullptr, H, I, MOE_BF16, epoch, ws, ws_bytes,
                     y_pool, nullptr, nullptr, g_pool, cfg, stream);
@@ -196,6 +208,7 @@ MOE355_API int moe_expert_ffn_train(const moe_plan_t* plan, int32_t pool_rows, c
 MOE355_API int moe_combine_backward(const void* dout, const float* topk_weights, const void* y_pool,
                                     int32_t pool_rows, const moe_plan_t* plan, int32_t H, void* dy_pool,
                                     float* d_topk_weights, void* stream) {
+  TraceRange trace("moe_combine_backward");
   int rc = check_plan(plan);
   if (rc != MOE_OK) return rc;
   if (!dout || !topk_weights || !y_pool || !dy_pool || !d_topk_weights || H < 8 || pool_rows < 0)
@@ -210,6 +223,7 @@ MOE355_API int moe_expert_ffn_backward(const moe_plan_t* plan, int32_t pool_rows
                                        const void* dy_pool, void* g_pool, const void* w1t, const void* w2t, int32_t H,
                                        int32_t I, void* ws, size_t ws_bytes, void* dx_pool, void* dw1, void* dw2,
                                        const moe_tile_config* cfg, void* stream) {
+  TraceRange trace("moe_expert_ffn_backward");
   int rc = check_plan(plan);
   if (rc != MOE_OK) return rc;
   if (!pool || !dy_pool || !g_pool || !w1t || !w2t || !ws || !dx_pool || !dw1 || !dw2 || H < 1 || I < 1)
@@ -241,6 +255,7 @@ MOE355_API int moe_expert_ffn_backward(const moe_plan_t* plan, int32_t pool_rows
 
 MOE355_API int moe_dispatch_backward(const void* dx_pool, int32_t pool_rows, const moe_plan_t* plan, int32_t H,
                                      void* dx, void* stream) {
+  TraceRange trace("moe_dispatch_backward");
   int rc = check_plan(plan);
   if (rc != MOE_OK) return rc;
   if (!dx_pool || !dx || H < 8 || pool_rows < 0) return MOE_ERR_INVALID;
@@ -251,6 +266,7 @@ MOE355_API int moe_dispatch_backward(const void* dx_pool, int32_t pool_rows, con
 
 MOE355_API int moe_combine(const void* y_pool, int32_t pool_rows, const float* topk_weights,
                            const moe_plan_t* plan, int32_t H, void* out, void* stream) {
+  TraceRange trace("moe_combine");
   int rc = check_plan(plan);
   if (rc != MOE_OK) return rc;
   if (!y_pool || !topk_weights || !out || H < 8 || pool_rows < 0) return MOE_ERR_INVALID;
@@ -261,6 +277,7 @@ MOE355_API int moe_combine(const void* y_pool, int32_t pool_rows, const float* t
 
 MOE355_API int moe_pack_weights(const void* w, int32_t E, int32_t rows, int32_t K, int32_t dtype, void* out,
                                 void* stream) {
+  TraceRange trace("moe_pack_weights");
   if (!w || !out || E < 1 || rows < 1 || K < 1) return MOE_ERR_INVALID;
   if (dtype != MOE_BF16 && dtype != MOE_FP8_E4M3_G128 && dtype != MOE_MXFP4) return MOE_ERR_INVALID;
   if (rows % 16 != 0 || K % (dtype == MOE_BF16 ? 32 : 128) != 0) return MOE_ERR_UNSUPPORTED;
@@ -274,6 +291,7 @@ MOE355_API int moe_pack_weights(const void* w, int32_t E, int32_t rows, int32_t 
 
 MOE355_API int moe_pack_weights_transposed(const void* w, int32_t E, int32_t rows, int32_t K, int32_t dtype,
                                            void* out, void* stream) {
+  TraceRange trace("moe_pack_weights_transposed");
   if (!w || !out || E < 1 || rows < 1 || K < 1) return MOE_ERR_INVALID;
   if (dtype != MOE_BF16) return dtype == MOE_FP8_E4M3_G128 || dtype == MOE_MXFP4 ? MOE_ERR_UNSUPPORTED : MOE_ERR_INVALID;
   if (K % 16 != 0 || rows % 32 != 0) return MOE_ERR_UNSUPPORTED;
@@ -286,6 +304,7 @@ MOE355_API int moe_pack_weights_transposed(const void* w, int32_t E, int32_t row
 }
 
 MOE355_API int moe_pack_mx_scales(const void* s, int32_t E, int32_t rows, int32_t K, void* out, void* stream) {
+  TraceRange trace("moe_pack_mx_scales");
   if (!s || !out || E < 1 || rows < 1 || K < 1) return MOE_ERR_INVALID;
   if (rows % 16 != 0 || K % 128 != 0) return MOE_ERR_UNSUPPORTED;
   const int64_t bytes = (int64_t)rows * (K / 32);
@@ -294,6 +313,25 @@ MOE355_API int moe_pack_mx_scales(const void* s, int32_t E, int32_t rows, int32_
   const char* b = static_cast<const char*>(out);
   if (a < b + bytes * E && b < a + bytes * E) return MOE_ERR_INVALID;  // overlap
   return launch_pack_mx_scales(s, E, rows, K, out, static_cast<hipStream_t>(stream));
+}
+
+MOE355_API int moe_calibrate_mfma(int32_t iters, float* sink, int32_t workgroups, void* stream) {
+  if (!sink || iters < 1 || workgroups < 1 || workgroups > 65535) return MOE_ERR_INVALID;
+  TraceRange trace("moe_calibrate_mfma");
+  return launch_calibrate_mfma(iters, sink, workgroups, static_cast<hipStream_t>(stream));
+}
+
+MOE355_API int moe_calibrate_stream(const void* src, void* dst, int64_t bytes, int32_t mode, uint32_t* sink,
+                                    int32_t workgroups, void* stream) {
+  if (bytes < 16 || bytes % 16 != 0 || workgroups < 1 || workgroups > 65535) return MOE_ERR_INVALID;
+  if (mode == 0 ? (!src || !sink) : mode == 1 ? !dst : mode == 2 ? (!src || !dst) : true) return MOE_ERR_INVALID;
+  if (mode == 2) {
+    const char* a = static_cast<const char*>(src);
+    const char* b = static_cast<const char*>(dst);
+    if (a < b + bytes && b < a + bytes) return MOE_ERR_INVALID;  // overlap
+  }
+  TraceRange trace("moe_calibrate_stream");
+  return launch_calibrate_stream(src, dst, bytes, mode, sink, workgroups, static_cast<hipStream_t>(stream));
 }
 
 MOE355_API int moe_get_error(void* ws, size_t ws_bytes, void* stream) {

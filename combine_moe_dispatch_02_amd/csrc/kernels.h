@@ -7,6 +7,9 @@
 
 namespace moe {
 
+// shape and pointer checks of a moe_plan_t (abi.hip)
+int check_plan(const moe_plan_t* p);
+
 int launch_plan(const int32_t* topk_idx, const moe_plan_t& p, const WsLayout& L, char* ws,
                 hipStream_t stream);
 
@@ -102,5 +105,10 @@ int launch_pack_weights_t(const void* w, int32_t E, int32_t rows, int32_t K, voi
 int launch_pack_mx_scales(const void* s, int32_t E, int32_t rows, int32_t K, void* out, hipStream_t stream);
 
 int device_cu_count();
+
+// calib.hip
+int launch_calibrate_mfma(int32_t iters, float* sink, int32_t workgroups, hipStream_t stream);
+int launch_calibrate_stream(const void* src, void* dst, int64_t bytes, int32_t mode, uint32_t* sink,
+                            int32_t workgroups, hipStream_t stream);
 
 }  // namespace moe

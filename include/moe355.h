@@ -360,6 +360,23 @@ MOE355_API int moe_pack_weights_transposed(const void* w, int32_t E, int32_t row
  */
 MOE355_API int moe_pack_mx_scales(const void* s, int32_t E, int32_t rows, int32_t K, void* out, void* stream);
 
+/*
+ * Measurement helpers (not part of a layer call): the rates the layer's roofline
+ * fractions are read against, measured on the current device.
+ * moe_calibrate_mfma: `workgroups` workgroups of 8 waves each issue `iters` x 16
+ * back-to-back v_mfma_f32_16x16x32_bf16 (16 384 flops each) on register operands, i.e.
+ * workgroups * 8 * iters * 16 * 16384 flops. sink: device float [workgroups * 512],
+ * overwritten (it only keeps the result alive).
+ * moe_calibrate_stream: one grid-stride pass of `workgroups` x 256 threads over `bytes`
+ * (a multiple of 16) with 16-byte accesses: mode 0 reads src (sink: device uint32
+ * [workgroups * 256]), 1 writes dst, 2 copies src to dst (non-overlapping).
+ * Errors: MOE_ERR_INVALID (null pointers the mode needs, iters < 1, workgroups not in
+ * [1, 65535], bytes < 16 or not a multiple of 16, unknown mode).
+ */
+MOE355_API int moe_calibrate_mfma(int32_t iters, float* sink, int32_t workgroups, void* stream);
+MOE355_API int moe_calibrate_stream(const void* src, void* dst, int64_t bytes, int32_t mode, uint32_t* sink,
+                                    int32_t workgroups, void* stream);
+
 /* Waits for `stream`, returns the first error recorded on the device in the
  * workspace since the last call (MOE_OK if none) and clears it. */
 MOE355_API int moe_get_error(void* ws, size_t ws_bytes, void* stream);

@@ -28,7 +28,7 @@ def lib():
 def test_header_declares_the_four_calls():
     names = set(declared_symbols())
     assert {"moe_plan", "moe_dispatch", "moe_expert_ffn", "moe_combine"} <= names
-    assert len(names) == 18
+    assert len(names) == 20
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -278,3 +278,28 @@ def test_pack_mx_scales_validation(lib):
 
 def test_get_error_validation(lib):
     assert lib.moe_get_error(None, 1 << 20, None) == 1
+
+
+def test_calibration_validation(lib):
+    # the measurement helpers reject bad arguments before any launch
+    S = ctypes.c_void_p(0x10000)
+    assert lib.moe_calibrate_mfma(0, S, 8, None) == 1            # iters >= 1
+    assert lib.moe_calibrate_mfma(10, None, 8, None) == 1        # sink needed
+    assert lib.moe_calibrate_mfma(10, S, 0, None) == 1           # workgroups in [1, 65535]
+    assert lib.moe_calibrate_mfma(10, S, 65536, None) == 1
+    A, B = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000)
+    assert lib.moe_calibrate_stream(A, None, 100, 0, S, 8, None) == 1       # not whole 16-byte chunks
+    assert lib.moe_calibrate_stream(None, None, 1024, 0, S, 8, None) == 1   # read needs src and sink
+    assert lib.moe_calibrate_stream(A, None, 1024, 0, None, 8, None) == 1
+    assert lib.moe_calibrate_stream(None, None, 1024, 1, None, 8, None) == 1  # write needs dst
+    assert lib.moe_calibrate_stream(A, None, 1024, 2, None, 8, None) == 1     # copy needs both
+    assert lib.moe_calibrate_stream(A, ctypes.c_void_p(0x100100), 1024, 2, None, 8, None) == 1  # overlap
+    assert lib.moe_calibrate_stream(A, B, 1024, 3, S, 8, None) == 1         # unknown mode
+
+
+def test_package_exports_the_binding():
+    # every name the binding lists is importable from the package
+    import combine_moe_dispatch_02_amd as moe
+    from combine_moe_dispatch_02_amd import layer
+    missing = [n for n in layer.__all__ if not hasattr(moe, n)]
+    assert not missing, missing
