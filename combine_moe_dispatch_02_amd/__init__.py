@@ -29,6 +29,7 @@ from .layer import (  # noqa: F401
     moe_pack_mx_scales,
     moe_pack_weights,
     moe_plan,
+    moe_plan_noalloc,
     moe_query_pool_rows,
     pool_rows_upper_bound,
     stream_moe,

@@ -73,6 +73,7 @@ SIGNATURES = [
     ("moe_pool_rows_upper_bound", _SZ, [_I32, _I32, _I32, _I32]),
     ("moe_workspace_bytes", _SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     ("moe_plan", ctypes.c_int, [_VP, _PP, _VP, _SZ, _VP]),
+    ("moe_plan_noalloc", ctypes.c_int, [_VP, _PP, _VP]),
     ("moe_query_pool_rows", ctypes.c_int, [_PP, ctypes.POINTER(_I32), _VP]),
     ("moe_dispatch", ctypes.c_int, [_VP, _I32, _I32, _PP, _I32, _VP, _VP, _U32, _VP, _SZ, _VP]),
     ("moe_expert_ffn", ctypes.c_int,

@@ -20,6 +20,8 @@
 //           base[c][e] + (pairs of e earlier in the column), with the in-wave
 //           part from mbcnt over the group mask. Writes pos and src.
 // With a single block both passes run in one launch.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -285,4 +287,49 @@ int launch_plan(const int32_t* topk_idx, const moe_plan_t& p, const WsLayout& L,
   return MOE_OK;
 }
 
+// ----------------------------------------------------------------------------
+// moe_plan_noalloc: moe_plan with its scratch (the per-column histogram and the blocks'
+// completion counter) in a file-scope device array instead of a caller's workspace.
+// Every call on a device shares that device's array.
+// ----------------------------------------------------------------------------
+constexpr size_t kPlanScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) uint8_t scratch[kPlanScratchBytes];
+
+// the array's device address, looked up once per device with that device current
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[1024];
+
+static void* plan_scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 1024) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+// the completion counter starts at zero (a kernel, not a memset, so the call can be captured
+// in a graph)
+__global__ void zero_word_kernel(uint32_t* w) { *w = 0u; }
+
 }  // namespace moe
+
+extern "C" MOE355_API int moe_plan_noalloc(const int32_t* topk_idx, const moe_plan_t* plan, void* stream) {
+  using namespace moe;
+  int rc = check_plan(plan);
+  if (rc != MOE_OK) return rc;
+  if (!topk_idx) return MOE_ERR_INVALID;
+  WsLayout L = ws_layout(plan->T, plan->K, plan->E_local, plan->tile, 0, 0, MOE_BF16);
+  if (L.hist + (size_t)L.ncols * plan->E_local * 4 > kPlanScratchBytes) return MOE_ERR_UNSUPPORTED;
+  char* base = static_cast<char*>(plan_scratch_ptr());
+  if (base == nullptr) return MOE_ERR_HIP;
+  // no layer workspace: nothing is prepared for moe_dispatch (no fill counters to clear)
+  L.ntiles_cap = 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(zero_word_kernel, dim3(1), dim3(1), 0, s, reinterpret_cast<uint32_t*>(base + L.done));
+  if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
+  return launch_plan(topk_idx, *plan, L, base, s);
+}

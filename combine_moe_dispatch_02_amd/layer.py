@@ -20,7 +20,7 @@ from ._abi import (MOE_BF16, MOE_FP8_E4M3_G128, MOE_MXFP4, MOE_WEIGHTS_MFMA_TILE
 
 __all__ = [
     "MOE_BF16", "MOE_FP8_E4M3_G128", "MOE_MXFP4", "MoeError", "Plan", "Workspace", "TileConfig",
-    "pool_rows_upper_bound", "workspace_bytes", "moe_plan", "moe_query_pool_rows",
+    "pool_rows_upper_bound", "workspace_bytes", "moe_plan", "moe_plan_noalloc", "moe_query_pool_rows",
     "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_combine", "moe_combine", "moe_get_error",
     "moe_pack_weights",
     "moe_pack_mx_scales", "moe_expert_ffn_train", "moe_combine_backward", "moe_expert_ffn_backward",
@@ -135,6 +135,16 @@ def moe_plan(topk_idx: torch.Tensor, plan: Plan, ws: Workspace, stream=None) -> 
     c = plan.c()
     check("moe_plan", load().moe_plan(_vp(topk_idx), ctypes.byref(c), _vp(ws.buf), ws.nbytes,
                                       _stream(stream)))
+
+
+def moe_plan_noalloc(topk_idx: torch.Tensor, plan: Plan, stream=None) -> None:
+    """moe_plan with the library's own device scratch instead of a workspace (nothing is
+    allocated; calls that overlap on one device race)."""
+    _need_cuda(topk_idx, "topk_idx", torch.int32)
+    if topk_idx.shape != (plan.T, plan.K):
+        raise ValueError(f"topk_idx shape {tuple(topk_idx.shape)} != {(plan.T, plan.K)}")
+    c = plan.c()
+    check("moe_plan_noalloc", load().moe_plan_noalloc(_vp(topk_idx), ctypes.byref(c), _stream(stream)))
 
 
 def moe_query_pool_rows(plan: Plan, stream=None) -> int:

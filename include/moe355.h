@@ -158,6 +158,24 @@ MOE355_API size_t moe_workspace_bytes(int32_t T, int32_t K, int32_t E_local, int
 MOE355_API int moe_plan(const int32_t* topk_idx, const moe_plan_t* plan, void* ws, size_t ws_bytes,
                         void* stream);
 
+/*
+ * moe_plan without a workspace, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same plan arrays, with the same values, as moe_plan. Its scratch (the per-column
+ * histogram and the blocks' completion counter) lives in a 4 MiB device array inside
+ * the library, one per device, held until the process ends; it allocates nothing and
+ * calls no allocating routine. The scratch needed is 256 + 4 * E_local * ceil(T*K / p)
+ * bytes, p = 256 pairs per column when T*K <= 4096, else 1024 (e.g. T*K up to 1 048 576
+ * pairs for E_local <= 1020). Every call on a device shares that device's array: calls
+ * that overlap on one device (on different streams, or from different host threads)
+ * race and must be ordered by the caller. Unlike moe_plan it prepares no workspace for
+ * moe_dispatch (a layer workspace's fill counters are not cleared): a caller that
+ * dispatches uses moe_plan with its workspace.
+ * Errors: those of moe_plan (except the workspace size); MOE_ERR_UNSUPPORTED when the
+ * scratch needed exceeds 4 MiB; MOE_ERR_HIP when the array's address cannot be found.
+ */
+MOE355_API int moe_plan_noalloc(const int32_t* topk_idx, const moe_plan_t* plan, void* stream);
+
 /* The one host sync of the layer (README, "Caller-owned streams"): waits for
  * `stream`, then copies offsets[E_local] (= P, the pool rows in use) to *host_P. */
 MOE355_API int moe_query_pool_rows(const moe_plan_t* plan, int32_t* host_P, void* stream);

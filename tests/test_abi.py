@@ -28,7 +28,7 @@ def lib():
 def test_header_declares_the_four_calls():
     names = set(declared_symbols())
     assert {"moe_plan", "moe_dispatch", "moe_expert_ffn", "moe_combine"} <= names
-    assert len(names) == 20
+    assert len(names) == 21
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -295,6 +295,19 @@ def test_calibration_validation(lib):
     assert lib.moe_calibrate_stream(A, None, 1024, 2, None, 8, None) == 1     # copy needs both
     assert lib.moe_calibrate_stream(A, ctypes.c_void_p(0x100100), 1024, 2, None, 8, None) == 1  # overlap
     assert lib.moe_calibrate_stream(A, B, 1024, 3, S, 8, None) == 1         # unknown mode
+
+
+def test_plan_noalloc_validation(lib):
+    # the allocation-free plan rejects what moe_plan rejects, and a plan whose histogram would
+    # not fit its 4 MiB scratch, before any launch
+    p = _fake_plan(T=0)
+    assert lib.moe_plan_noalloc(ctypes.c_void_p(0x8000), ctypes.byref(p), None) == _abi.MOE_ERR_INVALID
+    p = _fake_plan()
+    assert lib.moe_plan_noalloc(None, ctypes.byref(p), None) == _abi.MOE_ERR_INVALID
+    # 2^20 pairs x 1024 experts: 1024 columns x 1024 x 4 bytes > 4 MiB
+    big = _fake_plan(T=1 << 17, K=8, E_local=1024, tile=128,
+                     rows_cap=oracle.pool_rows_bound(1 << 17, 8, 1024, 128))
+    assert lib.moe_plan_noalloc(ctypes.c_void_p(0x8000), ctypes.byref(big), None) == _abi.MOE_ERR_UNSUPPORTED
 
 
 def test_package_exports_the_binding():
