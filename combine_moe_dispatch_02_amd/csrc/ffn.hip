@@ -472,8 +472,8 @@ struct Big {
   static constexpr int kALoads = (kAChunks + kThreads - 1) / kThreads;
 };
 
-// Combine on completion (StreamEP README, "How it works": combine starts on a token
-// as soon as its compute is done). After its last GEMM Y unit, a workgroup claims
+// Combine on completion (StreamEP README, "How it works": a token's combine need not
+// wait for the whole FFN, only for the expert outputs it reads). After its last GEMM Y unit, a workgroup claims
 // items of one token per wave from a device-wide counter. A wave waits until every
 // pool tile holding one of its token's pairs has all its GEMM Y units counted (an
 // acquire after the counts), then does the token's weighted gather-sum exactly as

@@ -3,14 +3,15 @@
  * on MI355X (gfx950).
  *
  * The layer is the streaming MoE layer of the StreamEP README ("How it works"):
- *   - pool-layout dispatch: each routed (token, k) pair lands in an expert-major,
- *     tile-padded pool, so dispatch's output is the grouped GEMM's input with no
- *     separate permute;
- *   - per-tile streaming: dispatch signals each pool tile as it fills and the
- *     expert GEMMs claim ready tiles;
- *   - caller-owned streams: the layer runs on a compute stream and a
- *     communicate stream that the caller supplies; the only host sync is an
- *     optional poll that sizes the pool;
+ *   - pool-layout dispatch: every routed (token, k) pair is written straight
+ *     into its expert's segment of one pool, segments padded to whole GEMM
+ *     tiles, and that pool is what the grouped GEMM reads (no permute pass);
+ *   - per-tile streaming: a flag per pool tile is raised once the tile's rows
+ *     are written, and the GEMM's work units wait on those flags, so compute
+ *     can start on full tiles while others are still being written;
+ *   - caller-owned streams: the caller hands in the streams (one for compute,
+ *     one for the data movement); at most one host synchronisation per layer,
+ *     the optional read-back of the pool size;
  *   - the forward grouped GEMMs "A" (w1, gate|up, then SwiGLU) and "Y" (w2);
  *   - combine: each token's expert outputs are reduced with its topk_weights.
  *
@@ -181,7 +182,8 @@ MOE355_API int moe_plan_noalloc(const int32_t* topk_idx, const moe_plan_t* plan,
 MOE355_API int moe_query_pool_rows(const moe_plan_t* plan, int32_t* host_P, void* stream);
 
 /*
- * A2. Dispatch: pool[pos[t,k]] = x[t] for every local pair (device x bf16 [T][H]).
+ * A2. Dispatch (StreamEP README, "How it works": pool-layout dispatch and per-tile
+ * streaming): pool[pos[t,k]] = x[t] for every local pair (device x bf16 [T][H]).
  * bf16: pool is bf16 [pool_rows][H] and pool_s must be NULL.
  * fp8:  pool is e4m3 [pool_rows][H] and pool_s holds pool_rows * H/128 fp32
  *       scale words; each 1x128 group g of x[t] is stored as codes e4m3(x/s) with
@@ -210,7 +212,9 @@ MOE355_API int moe_dispatch(const void* x, int32_t H, int32_t act_dtype, const m
                             void* ws, size_t ws_bytes, void* stream);
 
 /*
- * A3 + A4. Expert FFN over the pool, as a persistent grouped GEMM on MFMA:
+ * A3 + A4. Expert FFN over the pool (StreamEP README, "How it works": the forward
+ * grouped GEMMs A and Y of the compute kernels, fed tile by tile under per-tile
+ * streaming), as a persistent grouped GEMM on MFMA:
  *   GEMM A: g = pool_tile . w1[e]^T (fp32 accumulate), h = silu(g_gate) * g_up,
  *           silu(z) = z / (1 + exp(-z)); h is stored as bf16 (bf16 mode), as
  *           e4m3 + one fp32 scale per 1x128 group (fp8 mode), or as MXFP8 like
@@ -231,8 +235,10 @@ MOE355_API int moe_dispatch(const void* x, int32_t H, int32_t act_dtype, const m
  * pool_rows not a multiple of tile, a moe_tile_config field out of its range),
  * MOE_ERR_UNSUPPORTED (bf16: H % 128 or
  * I % 64 nonzero; fp8: H % 256 or I % 128 nonzero, or tile < 64; tiled weights:
- * bf16 with tile 64 or 128, H % 512 == 0 and I % 256 == 0 only; mxfp4: tiled
- * weights, tile 128, H % 512 == 0 and I % 256 == 0 only).
+ * bf16 with tile 128, H % 256 == 0 and I % 128 == 0 (256-row units), or with tile
+ * 64 or 128, H % 512 == 0 and I % 256 == 0 (one-tile units), only; mxfp4: tiled
+ * weights, tile 128, H % 512 == 0 and I % 256 == 0 only; unit_rows 256 outside the
+ * 256-row units' shapes).
  */
 MOE355_API int moe_expert_ffn(const moe_plan_t* plan, int32_t pool_rows, const void* pool,
                               const void* pool_s, const void* w1, const void* w1_s, const void* w2,
@@ -241,8 +247,8 @@ MOE355_API int moe_expert_ffn(const moe_plan_t* plan, int32_t pool_rows, const v
                               void* stream);
 
 /*
- * A3 + A4 + A5 with combine on completion (StreamEP README, "How it works": combine
- * starts on a token as soon as its compute is done). Does what moe_expert_ffn
+ * A3 + A4 + A5 with combine on completion (StreamEP README, "How it works": a
+ * token's combine waits only for its own expert outputs, not the whole FFN). Does what moe_expert_ffn
  * followed by moe_combine(y_pool, pool_rows, topk_weights, plan, H, out) on the same
  * stream does, with the same bits in out and y_pool. When GEMM Y runs on the big-tile
  * kernel (block N 512), each of its work units publishes the tile's progress in the
@@ -321,7 +327,9 @@ MOE355_API int moe_dispatch_backward(const void* dx_pool, int32_t pool_rows, con
                                      void* dx, void* stream);
 
 /*
- * A5. Combine: out[t] = sum over k with pos[t,k] >= 0, in ascending k, of
+ * A5. Combine (StreamEP README, "How it works": combine, the reduction of each
+ * token's expert outputs with its routing weights; the usage sample's topk_weights):
+ * out[t] = sum over k with pos[t,k] >= 0, in ascending k, of
  * topk_weights[t,k] * y_pool[pos[t,k]], accumulated in fp32 and stored bf16
  * (round to nearest even). Every row of out (bf16 [T][H]) is written; a token
  * with no local pair gets zeros. Weights are not renormalised.
