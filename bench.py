@@ -201,12 +201,17 @@ def summarize_profiles(workload, trace_dir, fetch_dir, write_dir, out_dir, comma
     for d, cname in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
         rows = [r for r in _read_csv(os.path.join(d, "run_counter_collection.csv")) if r["Counter_Name"] == cname]
         copies = sorted((float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]),
-                        reverse=True)[:3]
-        scale = (1 << 20) / (sum(copies) / len(copies))  # KiB of a 1 GiB copy -> bytes factor
+                        reverse=True)
+        scale = (1 << 20) / (sum(copies[:3]) / 3)  # KiB of a 1 GiB copy -> bytes factor
+        # the 256 MiB copies, where the run made them (a reading near a quarter of the 1 GiB
+        # one): the factor should not depend on the size
+        quarter = sum(copies[:3]) / 12
+        small = [c for c in copies[3:] if abs(c - quarter) < 0.2 * quarter][:3]
+        scale_small = (1 << 18) / (sum(small) / len(small)) if len(small) == 3 else None
         agg = collections.defaultdict(list)
         for r in rows:
             agg[r["Kernel_Name"]].append(float(r["Counter_Value"]) * 1024 * scale)
-        per[cname] = ({k: sum(v) / len(v) for k, v in agg.items()}, scale)
+        per[cname] = ({k: sum(v) / len(v) for k, v in agg.items()}, scale, scale_small)
     ffn = [r for r in stats if "ffn_" in r["Name"]]
     ffn_ns = sum(float(r["AverageNs"]) for r in ffn)
     fetch = sum(v for k, v in per["FETCH_SIZE"][0].items() if "ffn_" in k)
@@ -224,8 +229,13 @@ def summarize_profiles(workload, trace_dir, fetch_dir, write_dir, out_dir, comma
         lines.append(f"{_short(n):70s} {r['Calls']:>6s} {float(r['AverageNs'])/1e3:10.1f} "
                      f"{float(r['MinNs'])/1e3:10.1f} {float(r['MaxNs'])/1e3:10.1f} "
                      f"{(fv or 0)/1e6:10.1f} {(wv or 0)/1e6:10.1f}")
-    lines += ["", f"FETCH_SIZE scale (1 GiB copy): x{per['FETCH_SIZE'][1]:.3f} of the KiB reading; "
-              f"WRITE_SIZE scale: x{per['WRITE_SIZE'][1]:.3f}"]
+    def _sc(c):
+        s1, s2 = per[c][1], per[c][2]
+        return f"x{s1:.3f}" + (f" (256 MiB copy: x{s2:.3f})" if s2 else "")
+    lines += ["", f"fetch_MB / write_MB: FETCH_SIZE / WRITE_SIZE, the bytes the L2 requested from / wrote to the",
+              f"memory fabric (L2 misses; Infinity Cache hits included), scaled to bytes by what the counters",
+              f"read for a device copy of known size: FETCH_SIZE {_sc('FETCH_SIZE')} of the KiB reading "
+              f"(1 GiB copy), WRITE_SIZE {_sc('WRITE_SIZE')}."]
     os.makedirs(out_dir, exist_ok=True)
     if train:
         lines += ["The training step's kernels, by template: ffn_big_kernel<..., GEMM_A=true, ...> is the",
@@ -239,7 +249,7 @@ def summarize_profiles(workload, trace_dir, fetch_dir, write_dir, out_dir, comma
         print(txt)
         return
     lines.append(f"expert FFN (all ffn_ kernels of one call): {ffn_ns/1e3:.1f} us, "
-                 f"HBM fetch {fetch/1e9:.3f} GB + write {write/1e9:.3f} GB per call")
+                 f"L2-miss fetch {fetch/1e9:.3f} GB + write {write/1e9:.3f} GB per call")
     txt = os.path.join(out_dir, f"moe_layer_{workload}.txt")
     with open(txt, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -248,7 +258,10 @@ def summarize_profiles(workload, trace_dir, fetch_dir, write_dir, out_dir, comma
         json.dump({"workload": workload, "ffn_source_sha256_16": kernel_source_hash(),
                    "hbm_bytes_per_ffn_call": fetch + write, "fetch_bytes": fetch, "write_bytes": write,
                    "ffn_avg_us": ffn_ns / 1e3, "fetch_scale": per["FETCH_SIZE"][1],
-                   "write_scale": per["WRITE_SIZE"][1], "commands": commands}, f, indent=1)
+                   "write_scale": per["WRITE_SIZE"][1], "fetch_scale_256MiB": per["FETCH_SIZE"][2],
+                   "write_scale_256MiB": per["WRITE_SIZE"][2],
+                   "counts": "FETCH_SIZE / WRITE_SIZE: L2-to-memory-fabric bytes (Infinity Cache hits included)",
+                   "commands": commands}, f, indent=1)
     print(txt)
     print(js)
 
@@ -278,9 +291,11 @@ def train_bench(args, cfg):
     torch.cuda.synchronize()
     work = algorithmic_work(cfg, inp.topk_idx.numpy())
 
+    streams = moe.make_streams() if args.streams else None
+
     def step():
-        layer.forward(x, idx, w, w1, w2)
-        return layer.backward(dout, w, w1t, w2t)
+        layer.forward(x, idx, w, w1, w2, streams=streams)
+        return layer.backward(dout, w, w1t, w2t, streams=streams)
 
     for _ in range(args.warmup):
         step()
@@ -312,8 +327,10 @@ def train_bench(args, cfg):
         moe.moe_expert_ffn_train(layer.plan, layer.pool, w1, w2, ep, layer.ws, layer.y_pool, layer.g_pool,
                                  layer.cfg, s); ev[3].record(s)
         moe.moe_combine(layer.y_pool, w, layer.plan, layer.out, s); ev[4].record(s)
-        moe.moe_combine_backward(dout, w, layer.y_pool, layer.plan, layer.y_pool, layer.dw, s); ev[5].record(s)
-        moe.moe_expert_ffn_backward(layer.plan, layer.pool, layer.y_pool, layer.g_pool, w1t, w2t, layer.ws,
+        eb = layer.next_epoch()
+        moe.moe_combine_backward(dout, w, layer.y_pool, layer.plan, layer.y_pool, layer.dw, eb, layer.ws, s)
+        ev[5].record(s)
+        moe.moe_expert_ffn_backward(layer.plan, layer.pool, layer.y_pool, layer.g_pool, w1t, w2t, eb, layer.ws,
                                     layer.dx_pool, dw1, dw2, layer.cfg, s); ev[6].record(s)
         moe.moe_dispatch_backward(layer.dx_pool, layer.plan, layer.dx, s); ev[7].record(s)
         evs.append(ev)
@@ -335,7 +352,8 @@ def train_bench(args, cfg):
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "I": cfg.I, "experts": cfg.num_experts,
                    "local_experts": cfg.num_local_experts, "K": cfg.K, "tile": cfg.tile, "routing": cfg.routing,
-                   "pairs": work["pairs"], "mode": "training step (forward keeping G + backward)"},
+                   "pairs": work["pairs"], "mode": "training step (forward keeping G + backward)",
+                   "streams": "two (comm + compute)" if args.streams else "one"},
         "roofline": {"bound": "mfma", "kernel": "backward grouped GEMMs (dgrad + wgrad of A and Y)",
                      "achieved": round(bwd_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
@@ -345,6 +363,52 @@ def train_bench(args, cfg):
         "cpu_baseline": None,
     }
     print(json.dumps(result), flush=True)
+
+
+def summarize_counters(workload, pmc_dirs, out_dir, commands):
+    """rocprofv3 --pmc CSV output (one directory per counter pass) -> the per-kernel counter
+    averages of the GEMM kernels with the rates read from them, in
+    profiles/ffn_counters_<workload>.txt."""
+    import collections
+
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    for d in pmc_dirs:
+        for r in _read_csv(os.path.join(d, "run_counter_collection.csv")):
+            vals[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    lines = [f"# rocprofv3 counters: GEMM kernels, workload {workload}", "",
+             "Commands (from the repository root on one MI355X):"]
+    lines += [f"  {c}" for c in commands]
+    lines += ["", "Values are per dispatch, averaged over the run's dispatches, summed over XCDs and CUs.",
+              "GRBM_GUI_ACTIVE sums the 8 XCDs (cycles = GRBM_GUI_ACTIVE / 8); 1024 SIMDs, 256 CUs.", ""]
+    for k, cs in vals.items():
+        if not any(s in k for s in ("ffn_", "wgrad")):
+            continue
+        avg = {c: sum(v) / len(v) for c, v in cs.items()}
+        lines.append(_short(k))
+        for c in sorted(avg):
+            lines.append(f"  {c:30s} {avg[c]:.4g}")
+        cyc = avg.get("GRBM_GUI_ACTIVE", 0) / 8
+        notes = []
+        if cyc and "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+            notes.append(f"MFMA busy {avg['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * 1024):.1%} of SIMD cycles")
+        if "SQ_WAIT_INST_ANY" in avg and avg.get("SQ_WAVE_CYCLES"):
+            notes.append(f"waves waiting {avg['SQ_WAIT_INST_ANY'] / avg['SQ_WAVE_CYCLES']:.1%} of wave cycles")
+        if cyc and "SQ_LDS_BANK_CONFLICT" in avg:
+            notes.append(f"LDS bank-conflict cycles {avg['SQ_LDS_BANK_CONFLICT'] / (cyc * 256):.1%} of CU cycles")
+        if "TCC_HIT" in avg and "TCC_MISS" in avg:
+            notes.append(f"L2 hit rate {avg['TCC_HIT'] / (avg['TCC_HIT'] + avg['TCC_MISS']):.1%}")
+        if cyc and "TCP_PENDING_STALL_CYCLES" in avg:
+            notes.append(f"TCP pending-stall {avg['TCP_PENDING_STALL_CYCLES'] / (cyc * 256):.1%} of CU cycles")
+        if cyc and "TA_BUSY_avr" in avg:
+            notes.append(f"TA busy {avg['TA_BUSY_avr'] / cyc:.1%}")
+        if notes:
+            lines.append("  -> " + "; ".join(notes))
+        lines.append("")
+    os.makedirs(out_dir, exist_ok=True)
+    txt = os.path.join(out_dir, f"ffn_counters_{workload}.txt")
+    with open(txt, "w") as f:
+        f.write("\n".join(lines))
+    print(txt)
 
 
 def main():
@@ -380,8 +444,15 @@ def main():
                          "the FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/ summaries from rocprofv3 CSV output and exit (no GPU)")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="PMC_DIR",
+                    help="write profiles/ffn_counters_<workload>.txt from rocprofv3 --pmc CSV output and "
+                         "exit (no GPU)")
     ap.add_argument("--profile-commands", default="", help="';'-separated commands recorded in the summary")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(args.workload, args.summarize_counters, os.path.join(ROOT, "profiles"),
+                           [c.strip() for c in args.profile_commands.split(";") if c.strip()])
+        return
     if args.summarize_profiles:
         summarize_profiles(args.workload, *args.summarize_profiles, os.path.join(ROOT, "profiles"),
                            [c.strip() for c in args.profile_commands.split(";") if c.strip()], train=args.train)
@@ -399,10 +470,12 @@ def main():
 
     cfg = config_by_name(args.workload)
     if args.copy_calibration:
+        # three 1 GiB copies, then three 256 MiB ones: two known sizes for the byte counters
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0").fill_(1)
         dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
+        for n in (1 << 30, 1 << 28):
+            for _ in range(3):
+                dst[:n].copy_(src[:n])
         torch.cuda.synchronize()
         del src, dst
     if args.train:

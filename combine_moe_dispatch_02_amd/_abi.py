@@ -84,9 +84,10 @@ SIGNATURES = [
       ctypes.POINTER(TileConfig), _VP]),
     ("moe_expert_ffn_train", ctypes.c_int,
      [_PP, _I32, _VP, _VP, _VP, _I32, _I32, _U32, _VP, _SZ, _VP, _VP, ctypes.POINTER(TileConfig), _VP]),
-    ("moe_combine_backward", ctypes.c_int, [_VP, _VP, _VP, _I32, _PP, _I32, _VP, _VP, _VP]),
+    ("moe_combine_backward", ctypes.c_int, [_VP, _VP, _VP, _I32, _PP, _I32, _VP, _VP, _U32, _VP, _SZ, _VP]),
     ("moe_expert_ffn_backward", ctypes.c_int,
-     [_PP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _VP, _SZ, _VP, _VP, _VP, ctypes.POINTER(TileConfig), _VP]),
+     [_PP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _U32, _VP, _SZ, _VP, _VP, _VP, ctypes.POINTER(TileConfig),
+      _VP]),
     ("moe_dispatch_backward", ctypes.c_int, [_VP, _I32, _PP, _I32, _VP, _VP]),
     ("moe_pack_weights_transposed", ctypes.c_int, [_VP, _I32, _I32, _I32, _I32, _VP, _VP]),
     ("moe_combine", ctypes.c_int, [_VP, _I32, _VP, _PP, _I32, _VP, _VP]),

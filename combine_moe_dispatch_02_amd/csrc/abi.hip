@@ -207,26 +207,31 @@ MOE355_API int moe_expert_ffn_train(const moe_plan_t* plan, int32_t pool_rows, c
 
 MOE355_API int moe_combine_backward(const void* dout, const float* topk_weights, const void* y_pool,
                                     int32_t pool_rows, const moe_plan_t* plan, int32_t H, void* dy_pool,
-                                    float* d_topk_weights, void* stream) {
+                                    float* d_topk_weights, uint32_t epoch, void* ws, size_t ws_bytes,
+                                    void* stream) {
   TraceRange trace("moe_combine_backward");
   int rc = check_plan(plan);
   if (rc != MOE_OK) return rc;
-  if (!dout || !topk_weights || !y_pool || !dy_pool || !d_topk_weights || H < 8 || pool_rows < 0)
+  if (!dout || !topk_weights || !y_pool || !dy_pool || !d_topk_weights || !ws || H < 8 || pool_rows < 0 ||
+      epoch == 0)
     return MOE_ERR_INVALID;
   if (H % 8 != 0) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)H * 2 > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
-  return launch_combine_backward(dout, topk_weights, y_pool, pool_rows, *plan, H, dy_pool, d_topk_weights,
-                                 static_cast<hipStream_t>(stream));
+  const WsLayout L = ws_layout(plan->T, plan->K, plan->E_local, plan->tile, pool_rows, 0, MOE_BF16);
+  if (ws_bytes < L.plan_end) return MOE_ERR_INVALID;
+  return launch_combine_backward(dout, topk_weights, y_pool, pool_rows, *plan, H, dy_pool, d_topk_weights, epoch,
+                                 L, static_cast<char*>(ws), static_cast<hipStream_t>(stream));
 }
 
 MOE355_API int moe_expert_ffn_backward(const moe_plan_t* plan, int32_t pool_rows, const void* pool,
                                        const void* dy_pool, void* g_pool, const void* w1t, const void* w2t, int32_t H,
-                                       int32_t I, void* ws, size_t ws_bytes, void* dx_pool, void* dw1, void* dw2,
-                                       const moe_tile_config* cfg, void* stream) {
+                                       int32_t I, uint32_t epoch, void* ws, size_t ws_bytes, void* dx_pool, void* dw1,
+                                       void* dw2, const moe_tile_config* cfg, void* stream) {
   TraceRange trace("moe_expert_ffn_backward");
   int rc = check_plan(plan);
   if (rc != MOE_OK) return rc;
-  if (!pool || !dy_pool || !g_pool || !w1t || !w2t || !ws || !dx_pool || !dw1 || !dw2 || H < 1 || I < 1)
+  if (!pool || !dy_pool || !g_pool || !w1t || !w2t || !ws || !dx_pool || !dw1 || !dw2 || H < 1 || I < 1 ||
+      epoch == 0)
     return MOE_ERR_INVALID;
   if (pool_rows < 1 || pool_rows % plan->tile != 0) return MOE_ERR_INVALID;
   const int32_t block_n = cfg ? cfg->block_n : 0;
@@ -235,6 +240,7 @@ MOE355_API int moe_expert_ffn_backward(const moe_plan_t* plan, int32_t pool_rows
   if ((int64_t)pool_rows * std::max(2 * I, H) * 2 >= ((int64_t)1 << 32) - 16) return MOE_ERR_UNSUPPORTED;
   if (cfg && (cfg->gemm_workgroups < 0 || cfg->unit_order < 0 || cfg->unit_order > 9)) return MOE_ERR_INVALID;
   if (cfg && cfg->a_stages != 0 && cfg->a_stages != 2 && cfg->a_stages != 4) return MOE_ERR_INVALID;
+  if (cfg && cfg->dispatch_cus < 0) return MOE_ERR_INVALID;
   const WsLayout L = ws_layout(plan->T, plan->K, plan->E_local, plan->tile, pool_rows, I, MOE_BF16);
   if (ws_bytes < L.total) return MOE_ERR_INVALID;
   char* w = static_cast<char*>(ws);
@@ -242,13 +248,19 @@ MOE355_API int moe_expert_ffn_backward(const moe_plan_t* plan, int32_t pool_rows
   const int32_t wgs = cfg ? cfg->gemm_workgroups : 0;
   const int32_t order = cfg ? cfg->unit_order : 0;
   const int32_t stages = cfg ? cfg->a_stages : 0;
-  // backward GEMM Y: dh = dy . W2 -> dG (over G), and dW2 = dy^T h
-  rc = launch_ffn_dgrad(*plan, pool_rows, dy_pool, w2t, I, H, nullptr, g_pool, I, 1, wgs, order, stages, L, w, s);
+  const int32_t leave = cfg ? cfg->dispatch_cus : 0;
+  const uint64_t us = (cfg && cfg->spin_timeout_us) ? cfg->spin_timeout_us : 2000000u;
+  const uint64_t ticks = us * 100u;  // s_memrealtime counts at 100 MHz
+  // backward GEMM Y: dh = dy . W2 -> dG (over G), each unit after its dy tile's flag; then
+  // dW2 = dy^T h
+  rc = launch_ffn_dgrad(*plan, pool_rows, dy_pool, w2t, I, H, nullptr, g_pool, I, 1, wgs, order, stages, epoch,
+                        ticks, leave, L, w, s);
   if (rc != MOE_OK) return rc;
   rc = launch_wgrad(*plan, pool_rows, dy_pool, H, w + L.h, I, dw2, wgs, s);
   if (rc != MOE_OK) return rc;
   // backward GEMM A: dx_pool = dG . W1, and dW1 = dG^T X
-  rc = launch_ffn_dgrad(*plan, pool_rows, g_pool, w1t, H, 2 * I, dx_pool, nullptr, I, 0, wgs, order, stages, L, w, s);
+  rc = launch_ffn_dgrad(*plan, pool_rows, g_pool, w1t, H, 2 * I, dx_pool, nullptr, I, 0, wgs, order, stages, 0, 0,
+                        0, L, w, s);
   if (rc != MOE_OK) return rc;
   return launch_wgrad(*plan, pool_rows, g_pool, 2 * I, pool, H, dw1, wgs, s);
 }

@@ -21,6 +21,12 @@ namespace moe {
 // --------------------------------------------------------------------------------
 // combine backward: one wave per token, 16-byte lanes. dout[t] is read once; for each
 // local pair the y row is read for the dot product and the scaled dout row is stored.
+// A block's four waves take a run of consecutive tokens, then publish them the way
+// dispatch publishes its rows (the mirror of the forward's per-tile streaming): a
+// barrier, one device-scope release by wave 0, then a relaxed count per stored pair on
+// its tile's counter; the lane whose count completes the tile's real rows resets the
+// counter (every store of this call to that tile is counted by then), acquires, and
+// stores the epoch into tile_ready with release ordering.
 // --------------------------------------------------------------------------------
 struct CombineBwdArgs {
   const uint8_t* dout;
@@ -31,6 +37,14 @@ struct CombineBwdArgs {
   int32_t pool_rows;
   uint8_t* dy;
   float* dw;
+  int32_t tile, tile_shift;
+  int32_t tokens_per_block;   // a multiple of 4
+  const int32_t* tile_expert;
+  const int32_t* offsets;
+  const int32_t* counts;
+  uint32_t* tile_fill;
+  uint32_t* tile_ready;
+  uint32_t epoch;
 };
 
 __device__ inline float wave_sum(float v) {
@@ -40,11 +54,8 @@ __device__ inline float wave_sum(float v) {
 }
 
 template <int CPL>
-__global__ __launch_bounds__(256) void combine_backward_kernel(CombineBwdArgs a) {
+__device__ inline void combine_bwd_token(const CombineBwdArgs& a, int t, int lane) {
   constexpr int KMAX = 16;
-  const int lane = lane_id();
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= a.T) return;
   const int64_t pair0 = (int64_t)t * a.K;
   int p = lane < a.K ? a.pos[pair0 + lane] : -1;
   if (p >= a.pool_rows) p = -1;
@@ -97,9 +108,36 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(CombineBwdArgs a)
   if (lane < a.K) a.dw[pair0 + lane] = mine;
 }
 
+template <int CPL>
+__global__ __launch_bounds__(256) void combine_backward_kernel(CombineBwdArgs a) {
+  const int lane = lane_id();
+  const int w = threadIdx.x >> 6;
+  const int tb = blockIdx.x * a.tokens_per_block;        // the block's first token
+  const int te = min(a.T, tb + a.tokens_per_block);
+  for (int t = tb + w; t < te; t += 4) combine_bwd_token<CPL>(a, t, lane);
+
+  __syncthreads();
+  if (w != 0) return;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  const int npairs = (te - tb) * a.K;
+  for (int q = lane; q < npairs; q += 64) {
+    const int p = a.pos[(int64_t)tb * a.K + q];
+    if (p < 0 || p >= a.pool_rows) continue;
+    const int ti = p >> a.tile_shift;
+    const uint32_t old = __hip_atomic_fetch_add(&a.tile_fill[ti], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int e = a.tile_expert[ti];
+    const int real = min(a.tile, a.offsets[e] + a.counts[e] - (ti << a.tile_shift));
+    if ((int)old + 1 == real) {
+      __hip_atomic_store(&a.tile_fill[ti], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      __hip_atomic_store(&a.tile_ready[ti], a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 int launch_combine_backward(const void* dout, const float* topk_weights, const void* y_pool, int32_t pool_rows,
-                            const moe_plan_t& p, int32_t H, void* dy_pool, float* d_topk_weights,
-                            hipStream_t stream) {
+                            const moe_plan_t& p, int32_t H, void* dy_pool, float* d_topk_weights, uint32_t epoch,
+                            const WsLayout& L, char* ws, hipStream_t stream) {
   CombineBwdArgs a;
   a.dout = static_cast<const uint8_t*>(dout);
   a.w = topk_weights;
@@ -111,8 +149,20 @@ int launch_combine_backward(const void* dout, const float* topk_weights, const v
   a.pool_rows = pool_rows;
   a.dy = static_cast<uint8_t*>(dy_pool);
   a.dw = d_topk_weights;
+  a.tile = p.tile;
+  a.tile_shift = __builtin_ctz((unsigned)p.tile);
+  a.tile_expert = p.tile_expert;
+  a.offsets = p.offsets;
+  a.counts = p.counts;
+  a.tile_fill = reinterpret_cast<uint32_t*>(ws + L.bfill);
+  a.tile_ready = p.tile_ready;
+  a.epoch = epoch;
+  // tokens per block: a multiple of the four waves, up to 64, leaving about two blocks per
+  // CU (one device-scope release per block)
+  const int cus = std::max(1, device_cu_count());
+  a.tokens_per_block = std::max(4, std::min(64, p.T / (2 * cus)) & ~3);
   const int nch = H / 8;
-  const dim3 grid((p.T + 3) / 4);
+  const dim3 grid((p.T + a.tokens_per_block - 1) / a.tokens_per_block);
   if (nch <= 64)
     hipLaunchKernelGGL(combine_backward_kernel<1>, grid, dim3(256), 0, stream, a);
   else if (nch <= 128)

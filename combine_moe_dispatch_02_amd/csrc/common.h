@@ -27,6 +27,8 @@ struct WsLayout {
   size_t tiles_done = 192;  // uint32: tiles whose ready flag dispatch has raised (plan zeroes it)
   size_t hist = 256;     // int32 [ncols][E_local]: per-wave expert counts, then bases
   size_t fill = 0;       // uint32 [ntiles_cap]: rows stored per tile by dispatch
+  size_t bfill = 0;      // uint32 [ntiles_cap], right after fill: dy rows stored per tile by
+                         // combine backward (reset by the store that completes the tile)
   size_t ydone = 0;      // uint32 [ntiles_cap]: GEMM Y units finished per tile (combine on completion)
   size_t cq = 0;         // uint32: combine items claimed (combine on completion)
   size_t h = 0;          // h [pool_rows][I]: bf16, or e4m3 codes
@@ -63,7 +65,8 @@ inline WsLayout ws_layout(int32_t T, int32_t K, int32_t E, int32_t tile, int64_t
   L.ncols = (int32_t)((pairs + L.ppw - 1) / L.ppw);
   L.ntiles_cap = (int32_t)(cap / tile);
   L.fill = align_up(L.hist + (size_t)L.ncols * E * 4, 256);
-  L.ydone = align_up(L.fill + (size_t)L.ntiles_cap * 4, 256);
+  L.bfill = L.fill + (size_t)L.ntiles_cap * 4;   // contiguous: plan clears both in one pass
+  L.ydone = align_up(L.bfill + (size_t)L.ntiles_cap * 4, 256);
   L.cq = align_up(L.ydone + (size_t)L.ntiles_cap * 4, 256);
   L.plan_end = L.cq + 256;
   if (pool_rows <= 0) pool_rows = cap;

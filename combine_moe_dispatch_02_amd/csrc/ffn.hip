@@ -1866,11 +1866,13 @@ int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream
 // Backward data gradients on the big-tile kernel (bf16, tiled transposed weights):
 // out[rows][N] = A[rows][K] . Bt[e]^T per pool tile, Bt[e] = w[e]^T in fragment order.
 // epi 1 (backward GEMM Y): A = dy, Bt = W2^T [I][H], N = I; the epilogue turns dh into
-// dG in place of G (g_pool [rows][2I]). epi 0 (backward GEMM A): A = dG, Bt = W1^T
-// [H][2I], N = H, out = dx_pool.
+// dG in place of G (g_pool [rows][2I]); its units wait for the ready flags that combine
+// backward raises, as forward GEMM A's wait for dispatch's. epi 0 (backward GEMM A):
+// A = dG, Bt = W1^T [H][2I], N = H, out = dx_pool.
 int launch_ffn_dgrad(const moe_plan_t& p, int32_t pool_rows, const void* A, const void* Bt, int32_t N, int32_t K,
                      void* out, void* g_pool, int32_t I, int epi, int32_t workgroups, int32_t unit_order,
-                     int32_t a_stages, const WsLayout& L, char* ws, hipStream_t stream) {
+                     int32_t a_stages, uint32_t wait_epoch, uint64_t timeout_ticks, int32_t leave_cus,
+                     const WsLayout& L, char* ws, hipStream_t stream) {
   const int tile = p.tile;
   FfnArgs a{};
   a.tile_shift = __builtin_ctz((unsigned)tile);
@@ -1892,13 +1894,16 @@ int launch_ffn_dgrad(const moe_plan_t& p, int32_t pool_rows, const void* A, cons
   a.up_row0 = epi == 1 ? I : 0;
   a.ldo = (int64_t)N * 2;
   a.n_units = N / 512;
-  a.wait_ready = 0;
+  a.wait_ready = wait_epoch != 0 ? 1 : 0;
+  a.epoch = wait_epoch;
+  a.timeout = timeout_ticks;
   a.unit_order = unit_order ? unit_order : 3;
   a.ktiles = K / 32;
   a.g_save = static_cast<uint8_t*>(g_pool);
   a.g_ld = (int64_t)4 * I;
   int grid = workgroups > 0 ? workgroups : device_cu_count();
   if (grid <= 0) return MOE_ERR_HIP;
+  grid = std::max(1, grid - leave_cus);
   const int ntiles_cap = std::min(p.rows_cap, pool_rows) / tile;
   grid = (int)std::max<int64_t>(1, std::min<int64_t>(grid, (int64_t)ntiles_cap * a.n_units));
   constexpr int NW = kBigWaves;

@@ -90,14 +90,17 @@ bool ffn_sq_ok(int32_t H, int32_t I, int32_t dtype, int32_t tile, int32_t block_
 int launch_pack_weights(const void* w, int32_t E, int32_t rows, int32_t K, int32_t dtype, void* out,
                         hipStream_t stream);
 
+// wait_epoch != 0: each work unit first waits until its pool tile's ready flag equals
+// wait_epoch (timeout_ticks bounds one wait), and the persistent grid leaves leave_cus CUs
 int launch_ffn_dgrad(const moe_plan_t& p, int32_t pool_rows, const void* A, const void* Bt, int32_t N, int32_t K,
                      void* out, void* g_pool, int32_t I, int epi, int32_t workgroups, int32_t unit_order,
-                     int32_t a_stages, const WsLayout& L, char* ws, hipStream_t stream);
+                     int32_t a_stages, uint32_t wait_epoch, uint64_t timeout_ticks, int32_t leave_cus,
+                     const WsLayout& L, char* ws, hipStream_t stream);
 
 // backward.hip
 int launch_combine_backward(const void* dout, const float* topk_weights, const void* y_pool, int32_t pool_rows,
-                            const moe_plan_t& p, int32_t H, void* dy_pool, float* d_topk_weights,
-                            hipStream_t stream);
+                            const moe_plan_t& p, int32_t H, void* dy_pool, float* d_topk_weights, uint32_t epoch,
+                            const WsLayout& L, char* ws, hipStream_t stream);
 int launch_wgrad(const moe_plan_t& p, int32_t pool_rows, const void* A, int32_t N1, const void* B, int32_t N2,
                  void* C, int32_t workgroups, hipStream_t stream);
 int launch_pack_weights_t(const void* w, int32_t E, int32_t rows, int32_t K, void* out, hipStream_t stream);

@@ -263,7 +263,7 @@ int launch_plan(const int32_t* topk_idx, const moe_plan_t& p, const WsLayout& L,
   a.key_bits = bits;
   a.rows_cap = p.rows_cap;
   a.ntiles_cap = p.rows_cap / p.tile;
-  a.nfill = L.ntiles_cap;
+  a.nfill = 2 * L.ntiles_cap;   // dispatch's and combine backward's counters (adjacent)
   a.ncols = L.ncols;
   a.ppw = L.ppw;
   a.counts = p.counts;

@@ -235,9 +235,11 @@ def moe_expert_ffn_train(plan: Plan, pool: torch.Tensor, w1: torch.Tensor, w2: t
 
 
 def moe_combine_backward(dout: torch.Tensor, topk_weights: torch.Tensor, y_pool: torch.Tensor, plan: Plan,
-                         dy_pool: torch.Tensor, d_topk_weights: torch.Tensor, stream=None) -> None:
+                         dy_pool: torch.Tensor, d_topk_weights: torch.Tensor, epoch: int, ws: Workspace,
+                         stream=None) -> None:
     """dy_pool[pos[t,k]] = w[t,k] dout[t]; d_topk_weights[t,k] = <dout[t], y_pool[pos[t,k]]>.
-    dy_pool may be y_pool itself (each row is read before it is overwritten, by the same lane)."""
+    dy_pool may be y_pool itself (each row is read before it is overwritten, by the same lane).
+    Raises each pool tile's ready flag to ``epoch`` once its dy rows are stored."""
     _need_cuda(dout, "dout", torch.bfloat16)
     _need_cuda(topk_weights, "topk_weights", torch.float32)
     _need_cuda(d_topk_weights, "d_topk_weights", torch.float32)
@@ -250,14 +252,15 @@ def moe_combine_backward(dout: torch.Tensor, topk_weights: torch.Tensor, y_pool:
     c = plan.c()
     check("moe_combine_backward", load().moe_combine_backward(
         _vp(dout), _vp(topk_weights), _vp(y_pool), y_pool.shape[0], ctypes.byref(c), dout.shape[1], _vp(dy_pool),
-        _vp(d_topk_weights), _stream(stream)))
+        _vp(d_topk_weights), epoch, _vp(ws.buf), ws.nbytes, _stream(stream)))
 
 
 def moe_expert_ffn_backward(plan: Plan, pool: torch.Tensor, dy_pool: torch.Tensor, g_pool: torch.Tensor,
-                            w1t: torch.Tensor, w2t: torch.Tensor, ws: Workspace, dx_pool: torch.Tensor,
+                            w1t: torch.Tensor, w2t: torch.Tensor, epoch: int, ws: Workspace, dx_pool: torch.Tensor,
                             dw1: torch.Tensor, dw2: torch.Tensor, cfg: Optional[TileConfig] = None,
                             stream=None) -> None:
-    """Backward grouped GEMMs Y and A; g_pool's G is replaced by dG."""
+    """Backward grouped GEMMs Y and A; g_pool's G is replaced by dG. Backward Y's units wait
+    for the ready flags moe_combine_backward raised with the same ``epoch``."""
     for t, n in ((pool, "pool"), (dy_pool, "dy_pool"), (g_pool, "g_pool"), (w1t, "w1t"), (w2t, "w2t"),
                  (dx_pool, "dx_pool"), (dw1, "dw1"), (dw2, "dw2")):
         _need_cuda(t, n, torch.bfloat16)
@@ -273,8 +276,8 @@ def moe_expert_ffn_backward(plan: Plan, pool: torch.Tensor, dy_pool: torch.Tenso
     c = plan.c()
     cfgp = ctypes.byref(cfg) if cfg is not None else None
     check("moe_expert_ffn_backward", load().moe_expert_ffn_backward(
-        ctypes.byref(c), rows, _vp(pool), _vp(dy_pool), _vp(g_pool), _vp(w1t), _vp(w2t), H, I, _vp(ws.buf),
-        ws.nbytes, _vp(dx_pool), _vp(dw1), _vp(dw2), cfgp, _stream(stream)))
+        ctypes.byref(c), rows, _vp(pool), _vp(dy_pool), _vp(g_pool), _vp(w1t), _vp(w2t), H, I, epoch,
+        _vp(ws.buf), ws.nbytes, _vp(dx_pool), _vp(dw1), _vp(dw2), cfgp, _stream(stream)))
 
 
 def moe_dispatch_backward(dx_pool: torch.Tensor, plan: Plan, dx: torch.Tensor, stream=None) -> None:
@@ -415,19 +418,37 @@ class StreamMoE:
         """(w1t, w2t): the transposed, tiled weights the backward data GEMMs read (load time)."""
         return moe_pack_weights_transposed(w1), moe_pack_weights_transposed(w2)
 
-    def backward(self, dout, topk_weights, w1t, w2t):
+    def backward(self, dout, topk_weights, w1t, w2t, streams=None):
         """Gradients of the last forward (train=True) for the output gradient dout [T, H]:
         returns (dx [T, H] bf16, d_topk_weights [T, K] fp32, dw1 [E_local, 2I, H], dw2 [E_local, H, I]).
-        Runs on the current stream; y_pool is overwritten by dy."""
+        y_pool is overwritten by dy. ``streams=(compute, comm)`` mirrors forward(): combine
+        backward on comm raises each pool tile's flag as its dy rows land, and the backward GEMMs
+        on compute start on flagged tiles (backward Y's grid leaves CUs for combine backward);
+        dispatch backward follows on comm. None runs everything on the current stream."""
         if not self.train:
             raise RuntimeError("StreamMoE was built without train=True")
-        s = torch.cuda.current_stream()
+        epoch = self.next_epoch()
         dw1 = torch.empty(self.E_local, 2 * self.I, self.H, dtype=torch.bfloat16, device=dout.device)
         dw2 = torch.empty(self.E_local, self.H, self.I, dtype=torch.bfloat16, device=dout.device)
-        moe_combine_backward(dout, topk_weights, self.y_pool, self.plan, self.y_pool, self.dw, s)
-        moe_expert_ffn_backward(self.plan, self.pool, self.y_pool, self.g_pool, w1t, w2t, self.ws, self.dx_pool,
-                                dw1, dw2, self.cfg, s)
-        moe_dispatch_backward(self.dx_pool, self.plan, self.dx, s)
+        if streams is None:
+            s = torch.cuda.current_stream()
+            moe_combine_backward(dout, topk_weights, self.y_pool, self.plan, self.y_pool, self.dw, epoch, self.ws, s)
+            moe_expert_ffn_backward(self.plan, self.pool, self.y_pool, self.g_pool, w1t, w2t, epoch, self.ws,
+                                    self.dx_pool, dw1, dw2, self.cfg, s)
+            moe_dispatch_backward(self.dx_pool, self.plan, self.dx, s)
+            return self.dx, self.dw, dw1, dw2
+        compute, comm = streams
+        cur = torch.cuda.current_stream()
+        comm.wait_stream(cur)
+        compute.wait_stream(cur)            # w1t / w2t and the new dw1 / dw2 belong to the caller's stream
+        moe_combine_backward(dout, topk_weights, self.y_pool, self.plan, self.y_pool, self.dw, epoch, self.ws, comm)
+        moe_expert_ffn_backward(self.plan, self.pool, self.y_pool, self.g_pool, w1t, w2t, epoch, self.ws,
+                                self.dx_pool, dw1, dw2, self._concurrent_cfg(), compute)
+        done = torch.cuda.Event()
+        done.record(compute)
+        comm.wait_event(done)
+        moe_dispatch_backward(self.dx_pool, self.plan, self.dx, comm)
+        cur.wait_stream(comm)
         return self.dx, self.dw, dw1, dw2
 
     def check_errors(self, stream=None) -> None:

@@ -287,12 +287,23 @@ MOE355_API int moe_expert_ffn_train(const moe_plan_t* plan, int32_t pool_rows, c
  * bf16 RNE store) and d_topk_weights[t,k] = sum_h dout[t,h] * y_pool[p,h] (fp32);
  * d_topk_weights is 0 for non-local pairs. dout: device bf16 [T][H]; y_pool as
  * written by the forward; dy_pool: device bf16 [pool_rows][H] (padding rows are not
- * written); d_topk_weights: device fp32 [T][K].
- * Errors: MOE_ERR_INVALID (null pointers), MOE_ERR_UNSUPPORTED (H % 8 != 0).
+ * written; it may be y_pool itself, each row being read before the same lane overwrites
+ * it); d_topk_weights: device fp32 [T][K].
+ * Per-tile streaming, mirrored: once a pool tile's real dy rows are stored, its
+ * tile_ready entry is set to `epoch` (release, device scope), as moe_dispatch does for
+ * the pool, so that moe_expert_ffn_backward with the same epoch, on another stream, can
+ * start on the tile while other tiles are still being written. epoch must be nonzero and
+ * differ from the epoch of the forward's moe_dispatch (the flags are the plan's
+ * tile_ready). ws is the layer workspace after moe_plan: its per-tile counters of this
+ * call live there (each tile's counter is back at zero after the call, so the backward
+ * may be run again for the same plan).
+ * Errors: MOE_ERR_INVALID (null pointers, epoch 0, small workspace),
+ * MOE_ERR_UNSUPPORTED (H % 8 != 0).
  */
 MOE355_API int moe_combine_backward(const void* dout, const float* topk_weights, const void* y_pool,
                                     int32_t pool_rows, const moe_plan_t* plan, int32_t H, void* dy_pool,
-                                    float* d_topk_weights, void* stream);
+                                    float* d_topk_weights, uint32_t epoch, void* ws, size_t ws_bytes,
+                                    void* stream);
 
 /*
  * Backward grouped GEMMs Y and A (StreamEP README, "How it works": the four grouped
@@ -308,14 +319,20 @@ MOE355_API int moe_combine_backward(const void* dout, const float* topk_weights,
  * bf16 [pool_rows][H] (padding rows hold garbage, never read by moe_dispatch_backward),
  * dw1 bf16 [E_local][2I][H], dw2 bf16 [E_local][H][I] (zero for an expert with no
  * pair). Padding rows of dy_pool are excluded from the weight gradients.
- * Errors: MOE_ERR_INVALID (null pointers, bad pool_rows, small workspace, bad cfg),
- * MOE_ERR_UNSUPPORTED (shapes outside moe_expert_ffn_train's, or a pool whose
+ * Each backward-Y work unit waits until tile_ready of its pool tile equals `epoch`, the
+ * epoch moe_combine_backward raised (acquire), so the two may run on different streams
+ * (StreamEP README, "How it works": the backward mirrors the forward's overlaps); the
+ * weight gradients and backward A follow in stream order. A wait longer than the
+ * timeout records MOE_ERR_TIMEOUT and skips the unit. cfg->dispatch_cus CUs are left
+ * out of backward Y's persistent grid, for a combine backward running beside it.
+ * Errors: MOE_ERR_INVALID (null pointers, epoch 0, bad pool_rows, small workspace, bad
+ * cfg), MOE_ERR_UNSUPPORTED (shapes outside moe_expert_ffn_train's, or a pool whose
  * pool_rows * max(2I, H) * 2 bytes reach 4 GiB).
  */
 MOE355_API int moe_expert_ffn_backward(const moe_plan_t* plan, int32_t pool_rows, const void* pool,
                                        const void* dy_pool, void* g_pool, const void* w1t, const void* w2t, int32_t H,
-                                       int32_t I, void* ws, size_t ws_bytes, void* dx_pool, void* dw1, void* dw2,
-                                       const moe_tile_config* cfg, void* stream);
+                                       int32_t I, uint32_t epoch, void* ws, size_t ws_bytes, void* dx_pool,
+                                       void* dw1, void* dw2, const moe_tile_config* cfg, void* stream);
 
 /*
  * Backward of A2 (the mirror of dispatch: a gather-sum): dx[t] = sum over k with

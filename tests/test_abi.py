@@ -226,16 +226,26 @@ def test_backward_validation(lib):
                                     None, None) == 1
     assert lib.moe_expert_ffn_train(ctypes.byref(p), 256, v[0], v[1], v[2], 512, 512, 1, v[3], big, v[4], v[5],
                                     None, None) == 2
-    # combine backward
-    assert lib.moe_combine_backward(None, v[1], v[2], 256, ctypes.byref(p), 128, v[3], v[4], None) == 1
-    assert lib.moe_combine_backward(v[0], v[1], v[2], 256, ctypes.byref(p), 100, v[3], v[4], None) == 2
-    # expert backward: null pointer, then tile 16 / shapes outside the kernels
-    assert lib.moe_expert_ffn_backward(ctypes.byref(p), 256, v[0], None, v[2], v[3], v[4], 512, 512, v[5], big,
+    # combine backward: null pointer, epoch 0, no workspace, small workspace, H % 8
+    assert lib.moe_combine_backward(None, v[1], v[2], 256, ctypes.byref(p), 128, v[3], v[4], 1, v[5], big,
+                                    None) == 1
+    assert lib.moe_combine_backward(v[0], v[1], v[2], 256, ctypes.byref(p), 128, v[3], v[4], 0, v[5], big,
+                                    None) == 1
+    assert lib.moe_combine_backward(v[0], v[1], v[2], 256, ctypes.byref(p), 128, v[3], v[4], 1, None, big,
+                                    None) == 1
+    assert lib.moe_combine_backward(v[0], v[1], v[2], 256, ctypes.byref(p), 128, v[3], v[4], 1, v[5], 64,
+                                    None) == 1
+    assert lib.moe_combine_backward(v[0], v[1], v[2], 256, ctypes.byref(p), 100, v[3], v[4], 1, v[5], big,
+                                    None) == 2
+    # expert backward: null pointer, epoch 0, then tile 16 / shapes outside the kernels
+    assert lib.moe_expert_ffn_backward(ctypes.byref(p), 256, v[0], None, v[2], v[3], v[4], 512, 512, 1, v[5], big,
                                        v[6], v[7], v[8], None, None) == 1
-    assert lib.moe_expert_ffn_backward(ctypes.byref(p), 256, v[0], v[1], v[2], v[3], v[4], 512, 512, v[5], big,
+    assert lib.moe_expert_ffn_backward(ctypes.byref(p), 256, v[0], v[1], v[2], v[3], v[4], 512, 512, 0, v[5], big,
+                                       v[6], v[7], v[8], None, None) == 1
+    assert lib.moe_expert_ffn_backward(ctypes.byref(p), 256, v[0], v[1], v[2], v[3], v[4], 512, 512, 1, v[5], big,
                                        v[6], v[7], v[8], None, None) == 2
     q = _fake_plan(tile=128, rows_cap=oracle.pool_rows_bound(64, 2, 8, 128))
-    assert lib.moe_expert_ffn_backward(ctypes.byref(q), 256, v[0], v[1], v[2], v[3], v[4], 512, 256, v[5], big,
+    assert lib.moe_expert_ffn_backward(ctypes.byref(q), 256, v[0], v[1], v[2], v[3], v[4], 512, 256, 1, v[5], big,
                                        v[6], v[7], v[8], None, None) == 2      # I % 512
     # dispatch backward
     assert lib.moe_dispatch_backward(None, 256, ctypes.byref(p), 128, v[1], None) == 1

@@ -4,7 +4,11 @@ each; the training forward keeps G (checked against the oracle's G) and leaves o
 bitwise unchanged; the transposed weight re-layout is checked bit for bit.
 
 Small shapes are compared on every element; the skew workload at full size on sampled
-tokens (dx, d_topk_weights) and on the weight gradients of sampled experts."""
+tokens (dx, d_topk_weights) and on the weight gradients of sampled experts.
+
+The backward mirrors the forward's per-tile streaming: combine backward raises a ready
+flag per dy tile and backward GEMM Y waits on it, so on two streams the two overlap; the
+two-stream gradients must equal the one-stream ones bit for bit."""
 import random
 
 import numpy as np
@@ -66,10 +70,11 @@ def _poison(t):
     t.view(torch.uint8).fill_(0xFF)          # NaN as bf16 and fp32
 
 
-def _train_run(cfg, seed=None, tile_cfg=None, poison=False):
+def _train_run(cfg, seed=None, tile_cfg=None, poison=False, streams=None, layer=None):
     inp = make_inputs(cfg) if seed is None else make_inputs(cfg, seed)
     d = dev_inputs(inp)
-    layer = make_layer(cfg, train=True, cfg=tile_cfg)
+    if layer is None:
+        layer = make_layer(cfg, train=True, cfg=tile_cfg)
     if poison:
         # padding rows of every pool-shaped buffer (pool, y / dy, G / dG, dx_pool) and of h hold
         # NaN; the real rows are all written before they are read
@@ -79,10 +84,10 @@ def _train_run(cfg, seed=None, tile_cfg=None, poison=False):
         layer.ws.buf[plan_end:].fill_(0xFF)
     w1, w2, _, _ = layer.prepare_weights(d["w1"], d["w2"])
     w1t, w2t = layer.prepare_backward_weights(d["w1"], d["w2"])
-    out = layer.forward(d["x"], d["idx"], d["w"], w1, w2).clone()
+    out = layer.forward(d["x"], d["idx"], d["w"], w1, w2, streams=streams).clone()
     g_saved = layer.g_pool.clone()
     dout = make_dout(cfg, inp.seed)
-    dx, dw, dW1, dW2 = layer.backward(dout.cuda(), d["w"], w1t, w2t)
+    dx, dw, dW1, dW2 = layer.backward(dout.cuda(), d["w"], w1t, w2t, streams=streams)
     torch.cuda.synchronize()
     assert moe.moe_get_error(layer.ws) == 0
     return inp, d, layer, out, g_saved, dout, dx.clone(), dw.clone(), dW1, dW2
@@ -146,6 +151,93 @@ def test_backward_a_pipelines_agree():
     for i in (6, 7, 8, 9):                        # dx, dw, dW1, dW2
         assert torch.equal(ring[i].view(torch.int32 if ring[i].dtype == torch.float32 else torch.int16),
                            two[i].view(torch.int32 if two[i].dtype == torch.float32 else torch.int16)), i
+
+
+def _grads_equal(a, b):
+    for i in (3, 6, 7, 8, 9):                     # out, dx, dw, dW1, dW2
+        assert torch.equal(a[i].view(torch.int32 if a[i].dtype == torch.float32 else torch.int16),
+                           b[i].view(torch.int32 if b[i].dtype == torch.float32 else torch.int16)), i
+
+
+@pytest.mark.parametrize("cfg", [CASES[1], CASES[2]], ids=[CASES[1].name, CASES[2].name])
+def test_backward_two_streams(cfg):
+    # the backward's mirrored overlap: combine backward on the comm stream raises each dy
+    # tile's flag, backward GEMM Y on the compute stream starts on flagged tiles; same bits
+    # as one stream, and within tolerance of the oracle's exact gradients
+    say("backward two streams", cfg.name)
+    one = _train_run(cfg)
+    two = _train_run(cfg, streams=moe.make_streams())
+    _grads_equal(one, two)
+    inp, dout = two[0], two[5]
+    g = oracle.moe_layer_backward(inp, dout)
+    errs = {"dx": rel_err(_bf(two[6]), g.dx), "dW1": rel_err(_bf(two[8]), g.dW1), "dW2": rel_err(_bf(two[9]), g.dW2)}
+    if np.abs(g.dw).max() > 0:
+        errs["dw"] = rel_err(two[7].cpu().numpy().astype(np.float64), g.dw)
+    print(cfg.name, {k: f"{v:.2e}" for k, v in errs.items()})
+    assert max(errs.values()) <= TOL, errs
+
+
+def test_backward_two_streams_full_size_skew():
+    # the skew workload: forward and backward on two streams at the default config give the
+    # one-stream bits (those are checked against the oracle by the sampled full-size test)
+    cfg = config_by_name("zipf_skew")
+    say("backward two streams full size", cfg.name)
+    layer = make_layer(cfg, train=True)
+    one = _train_run(cfg, layer=layer)
+    one = one[:6] + tuple(t.clone() for t in one[6:])
+    two = _train_run(cfg, layer=layer, streams=moe.make_streams())
+    _grads_equal(one, two)
+
+
+def test_combine_backward_raises_flags_and_rearms():
+    # every real tile's flag equals the call's epoch after combine backward, tiles past the
+    # plan's stay 0, and a second call for the same plan (its per-tile counters reset by the
+    # first) raises them again with its own epoch and writes the same dy
+    cfg = CASES[1]
+    inp = make_inputs(cfg)
+    d = dev_inputs(inp)
+    layer = make_layer(cfg, train=True)
+    say("combine backward flags", cfg.name)
+    moe.moe_plan(d["idx"], layer.plan, layer.ws)
+    g = torch.Generator().manual_seed(5)
+    y = (torch.randn(layer.y_pool.shape, generator=g) * 0.5).to(torch.bfloat16).cuda()
+    dout = make_dout(cfg, inp.seed).cuda()
+    nt = int(layer.plan.num_tiles.item())
+    dys = []
+    for epoch in (11, 12):
+        dy = torch.zeros_like(y)
+        moe.moe_combine_backward(dout, d["w"], y, layer.plan, dy, layer.dw, epoch, layer.ws)
+        torch.cuda.synchronize()
+        ready = layer.plan.tile_ready.cpu().numpy().astype(np.int64)
+        assert (ready[:nt] == epoch).all() and (ready[nt:] == 0).all()
+        dys.append(dy)
+    assert moe.moe_get_error(layer.ws) == 0
+    assert torch.equal(dys[0].view(torch.int16), dys[1].view(torch.int16))
+    # dy rows: w[t,k] * dout[t] rounded once to bf16
+    pos = layer.plan.pos.cpu().numpy().reshape(cfg.T, cfg.K)
+    t, k = np.nonzero(pos >= 0)
+    ref = (inp.topk_weights.numpy()[t, k, None].astype(np.float32)
+           * oracle.bf16_to_f64(make_dout(cfg, inp.seed)).astype(np.float32)[t])
+    got = dys[0][torch.as_tensor(pos[t, k], device="cuda")].float().cpu().numpy()
+    assert np.array_equal(got, torch.from_numpy(ref).to(torch.bfloat16).float().numpy())
+
+
+def test_ffn_backward_without_combine_backward_times_out():
+    # forced from the host: backward GEMM Y waits on an epoch that no combine backward raised,
+    # with a 2 ms bound per wait; the call ends with MOE_ERR_TIMEOUT and the workspace is
+    # usable again at once
+    cfg = CASES[0]
+    say("backward forced timeout", cfg.name)
+    inp, d, layer, out, g_saved, dout, dx, dw, dW1, dW2 = _train_run(cfg, tile_cfg=moe.TileConfig(0, 0, 2000, 0))
+    w1t, w2t = layer.prepare_backward_weights(d["w1"], d["w2"])
+    dw1 = torch.empty_like(dW1)
+    dw2 = torch.empty_like(dW2)
+    moe.moe_expert_ffn_backward(layer.plan, layer.pool, layer.y_pool, layer.g_pool, w1t, w2t, 0xABC, layer.ws,
+                                layer.dx_pool, dw1, dw2, layer.cfg)
+    torch.cuda.synchronize()
+    assert moe.moe_get_error(layer.ws) == moe.layer._abi.MOE_ERR_TIMEOUT
+    assert moe.moe_get_error(layer.ws) == 0
+    _train_run(cfg, layer=layer)
 
 
 def test_backward_full_size_skew_sampled():
