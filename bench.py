@@ -30,7 +30,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-FFN_SOURCES = ("ffn.hip", "ffn_sq.hip")
+FFN_SOURCES = ("ffn.hip", "ffn_sq.hip", "ffn_sq.h")
 
 
 def kernel_source_hash() -> str:

@@ -1,0 +1,98 @@
+// Work units of the 256-row GEMM kernel (ffn_sq.hip): a unit is two consecutive pool tiles
+// of one expert (or its last, odd tile) and one N block of 256 columns: the unit walk, the
+// per-expert prefix of row units and the ready-flag wait. Internal; not part of the C ABI.
+#pragma once
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int kMaxExpertsSq = 1024;
+
+struct SqUnit {
+  int e;     // local expert
+  int m;     // first pool tile
+  int two;   // 1: tiles m and m + 1; 0: tile m only
+  int j;     // N block of 256 columns
+};
+
+// Unit u -> coordinates. s_ru[e] = row units (tile pairs, rounded up) of the experts
+// before e. Within expert e, units go in groups of `group` row units; inside a group,
+// N block by N block, the group's row units back to back: units that run together
+// share weight panels and pool rows.
+__device__ __attribute__((always_inline)) inline SqUnit sq_unit(const SqArgs& a, const int32_t* s_ru, int u) {
+  int lo = 0, hi = a.n_experts - 1;
+  while (lo < hi) {  // the last expert whose first unit is <= u (empty experts share a start)
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_ru[mid] * a.NB <= u) lo = mid;
+    else hi = mid - 1;
+  }
+  SqUnit r;
+  r.e = lo;
+  const int R = s_ru[lo + 1] - s_ru[lo];
+  const int l = u - s_ru[lo] * a.NB;
+  const int g = l / (a.group * a.NB);
+  const int gsz = min(a.group, R - g * a.group);
+  const int l2 = l - g * a.group * a.NB;
+  r.j = l2 / gsz;
+  const int ru = g * a.group + (l2 - r.j * gsz);
+  const int t0 = min(a.offsets[lo] >> 7, a.max_tiles);
+  const int t1 = min(a.offsets[lo + 1] >> 7, a.max_tiles);
+  r.m = t0 + 2 * ru;
+  r.two = r.m + 1 < t1;
+  // uniform over the wave (all lanes read the same LDS words): keep the unit in scalar
+  // registers, so that its buffer resources stay scalar too
+  r.e = __builtin_amdgcn_readfirstlane(r.e);
+  r.m = __builtin_amdgcn_readfirstlane(r.m);
+  r.two = __builtin_amdgcn_readfirstlane(r.two);
+  r.j = __builtin_amdgcn_readfirstlane(r.j);
+  return r;
+}
+
+// s_ru[e] for e <= E (row units of the experts before e; s_ru[E] = all of them): lane i
+// of wave 0 sums a run of experts, then a wave scan. The caller syncs the workgroup.
+__device__ __attribute__((always_inline)) inline void sq_row_units(const SqArgs& a, int32_t* s_ru, int lane) {
+  const int E = a.n_experts;
+  const int per = (E + 63) >> 6;
+  int sum = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = lane * per + i;
+    if (e < E) {
+      const int t0 = min(a.offsets[e] >> 7, a.max_tiles), t1 = min(a.offsets[e + 1] >> 7, a.max_tiles);
+      sum += (t1 - t0 + 1) >> 1;
+    }
+  }
+  const int incl = wave_inclusive_scan(sum);
+  int run = incl - sum;
+  for (int i = 0; i < per; ++i) {
+    const int e = lane * per + i;
+    if (e < E) {
+      s_ru[e] = run;
+      const int t0 = min(a.offsets[e] >> 7, a.max_tiles), t1 = min(a.offsets[e + 1] >> 7, a.max_tiles);
+      run += (t1 - t0 + 1) >> 1;
+    }
+  }
+  if (lane == 63) s_ru[E] = incl;
+}
+
+// Wait until the unit's tiles carry this call's epoch (see the file comment).
+__device__ __attribute__((always_inline)) inline void sq_wait_tiles(const SqArgs& a, const SqUnit& U) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  for (;;) {
+    const bool r0 = __hip_atomic_load(&a.tile_ready[U.m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch;
+    const bool r1 = !U.two ||
+                    __hip_atomic_load(&a.tile_ready[U.m + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch;
+    if (r0 && r1) break;
+    if (__hip_atomic_load(a.abort_epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch) break;
+    if (__builtin_amdgcn_s_memrealtime() - t0 > a.timeout) {
+      record_error(a.err, MOE_ERR_TIMEOUT);
+      __hip_atomic_store(a.abort_epoch, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(4);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+}  // namespace moe

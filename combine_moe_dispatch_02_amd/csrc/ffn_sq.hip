@@ -55,6 +55,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "ffn_sq.h"
 #include "kernels.h"
 
 namespace moe {
@@ -67,49 +68,8 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kSqWaves = 8;
 constexpr int kAStage = 32768;   // 256 pool rows x 128 bytes (64 K values)
 constexpr int kBStage = 16384;   // 16 weight row blocks x 1 KiB (32 K values)
-constexpr int kMaxExpertsSq = 1024;
 
 __device__ inline float sq_silu_mul(float g, float u) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u; }
-
-struct SqUnit {
-  int e;     // local expert
-  int m;     // first pool tile
-  int two;   // 1: tiles m and m + 1; 0: tile m only
-  int j;     // N block of 256 columns
-};
-
-// Unit u -> coordinates. s_ru[e] = row units (tile pairs, rounded up) of the experts
-// before e. Within expert e, units go in groups of `group` row units; inside a group,
-// N block by N block, the group's row units back to back: units that run together
-// share weight panels and pool rows.
-__device__ __attribute__((always_inline)) inline SqUnit sq_unit(const SqArgs& a, const int32_t* s_ru, int u) {
-  int lo = 0, hi = a.n_experts - 1;
-  while (lo < hi) {  // the last expert whose first unit is <= u (empty experts share a start)
-    const int mid = (lo + hi + 1) >> 1;
-    if (s_ru[mid] * a.NB <= u) lo = mid;
-    else hi = mid - 1;
-  }
-  SqUnit r;
-  r.e = lo;
-  const int R = s_ru[lo + 1] - s_ru[lo];
-  const int l = u - s_ru[lo] * a.NB;
-  const int g = l / (a.group * a.NB);
-  const int gsz = min(a.group, R - g * a.group);
-  const int l2 = l - g * a.group * a.NB;
-  r.j = l2 / gsz;
-  const int ru = g * a.group + (l2 - r.j * gsz);
-  const int t0 = min(a.offsets[lo] >> 7, a.max_tiles);
-  const int t1 = min(a.offsets[lo + 1] >> 7, a.max_tiles);
-  r.m = t0 + 2 * ru;
-  r.two = r.m + 1 < t1;
-  // uniform over the wave (all lanes read the same LDS words): keep the unit in scalar
-  // registers, so that its buffer resources stay scalar too
-  r.e = __builtin_amdgcn_readfirstlane(r.e);
-  r.m = __builtin_amdgcn_readfirstlane(r.m);
-  r.two = __builtin_amdgcn_readfirstlane(r.two);
-  r.j = __builtin_amdgcn_readfirstlane(r.j);
-  return r;
-}
 
 // DMA sources of one unit for this wave: the unit's rows (A) and its expert's tiled
 // weights (B), and the byte offsets of the wave's two B row blocks
@@ -130,25 +90,6 @@ __device__ __attribute__((always_inline)) inline SqSrc sq_src(const SqArgs& a, c
   s.b0 = (uint32_t)rb * (uint32_t)a.ktiles * 1024u;
   s.b1 = s.b0 + (uint32_t)a.ktiles * 1024u;
   return s;
-}
-
-// Wait until the unit's tiles carry this call's epoch (see the file comment).
-__device__ __attribute__((always_inline)) inline void sq_wait_tiles(const SqArgs& a, const SqUnit& U) {
-  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-  for (;;) {
-    const bool r0 = __hip_atomic_load(&a.tile_ready[U.m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch;
-    const bool r1 = !U.two ||
-                    __hip_atomic_load(&a.tile_ready[U.m + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch;
-    if (r0 && r1) break;
-    if (__hip_atomic_load(a.abort_epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch) break;
-    if (__builtin_amdgcn_s_memrealtime() - t0 > a.timeout) {
-      record_error(a.err, MOE_ERR_TIMEOUT);
-      __hip_atomic_store(a.abort_epoch, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      break;
-    }
-    __builtin_amdgcn_s_sleep(4);
-  }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
 }  // namespace
@@ -191,30 +132,8 @@ __global__ __launch_bounds__(64 * kSqWaves, 1) void ffn_sq_kernel(SqArgs a) {
     if (blockIdx.x == 0 && tid == 0) record_error(a.err, MOE_ERR_INVALID);
     ntiles = a.max_tiles;
   }
-  // row units per expert, prefix-summed: lane i of wave 0 sums a run of experts
-  if (w == 0) {
-    const int E = a.n_experts;
-    const int per = (E + 63) >> 6;
-    int sum = 0;
-    for (int i = 0; i < per; ++i) {
-      const int e = lane * per + i;
-      if (e < E) {
-        const int t0 = min(a.offsets[e] >> 7, a.max_tiles), t1 = min(a.offsets[e + 1] >> 7, a.max_tiles);
-        sum += (t1 - t0 + 1) >> 1;
-      }
-    }
-    const int incl = wave_inclusive_scan(sum);
-    int run = incl - sum;
-    for (int i = 0; i < per; ++i) {
-      const int e = lane * per + i;
-      if (e < E) {
-        s_ru[e] = run;
-        const int t0 = min(a.offsets[e] >> 7, a.max_tiles), t1 = min(a.offsets[e + 1] >> 7, a.max_tiles);
-        run += (t1 - t0 + 1) >> 1;
-      }
-    }
-    if (lane == 63) s_ru[E] = incl;
-  }
+  // row units per expert, prefix-summed
+  if (w == 0) sq_row_units(a, s_ru, lane);
   __syncthreads();
   const int total = __builtin_amdgcn_readfirstlane(s_ru[a.n_experts] * a.NB);
   const int G = gridDim.x;
