@@ -228,6 +228,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ inline u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
+// the same load with the non-temporal cache policy (NT bit): for data read exactly once
+__device__ inline u32x4 buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
+}
 __device__ inline void buf_store16(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
 }

@@ -64,7 +64,7 @@ __device__ inline void dispatch_token(const DispatchArgs& a, int t, int p, uint6
   for (int c0 = 0; c0 < nch; c0 += kWave * CPL) {
     u32x4 v[CPL];
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) v[i] = buf_load16(xr, (uint32_t)(c0 + i * kWave + lane) * 16u);
+    for (int i = 0; i < CPL; ++i) v[i] = buf_load16_nt(xr, (uint32_t)(c0 + i * kWave + lane) * 16u);  // x is read once
     if constexpr (FMT == 0) {
       for (int k = 0; k < a.K; ++k) {
         if (!((dest >> k) & 1ull)) continue;

@@ -40,6 +40,7 @@
 
 #include "combine.h"
 #include "common.h"
+#include "ffn_sq.h"
 #include "kernels.h"
 
 namespace moe {
@@ -98,6 +99,8 @@ struct FfnArgs {
   uint8_t* g_save;
   int64_t g_ld;              // bytes per row of g_save (2I * 2)
   int32_t a_stages;          // 2: two A stages; else the four-stage ring where the kernel has it
+  int32_t select;            // GEMM A, 1: return at once if the 256-row units win (sel)
+  SqSelect sel;
 };
 
 __device__ inline uint32_t swz(int row, int chunk) { return (uint32_t)(row * 128 + ((chunk ^ (row & 7)) << 4)); }
@@ -579,6 +582,7 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_hstage[GEMM_A ? BM * (FP8 ? 256 : 512) : 16];
   __shared__ float s_red[FP8 && GEMM_A && !MX ? NW : 1][FP8 && GEMM_A && !MX ? BM : 1];
   __shared__ int s_go;
+  __shared__ int s_sel;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -586,6 +590,14 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
   const int l16 = lane & 15;
   const int lhi = lane >> 4;
 
+  if (GEMM_A && a.select) {   // launched beside the 256-row kernel: run only if that one loses
+    if (tid < 64) {
+      const bool win = sq_gemm_a_wins(a.offsets, a.n_experts, a.max_tiles, a.sel, lane);
+      if (lane == 0) s_sel = win ? 1 : 0;
+    }
+    __syncthreads();
+    if (s_sel) return;
+  }
   int ntiles = a.num_tiles[0];
   int order = a.unit_order;
   if (ntiles > a.max_tiles) {
@@ -1725,6 +1737,33 @@ int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream
     a.pool_rows = f.pool_rows;
   }
 
+  // GEMM A: pool x w1^T -> SwiGLU -> h
+  a.A = static_cast<const uint8_t*>(f.pool);
+  a.A_s = fp8 ? static_cast<const float*>(f.pool_s) : nullptr;
+  a.B = static_cast<const uint8_t*>(f.w1);
+  a.B_s = fp8 ? static_cast<const float*>(f.w1_s) : nullptr;
+  a.out = h;
+  a.out_s = hs;
+  a.A_e8 = mx ? static_cast<const uint8_t*>(f.pool_s) : nullptr;
+  a.B_e8 = mx ? static_cast<const uint8_t*>(f.w1_s) : nullptr;
+  a.out_e8 = hs8;
+  a.b_e8_expert = (int64_t)2 * I * (H / 32);
+  a.ksteps = H * eb / 128;
+  a.lda = (int64_t)H * eb;
+  a.b_expert = mx ? (int64_t)2 * I * (H / 2) : (int64_t)2 * I * H * eb;
+  a.ldb = (int64_t)H * eb;
+  a.up_row0 = I;
+  a.ldo = (int64_t)I * eb;
+  a.n_units = I / (bn_a / 2);
+  a.s_kblocks = H / 128;
+  a.bs_ld = H / 128;
+  a.bs_expert = (int64_t)(2 * I / 128) * (H / 128);
+  a.out_groups = I / 128;
+  a.wait_ready = 1;
+  a.unit_order = bn_a == 512 ? (f.unit_order ? f.unit_order : mx ? 1 : 3) : 1;   // mxfp4: tiles then N blocks measured 1% faster
+  const bool packed = f.weight_layout == MOE_WEIGHTS_MFMA_TILED;
+  a.ktiles = H / (fp8 || mx ? 128 : 32);
+
   // 256-row units wherever they take the shape (unless 128 is asked for); the 128 x 512
   // units otherwise
   const bool sq = f.unit_rows != 128 && ffn_sq_ok(H, I, f.dtype, tile, f.block_n, f.weight_layout,
@@ -1762,9 +1801,25 @@ int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream
     q.NB = 2 * I / 256;
     q.up_rb = I / 16;
     q.wait_ready = 1;
-    int ga = (int)std::min<int64_t>(std::max(1, grid - f.dispatch_cus), pairs_cap * q.NB);
-    int rc = launch_ffn_sq(q, std::max(1, ga), true, f.g_pool != nullptr, stream);
+    int ga = std::max(1, (int)std::min<int64_t>(std::max(1, grid - f.dispatch_cus), pairs_cap * q.NB));
+    // with the unit shape left to the library, GEMM A is launched on both kernels and the plan
+    // decides on the device which one computes (sq_gemm_a_wins); the other returns at once
+    const bool dual = f.unit_rows == 0 && bn_a == 512 && packed && big_a_ok(H, I, f.dtype, tile);
+    const int ga_big = std::max(1, (int)std::min<int64_t>(std::max(1, grid - f.dispatch_cus),
+                                                          (int64_t)ntiles_cap * a.n_units));
+    const SqSelect sel{q.NB, ga, a.n_units, ga_big};
+    q.select = dual ? 1 : 0;
+    q.sel = sel;
+    int rc = launch_ffn_sq(q, ga, true, f.g_pool != nullptr, stream);
     if (rc != MOE_OK) return rc;
+    if (dual) {
+      a.select = 1;
+      a.sel = sel;
+      rc = launch_shape<false, true>(tile, bn_a, packed, a, ga_big, stream);
+      if (rc != MOE_OK) return rc;
+      if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
+      a.select = 0;
+    }
     // GEMM Y: h x w2^T -> y_pool (same stream, so every h row is complete)
     q.A = h;
     q.lda = (int64_t)I * 2;
@@ -1778,42 +1833,17 @@ int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream
     q.NB = H / 256;
     q.up_rb = 0;
     q.wait_ready = 0;
+    q.select = 0;   // GEMM Y always runs on the 256-row units
     int gy = (int)std::min<int64_t>(grid, pairs_cap * q.NB);
     return launch_ffn_sq(q, std::max(1, gy), false, false, stream);
   }
 
-  // GEMM A: pool x w1^T -> SwiGLU -> h
-  a.A = static_cast<const uint8_t*>(f.pool);
-  a.A_s = fp8 ? static_cast<const float*>(f.pool_s) : nullptr;
-  a.B = static_cast<const uint8_t*>(f.w1);
-  a.B_s = fp8 ? static_cast<const float*>(f.w1_s) : nullptr;
-  a.out = h;
-  a.out_s = hs;
-  a.A_e8 = mx ? static_cast<const uint8_t*>(f.pool_s) : nullptr;
-  a.B_e8 = mx ? static_cast<const uint8_t*>(f.w1_s) : nullptr;
-  a.out_e8 = hs8;
-  a.b_e8_expert = (int64_t)2 * I * (H / 32);
-  a.ksteps = H * eb / 128;
-  a.lda = (int64_t)H * eb;
-  a.b_expert = mx ? (int64_t)2 * I * (H / 2) : (int64_t)2 * I * H * eb;
-  a.ldb = (int64_t)H * eb;
-  a.up_row0 = I;
-  a.ldo = (int64_t)I * eb;
-  a.n_units = I / (bn_a / 2);
-  a.s_kblocks = H / 128;
-  a.bs_ld = H / 128;
-  a.bs_expert = (int64_t)(2 * I / 128) * (H / 128);
-  a.out_groups = I / 128;
-  a.wait_ready = 1;
-  a.unit_order = bn_a == 512 ? (f.unit_order ? f.unit_order : mx ? 1 : 3) : 1;   // mxfp4: tiles then N blocks measured 1% faster
   int grid = f.workgroups > 0 ? f.workgroups : device_cu_count();
   if (grid <= 0) return MOE_ERR_HIP;
   // GEMM A waits on flags that a concurrent dispatch raises: its persistent grid leaves
   // dispatch_cus CUs free (one workgroup fills a CU), so that dispatch can always run
   int ga = (int)std::min<int64_t>(std::max(1, grid - f.dispatch_cus), (int64_t)ntiles_cap * a.n_units);
   if (ga < 1) ga = 1;
-  const bool packed = f.weight_layout == MOE_WEIGHTS_MFMA_TILED;
-  a.ktiles = H / (fp8 || mx ? 128 : 32);
   int rc = mx    ? launch_mx<true>(tile, bn_a, packed, a, ga, stream)
            : fp8 ? launch_shape<true, true>(tile, bn_a, packed, a, ga, stream)
                  : launch_shape<false, true>(tile, bn_a, packed, a, ga, stream);

@@ -76,6 +76,36 @@ __device__ __attribute__((always_inline)) inline void sq_row_units(const SqArgs&
   if (lane == 63) s_ru[E] = incl;
 }
 
+// Which unit shape runs GEMM A when both kernels are launched for it (the 256-row one
+// first, the 128-row one after it, each returning at once unless chosen). It is decided on
+// the device from the plan, with the same answer in every workgroup of both launches: the
+// 256-row units, unless the experts hold two tiles or more on average (with fewer the FFN
+// streams weights, and a 256-row unit reads an expert's weight panel once per tile pair
+// rather than once per tile) and 0.85 of their rounds over the grid exceeds the 128-row
+// units' rounds (0.85: about what a 256-row unit costs against a 128-row unit of the same
+// flops, measured at the skew and ep_share workloads). One wave evaluates it.
+__device__ __attribute__((always_inline)) inline bool sq_gemm_a_wins(const int32_t* offsets, int E, int max_tiles,
+                                                                     const SqSelect& s, int lane) {
+  int pairs = 0, tiles = 0, nonempty = 0;
+  for (int e = lane; e < E; e += 64) {
+    const int t0 = min(offsets[e] >> 7, max_tiles), t1 = min(offsets[e + 1] >> 7, max_tiles);
+    const int n = t1 - t0;
+    pairs += (n + 1) >> 1;
+    tiles += n;
+    nonempty += n > 0 ? 1 : 0;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    pairs += __shfl_xor(pairs, o);
+    tiles += __shfl_xor(tiles, o);
+    nonempty += __shfl_xor(nonempty, o);
+  }
+  if (tiles < 2 * nonempty) return true;
+  const int64_t r_sq = ((int64_t)pairs * s.nb_sq + s.grid_sq - 1) / s.grid_sq;
+  const int64_t r_big = ((int64_t)tiles * s.nb_big + s.grid_big - 1) / s.grid_big;
+  return 17 * r_sq <= 20 * r_big;
+}
+
 // Wait until the unit's tiles carry this call's epoch (see the file comment).
 __device__ __attribute__((always_inline)) inline void sq_wait_tiles(const SqArgs& a, const SqUnit& U) {
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();

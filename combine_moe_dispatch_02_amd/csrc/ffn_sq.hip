@@ -105,6 +105,7 @@ __global__ __launch_bounds__(64 * kSqWaves, 1) void ffn_sq_kernel(SqArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_b3[kBStage];
   __shared__ __attribute__((aligned(16))) uint8_t s_out[kSqWaves * 2048];
   __shared__ int32_t s_ru[kMaxExpertsSq + 1];
+  __shared__ int s_sel;
   auto aring = [&](auto ST) __attribute__((always_inline)) -> uint8_t* {
     if constexpr (decltype(ST)::value == 0) return s_a0;
     else return s_a1;
@@ -132,9 +133,16 @@ __global__ __launch_bounds__(64 * kSqWaves, 1) void ffn_sq_kernel(SqArgs a) {
     if (blockIdx.x == 0 && tid == 0) record_error(a.err, MOE_ERR_INVALID);
     ntiles = a.max_tiles;
   }
-  // row units per expert, prefix-summed
-  if (w == 0) sq_row_units(a, s_ru, lane);
+  // row units per expert, prefix-summed; whether this launch is the call's GEMM A
+  if (w == 0) {
+    sq_row_units(a, s_ru, lane);
+    if (a.select) {
+      const bool win = sq_gemm_a_wins(a.offsets, a.n_experts, a.max_tiles, a.sel, lane);
+      if (lane == 0) s_sel = win ? 1 : 0;
+    }
+  }
   __syncthreads();
+  if (a.select && !s_sel) return;
   const int total = __builtin_amdgcn_readfirstlane(s_ru[a.n_experts] * a.NB);
   const int G = gridDim.x;
   int u = unit_slot(blockIdx.x, G);

@@ -45,6 +45,13 @@ struct FfnLaunch {
 int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream_t stream);
 
 // ffn_sq.hip: one grouped GEMM of the FFN on 256 x 256 units (bf16, tiled weights, tile 128)
+// The two GEMM A unit shapes of a call launched back to back, each running only if the plan
+// makes it the faster one (ffn_sq.h, sq_gemm_a_wins): units per tile pair and grid of the
+// 256-row kernel, units per tile and grid of the 128-row kernel
+struct SqSelect {
+  int32_t nb_sq, grid_sq, nb_big, grid_big;
+};
+
 struct SqArgs {
   const uint8_t* A;          // pool (GEMM A) or h (GEMM Y), bf16 [rows][K]
   int64_t lda;               // bytes per A row
@@ -72,6 +79,8 @@ struct SqArgs {
   uint32_t* abort_epoch;
   uint64_t timeout;
   int32_t wait_ready;
+  int32_t select;            // 1: return at once unless the 256-row units win (sel)
+  SqSelect sel;
 };
 int launch_ffn_sq(const SqArgs& a, int grid, bool gemm_a, bool gsave, hipStream_t stream);
 

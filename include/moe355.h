@@ -124,10 +124,13 @@ typedef struct moe_tile_config {
   int32_t unit_rows;        /* rows of a GEMM work unit: 128 = one pool tile (128 x 512 units),
                                256 = two pool tiles of one expert (256 x 256 units, both operands
                                by LDS-DMA; bf16, tiled weights, tile 128, H % 256 == 0,
-                               I % 128 == 0, not with combine on completion); 0 = auto (256
-                               where it applies, else 128). With 256, unit_order k >= 1 walks
-                               each expert in groups of k tile pairs (0 = auto: 6). Same
-                               results. */
+                               I % 128 == 0, not with combine on completion); 0 = auto: 256
+                               where it applies, else 128, except that GEMM A, where both
+                               shapes apply, is launched on both and each launch decides on
+                               the device from the plan (tile pairs and tiles per expert,
+                               rounds over the grid) whether it computes or returns at once.
+                               With 256, unit_order k >= 1 walks each expert in groups of k
+                               tile pairs (0 = auto: 6). Same results. */
 } moe_tile_config;
 
 /* Host-only size helpers (no device access). */

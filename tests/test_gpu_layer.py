@@ -186,6 +186,22 @@ SQ_CASES = [
 ]
 
 
+@pytest.mark.parametrize("name", ["ep_share", "big_both"])
+def test_layer_auto_unit_shape(name):
+    # with the unit shape left to the library, GEMM A runs on whichever kernel the plan picks
+    # on the device (ep_share: the 128-row units; big_both: the 256-row ones): the same bits as
+    # either shape forced
+    import combine_moe_dispatch_02_amd as moe
+    cfg = config_by_name(name) if name == "ep_share" else next(c for c in FULL_COMPARE if c.name == name)
+    inp = make_inputs(cfg)
+    d = dev_inputs(inp)
+    say("auto unit shape", cfg.name)
+    auto = run_layer(make_layer(cfg), d).clone()
+    for rows in (128, 256):
+        got = run_layer(make_layer(cfg, cfg=moe.TileConfig(0, 0, 0, 0, 0, 0, 0, rows)), d)
+        assert torch.equal(auto.view(torch.int16), got.view(torch.int16)), rows
+
+
 @pytest.mark.parametrize("cfg", SQ_CASES, ids=[c.name for c in SQ_CASES])
 def test_layer_unit_rows_agree(cfg):
     # the 256 x 256 units (two pool tiles, both operands by LDS-DMA) run the same MFMA chain
