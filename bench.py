@@ -83,8 +83,8 @@ def algorithmic_work(cfg, idx_np):
 
 
 def cpu_baseline(inp, max_tokens: int, target_s: float = 15.0, gpu_out=None):
-    """The oracle as it stands, timed on the first tokens of the same workload: a probe on 64
-    tokens sizes the sample to about ``target_s`` seconds of CPU work (at most ``max_tokens``).
+    """The oracle as it stands, timed on the first tokens of the same workload: probes on 64 and
+    256 tokens size the sample to about ``target_s`` seconds of CPU work (at most ``max_tokens``).
     With ``gpu_out`` (the layer's output on the GPU), also the max-normwise relative error of
     those tokens against the oracle."""
     import numpy as np
@@ -95,17 +95,25 @@ def cpu_baseline(inp, max_tokens: int, target_s: float = 15.0, gpu_out=None):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = 1
-    t0 = time.perf_counter()
-    oracle.moe_layer(inp, tokens=np.arange(min(64, max_tokens)))
-    probe = time.perf_counter() - t0
-    n = int(max(64, min(max_tokens, 64 * target_s / max(probe, 1e-3))))
+    # two probes: the oracle's time is a fixed part (the experts' weights in float64) plus a
+    # part per token, so a straight line through two sample sizes sizes the run
+    probes = []
+    for m in (min(64, max_tokens), min(256, max_tokens)):
+        t0 = time.perf_counter()
+        oracle.moe_layer(inp, tokens=np.arange(m))
+        probes.append((m, time.perf_counter() - t0))
+    (m0, p0), (m1, p1) = probes
+    per_tok = max((p1 - p0) / max(m1 - m0, 1), 1e-6)
+    fixed = max(p0 - m0 * per_tok, 0.0)
+    n = int(max(64, min(max_tokens, (target_s - fixed) / per_tok)))
     toks = np.arange(n)
     t0 = time.perf_counter()
     ref = oracle.moe_layer(inp, tokens=toks)
     dt = time.perf_counter() - t0
     out = {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
            "sample": f"tokens 0..{n - 1} of the workload (all their pairs), float64 NumPy oracle incl. "
-                     f"weight dequantisation, {dt:.1f} s (sized by a 64-token probe of {probe:.1f} s)"}
+                     f"weight dequantisation, {dt:.1f} s (sized by probes of {m0} and {m1} tokens: "
+                     f"{p0:.1f} and {p1:.1f} s)"}
     if gpu_out is not None:
         got = oracle.bf16_to_f64(gpu_out[:n].cpu())
         out["gpu_max_norm_rel_err"] = float(oracle.max_norm_rel_err(got, ref.out))
