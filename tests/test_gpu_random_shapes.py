@@ -1,7 +1,8 @@
 """Seeded random layer shapes on the GPU against the oracle, over the shapes each path
 accepts: bf16 on every tile (16/32/64/128; H a multiple of 128, I of 64), fp8 (tile 64 or
 128; H % 256, I % 128), mxfp4 (tile 128; H % 512, I % 256); top-k 1..16, EP slices with
-pairs to other GPUs, uniform or Zipf routing. Every output element is compared (max-norm
+pairs to other GPUs, uniform or Zipf routing; and larger bf16 shapes of the 256-row units
+(several tiles per expert). Every output element is compared (max-norm
 relative error 1e-2 bf16, 3e-2 fp8 / mxfp4), the plan bit for bit, and tokens without a
 local pair must be exactly zero."""
 import random
@@ -45,7 +46,27 @@ def _shapes(n=18, seed=20261203):
     return out
 
 
-SHAPES = _shapes()
+def _sq_shapes(n=6, seed=78):
+    """Seeded shapes of the 256-row units (bf16, tile 128, H % 256, I % 128): several tiles per
+    expert, odd tile counts (one-tile units), EP slices, empty experts under Zipf routing, and
+    I % 256 both zero (GEMM A launched on both unit shapes, the plan choosing) and not."""
+    rng = random.Random(seed)
+    out = []
+    for i in range(n):
+        H = 256 * rng.randint(1, 4)
+        I = 128 * rng.randint(1, 4)
+        E_local = rng.randint(2, 12)
+        expert_begin = rng.choice([0, rng.randint(1, 6)])
+        num_experts = expert_begin + E_local + rng.choice([0, rng.randint(1, 8)])
+        K = rng.randint(1, min(8, num_experts))
+        T = rng.randint(300, 1500)
+        routing = rng.choice(["uniform", "zipf1.2"])
+        out.append(MoEConfig(f"sqrand{i}_h{H}_i{I}", T, H, I, num_experts, expert_begin, E_local, K, 128,
+                             "bf16", routing))
+    return out
+
+
+SHAPES = _shapes() + _sq_shapes()
 
 
 @pytest.mark.parametrize("cfg", SHAPES, ids=[c.name for c in SHAPES])
