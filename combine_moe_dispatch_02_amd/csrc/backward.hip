@@ -197,13 +197,21 @@ int launch_combine_backward(const void* dout, const float* topk_weights, const v
 // step, after a vmcnt wait that leaves the two newer steps outstanding. The stages are
 // separate LDS objects used with constant indices, so the compiler can tell a step's
 // reads from the DMA writes in flight (and adds no wait of its own).
+//
+// The K loop issues no vector ALU work: each lane's fragment and DMA offsets are fixed for
+// the whole kernel (stage bases and the fragment's second half are immediate offsets), and
+// the step's first row, the tile's first column and the segment's end go into the DMA's
+// buffer resource (scalar work). At 16 cycles per MFMA and two waves per SIMD, per-step
+// address arithmetic of about 90 vector instructions per wave had filled most of the issue
+// slots the MFMAs leave. The last three steps of a unit already load the first three steps
+// of the workgroup's next unit, whose output then goes out through a per-wave staging
+// buffer while the ring keeps those steps.
 // --------------------------------------------------------------------------------
 struct WgradArgs {
   const uint8_t* A;
   const uint8_t* B;
   uint8_t* C;
   int32_t N1, N2;
-  uint32_t a_bytes, b_bytes;   // buffer ranges of A and B (pool_rows rows)
   const int32_t* offsets;
   const int32_t* counts;
   int32_t E;
@@ -235,7 +243,12 @@ __global__ __launch_bounds__(512, 1) void wgrad_kernel(WgradArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_t1[2][kWgOpBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_t2[2][kWgOpBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_t3[2][kWgOpBytes];
+  // experts in unit order with their segments: read from LDS when a unit starts (a global
+  // load there would wait on every DMA and store the wave has in flight)
   __shared__ int s_order[kWgMaxE];
+  __shared__ int s_r0[kWgMaxE];
+  __shared__ int s_cnt[kWgMaxE];
+  __shared__ __attribute__((aligned(16))) uint8_t s_out[8][2048];   // per-wave output staging
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -253,6 +266,8 @@ __global__ __launch_bounds__(512, 1) void wgrad_kernel(WgradArgs a) {
       r += (cf > c) || (cf == c && f < e);
     }
     s_order[r] = e;
+    s_r0[r] = a.offsets[e];
+    s_cnt[r] = c;
   }
   __syncthreads();
 
@@ -271,97 +286,135 @@ __global__ __launch_bounds__(512, 1) void wgrad_kernel(WgradArgs a) {
   const int frow = 8 * lhi + (l16 >> 2);
   const int fbyte = 8 * (l16 & 3);
 
-  for (int round = 0;; ++round) {
-    if (round * G >= total) break;
+  // a unit's sources: its expert, output tile and segment (wave-uniform), and its K steps
+  // rounded up to whole rounds of four, at least one round (the steps past the segment add
+  // zeros; a unit with no rows still runs one round, which carries the next unit's first
+  // three steps)
+  struct WgUnit {
+    int e, t1, t2, r0, cnt, nr;
+    bool ok;
+  };
+  auto unit_of = [&](int round) {
+    WgUnit U;
     const int u = round * G + ((round & 1) ? G - 1 - slot : slot);
-    if (u >= total) continue;
-    const int e = s_order[u / per_e];
-    const int tix = u % per_e;
-    const int t1 = tix / a.tiles2, t2 = tix % a.tiles2;
-    const int r0 = a.offsets[e];
-    const int cnt = a.counts[e];
-    const int nsteps = (cnt + kWgK - 1) / kWgK;
+    U.ok = u < total;
+    const int uu = U.ok ? u : 0;
+    const int rk = uu / per_e;
+    U.e = __builtin_amdgcn_readfirstlane(s_order[rk]);
+    U.r0 = __builtin_amdgcn_readfirstlane(s_r0[rk]);
+    U.cnt = __builtin_amdgcn_readfirstlane(s_cnt[rk]);
+    const int tix = uu % per_e;
+    U.t1 = tix / a.tiles2;
+    U.t2 = tix % a.tiles2;
+    const int nr = ((U.cnt + kWgK - 1) / kWgK + 3) & ~3;
+    U.nr = nr > 4 ? nr : 4;
+    return U;
+  };
 
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(dma_b ? a.B : a.A, dma_b ? a.b_bytes : a.a_bytes);
-    const uint32_t ld = (uint32_t)(dma_b ? a.N2 : a.N1) * 2u;
-    const uint32_t col0 = (uint32_t)((dma_b ? t2 : t1) * kWgTile) * 2u;
-    const uint32_t oob = dma_b ? a.b_bytes : a.a_bytes;
-
-    auto stage = [&](auto ST) -> uint8_t(*)[kWgOpBytes] {
-      constexpr int k = decltype(ST)::value;
-      if constexpr (k == 0) return s_t0;
-      else if constexpr (k == 1) return s_t1;
-      else if constexpr (k == 2) return s_t2;
-      else return s_t3;
-    };
-    auto dma = [&](int s, auto ST) {
-      uint8_t* base = &stage(ST)[dma_b ? 1 : 0][0];
+  const uint8_t* src = dma_b ? a.B : a.A;
+  const uint32_t ld = (uint32_t)(dma_b ? a.N2 : a.N1) * 2u;
+  // the lane's source offset within a step for each of its 4 blocks: row of the step times
+  // the row pitch, plus its chunk moved by the row's permutation (the step's first row and
+  // the tile's first column go into the buffer resource, so no per-step vector work)
+  uint32_t voff[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int blk = (blk0 + q) & 15;
-        const int row = 2 * blk + lrow;                  // row of the step
-        const int r = s * kWgK + row;                    // row of the segment
-        const uint32_t off = r < cnt ? (uint32_t)(r0 + r) * ld + col0 + (uint32_t)((lchunk ^ wg_swz(row)) << 4) : oob;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (__attribute__((address_space(3))) void*)(base + blk * 1024), 16, off, 0, 0, 0);
-      }
-    };
-    // fr, fb: this lane's fragment row and byte, passed through an empty asm at each step
-    // so the compiler recomputes the 48 read addresses per step instead of keeping them
-    // all live across the loop
-    auto frag = [&](const uint8_t* tile, int col16, int fr, int fbt) {   // columns col16..col16+15
-      const uint8_t* p0 = tile + wg_at(fr, col16 * 2 + fbt);
-      const uint8_t* p1 = tile + wg_at(fr + 4, col16 * 2 + fbt);
-      const wg_bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((wg_lds_bf16x4*)(p0));
-      const wg_bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((wg_lds_bf16x4*)(p1));
-      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    };
+  for (int q = 0; q < 4; ++q) {
+    const int row = 2 * ((blk0 + q) & 15) + lrow;
+    voff[q] = (uint32_t)row * ld + (uint32_t)((lchunk ^ wg_swz(row)) << 4);
+  }
 
-    wg_f32x4 acc[8][4];
+  auto stage = [&](auto ST) -> uint8_t(*)[kWgOpBytes] {
+    constexpr int k = decltype(ST)::value;
+    if constexpr (k == 0) return s_t0;
+    else if constexpr (k == 1) return s_t1;
+    else if constexpr (k == 2) return s_t2;
+    else return s_t3;
+  };
+  // the 4 DMAs of step s of a segment (r0, cnt) at byte column col0 into stage ST: the
+  // resource starts at the step's first row and ends after the segment's last row, so the
+  // rows past the segment read out of range (zeros, no traffic); cnt = 0 reads only zeros
+  auto dma = [&](int r0, int cnt, uint32_t col0, int s, auto ST) {
+    uint8_t* base = &stage(ST)[dma_b ? 1 : 0][0];
+    const int left = cnt - s * kWgK;
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(src + (int64_t)(r0 + s * kWgK) * ld + col0, left > 0 ? (uint32_t)left * ld : 0u);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int blk = (blk0 + q) & 15;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(base + blk * 1024), 16, voff[q], 0, 0, 0);
+    }
+  };
+  auto col_of = [&](const WgUnit& U) { return (uint32_t)((dma_b ? U.t2 : U.t1) * kWgTile) * 2u; };
+  // the lane's fragment offsets within a step's operand tile: B fragments tn (N2 columns
+  // wn*64 + tn*16 ..), A fragments tm (N1 columns wm*128 + tm*16 ..); the second half of a
+  // fragment is 4 rows further (the row permutation ignores that row bit): +2048 bytes
+  uint32_t fb_off[4], fa_off[8];
+#pragma unroll
+  for (int tn = 0; tn < 4; ++tn) fb_off[tn] = wg_at(frow, (wn * 64 + tn * 16) * 2 + fbyte);
+#pragma unroll
+  for (int tm = 0; tm < 8; ++tm) fa_off[tm] = wg_at(frow, (wm * 128 + tm * 16) * 2 + fbyte);
+  auto frag = [&](const uint8_t* tile, uint32_t off) {
+    const wg_bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((wg_lds_bf16x4*)(tile + off));
+    const wg_bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((wg_lds_bf16x4*)(tile + off + 2048));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
+  using C3 = std::integral_constant<int, 3>;
+
+  int round = 0;
+  WgUnit cur = unit_of(0);
+  if (!cur.ok) return;
+  // the first unit's steps 0..2 in flight, then wait for step 0. Every step issues its 4
+  // DMAs (rows past the segment read zeros), so the counts below are exact. Later units'
+  // first three steps go out during the last steps of the unit before (below).
+  dma(cur.r0, cur.cnt, col_of(cur), 0, C0{});
+  dma(cur.r0, cur.cnt, col_of(cur), 1, C1{});
+  dma(cur.r0, cur.cnt, col_of(cur), 2, C2{});
+  __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): step 0 has landed
+  __syncthreads();
+
+  wg_f32x4 acc[8][4];
+  for (;;) {
+    const WgUnit nxt = unit_of(round + 1);
+    const uint32_t col_cur = col_of(cur), col_nxt = col_of(nxt);
+    const int cnt_nxt = nxt.ok ? nxt.cnt : 0;
 #pragma unroll
     for (int tm = 0; tm < 8; ++tm)
 #pragma unroll
       for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = wg_f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // prologue: steps 0..2 in flight, wait for step 0. Every step issues its 4 DMAs
-    // (rows past the segment read zeros), so the counts below are exact.
-    using C0 = std::integral_constant<int, 0>;
-    using C1 = std::integral_constant<int, 1>;
-    using C2 = std::integral_constant<int, 2>;
-    using C3 = std::integral_constant<int, 3>;
-    dma(0, C0{});
-    dma(1, C1{});
-    dma(2, C2{});
-    __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): step 0 has landed
-    __syncthreads();
     // step s computes from stage s % 4 and sends step s+3 into stage (s+3) % 4, the one
-    // step s-1 read (all its reads are behind the last barrier)
+    // step s-1 read (all its reads are behind the last barrier). Past this unit's steps,
+    // s+3 is the next unit's step s+3-nr (nr is a multiple of four, so the stages line up).
     auto step = [&](int s, auto ST, auto SN) {
-      int fr = frow, fbt = fbyte;
-      asm volatile("" : "+v"(fr), "+v"(fbt));
-      __builtin_amdgcn_sched_barrier(0);
       const uint8_t* ta = &stage(ST)[0][0];
       const uint8_t* tb = &stage(ST)[1][0];
       wg_bf16x8 fb[4];
 #pragma unroll
-      for (int tn = 0; tn < 4; ++tn) fb[tn] = frag(tb, wn * 64 + tn * 16, fr, fbt);
-      wg_bf16x8 fa_cur = frag(ta, wm * 128, fr, fbt);
+      for (int tn = 0; tn < 4; ++tn) fb[tn] = frag(tb, fb_off[tn]);
+      wg_bf16x8 fa_cur = frag(ta, fa_off[0]);
       // the step's first fragment reads go out before its DMAs, whose issue then overlaps
       // their latency (about 3% faster than the other way round)
       __builtin_amdgcn_sched_barrier(0);
-      dma(s + 3, SN);
+      const bool here = s + 3 < cur.nr;
+      dma(here ? cur.r0 : nxt.r0, here ? cur.cnt : cnt_nxt, here ? col_cur : col_nxt,
+          here ? s + 3 : s + 3 - cur.nr, SN);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int tm = 0; tm < 8; ++tm) {
         wg_bf16x8 fa_next = fa_cur;
-        if (tm + 1 < 8) fa_next = frag(ta, wm * 128 + (tm + 1) * 16, fr, fbt);
+        if (tm + 1 < 8) fa_next = frag(ta, fa_off[tm + 1]);
 #pragma unroll
         for (int tn = 0; tn < 4; ++tn)
           acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[tn], fa_cur, acc[tm][tn], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         fa_cur = fa_next;
       }
-      // vmcnt(8): this wave's DMAs of step s+1 have landed (s+2, s+3 may not); a bare
+      // vmcnt(8): this wave's DMAs of step s+1 have landed (s+2, s+3 may not; loads land in
+      // order, and a unit's output stores in between only make the wait longer); a bare
       // barrier then makes step s+1 whole for every wave. (A __syncthreads would add a
       // workgroup release, which waits for every DMA in flight.) The stage the next step
       // overwrites was read by this step, whose reads the MFMAs above have consumed.
@@ -369,57 +422,53 @@ __global__ __launch_bounds__(512, 1) void wgrad_kernel(WgradArgs a) {
       __builtin_amdgcn_s_barrier();
     };
     // whole rounds of four steps (a branch between the steps would make the compiler
-    // copy the accumulators at each exit): the steps past the segment add zeros
-    for (int s = 0; s < nsteps; s += 4) {
+    // copy the accumulators at each exit)
+    for (int s = 0; s < cur.nr; s += 4) {
       step(s, C0{}, C3{});
       step(s + 1, C1{}, C0{});
       step(s + 2, C2{}, C1{});
       step(s + 3, C3{}, C2{});
     }
-    // the DMAs still in flight (up to three steps past the end) land before the ring is reused
-    wait_vm0();
-    __syncthreads();
 
-    // Output through the idle ring: stored straight from the accumulators, a lane's 8-byte
-    // pieces of 16 rows would make every store instruction touch 16 rows. Each wave instead
-    // writes its 128 x 64 bf16 block into its own 16 KiB of the ring (128-byte rows, 16-byte
-    // chunks rotated by row & 7), reads it back row-contiguous (a wave's LDS accesses complete
-    // in order) and stores 8 whole 128-byte row segments per instruction.
+    // Output through the wave's 2 KiB of staging: stored straight from the accumulators, a
+    // lane's 8-byte pieces of 16 rows would make every store instruction touch 16 rows. Each
+    // wave writes one 16-row tile row of its 128 x 64 bf16 block at a time (128-byte rows,
+    // 16-byte chunks rotated by row), reads it back row-contiguous (a wave's LDS accesses
+    // complete in order) and stores 2 x 8 whole 128-byte row segments. The ring is not
+    // touched: it already holds the next unit's first steps.
     // Accumulator (tm, tn) of a lane: block row tm*16 + l16, block columns tn*16 + 4*lhi + (0..3).
-    uint8_t* sw = wave < 2 ? &s_t0[wave & 1][0] : wave < 4 ? &s_t1[wave & 1][0]
-                : wave < 6 ? &s_t2[wave & 1][0] : &s_t3[wave & 1][0];
+    uint8_t* sw = &s_out[wave][0];
+    // C[e][n1][n2]: block row r is n1 = t1*256 + wm*128 + r, block column c is n2 = t2*256 + wn*64 + c
+    uint8_t* cbase = a.C + ((int64_t)cur.e * a.N1 + cur.t1 * kWgTile + wm * 128) * a.N2 * 2 +
+                     (int64_t)(cur.t2 * kWgTile + wn * 64) * 2;
+    // lane-dependent addresses formed here, from an opaque copy of the lane index: hoisted
+    // above the K loop, they would hold registers there
+    int el = lane;
+    asm volatile("" : "+v"(el));
+    const int e16 = el & 15, ehi = el >> 4, oc = el & 7, orow = el >> 3;
 #pragma unroll
-    for (int tm = 0; tm < 8; ++tm)
+    for (int tm = 0; tm < 8; ++tm) {
 #pragma unroll
       for (int tn = 0; tn < 4; ++tn) {
         u32x2 o;
         o.x = pack_bf16x2(acc[tm][tn][0], acc[tm][tn][1]);
         o.y = pack_bf16x2(acc[tm][tn][2], acc[tm][tn][3]);
-        const int row = tm * 16 + l16;
-        const int chunk = tn * 2 + (lhi >> 1);
-        *reinterpret_cast<u32x2*>(sw + row * 128 + ((chunk ^ (row & 7)) << 4) + (lhi & 1) * 8) = o;
+        const int chunk = tn * 2 + (ehi >> 1);
+        *reinterpret_cast<u32x2*>(sw + e16 * 128 + ((chunk ^ (e16 & 7)) << 4) + (ehi & 1) * 8) = o;
       }
-    // C[e][n1][n2]: block row r is n1 = t1*256 + wm*128 + r, block column c is n2 = t2*256 + wn*64 + c
-    uint8_t* cbase = a.C + ((int64_t)e * a.N1 + t1 * kWgTile + wm * 128) * a.N2 * 2 +
-                     (int64_t)(t2 * kWgTile + wn * 64) * 2;
-    // through an empty asm, so that the 16 row addresses are formed here rather than
-    // hoisted above the K loop, where they would hold 32 registers
-    int oc = lane & 7, orow = lane >> 3;
-    asm volatile("" : "+v"(oc), "+v"(orow));
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = i * 8 + orow;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(sw + row * 128 + ((oc ^ (row & 7)) << 4));
-      *reinterpret_cast<u32x4*>(cbase + (int64_t)row * a.N2 * 2 + oc * 16) = v;
+      for (int p = 0; p < 2; ++p) {
+        const int row = p * 8 + orow;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(sw + row * 128 + ((oc ^ (row & 7)) << 4));
+        *reinterpret_cast<u32x4*>(cbase + (int64_t)(tm * 16 + row) * a.N2 * 2 + oc * 16) = v;
+      }
     }
-    // every wave has read its block back (the stores consumed the reads) before the next
-    // unit's DMAs refill the ring; a bare barrier, since a __syncthreads would also wait
-    // for the stores to complete
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
+    if (!nxt.ok) break;
+    cur = nxt;
+    ++round;
   }
+  // the reloads of the last steps land before the workgroup ends
+  wait_vm0();
 }
 
 int launch_wgrad(const moe_plan_t& p, int32_t pool_rows, const void* A, int32_t N1, const void* B, int32_t N2,
@@ -430,8 +479,6 @@ int launch_wgrad(const moe_plan_t& p, int32_t pool_rows, const void* A, int32_t 
   a.C = static_cast<uint8_t*>(C);
   a.N1 = N1;
   a.N2 = N2;
-  a.a_bytes = (uint32_t)((int64_t)pool_rows * N1 * 2);
-  a.b_bytes = (uint32_t)((int64_t)pool_rows * N2 * 2);
   a.offsets = p.offsets;
   a.counts = p.counts;
   a.E = p.E_local;
