@@ -528,11 +528,14 @@ __device__ inline void combine_tail(const FfnArgs& a, int* s_item) {
 }
 
 
+// Slot of chunk c of pool row r in an A stage (128-byte rows). bf16 (16-byte fragment
+// reads): the chunk moves by r % 8, so 8 consecutive rows reading one chunk column hit 8
+// distinct 16-byte bank groups. fp8 / mxfp4 (32-byte fragment reads, two chunks per lane):
+// rows r and r + 8 also differ in the slot's low bit -- with r % 8 alone these reads spent
+// 9-11% of CU cycles in bank conflicts, and the extra bit gives the bf16 reads 11-17%.
+template <bool FP8>
 __device__ inline uint32_t swz_a(int r, int c) {
-  // 16 consecutive rows reading one chunk column hit 16 distinct 16-byte bank groups: the
-  // chunk moves by r % 8, and rows r and r + 8 (same banks otherwise) differ in the slot's
-  // low bit (with r % 8 alone, the fp8 fragment reads spent 9-11% of CU cycles in bank conflicts)
-  return (uint32_t)(r * 128 + ((c ^ (r & 7) ^ ((r >> 3) & 1)) << 4));
+  return (uint32_t)(r * 128 + ((c ^ (r & 7) ^ (FP8 ? (r >> 3) & 1 : 0)) << 4));
 }
 
 // MX (mxfp4): A is MXFP8 (e4m3 rows as in fp8, plus one E8M0 byte per 32 K), B is
@@ -679,7 +682,7 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
       for (int i = 0; i < C::kALoads; ++i) {
         const int c = tid + i * C::kThreads;
         if (C::kAChunks % C::kThreads == 0 || c < C::kAChunks)
-          *reinterpret_cast<u32x4*>(&s_a[stage][0] + swz_a(c >> 3, c & 7)) = ra[st][i];
+          *reinterpret_cast<u32x4*>(&s_a[stage][0] + swz_a<false>(c >> 3, c & 7)) = ra[st][i];
       }
       if constexpr (FP8) {
         if (tid < BM) s_as[stage][tid] = ras[st];
@@ -742,7 +745,7 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
       rbh[bb][tn][hf] = __builtin_amdgcn_raw_buffer_load_b128(br, (uint32_t)lane * 16u, tbase, 0);
     };
     // fp8: the A rows of step ks into LDS stage ST by LDS-DMA (row r at r*128, chunk c at
-    // slot c ^ (r & 7) ^ ((r >> 3) & 1), as swz_a: lane i of 1 KiB load q fetches row
+    // slot c ^ (r & 7) ^ ((r >> 3) & 1), as swz_a<true>: lane i of 1 KiB load q fetches row
     // 8q + i/8, chunk (i%8) ^ (i/8) ^ (q & 1)),
     // and the rows' activation scales into ras[0] (stored to LDS before the barrier)
     auto dma_rows = [&](auto STAGE, int ks) {
@@ -819,7 +822,7 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
       for (int i = 0; i < kDma; ++i) {
         const int q = wn * kDma + i;
         const uint32_t off = (uint32_t)(q * 8 + (lane >> 3)) * (uint32_t)a.lda +
-                             (uint32_t)((lane & 7) ^ (lane >> 3) ^ (q & 1)) * 16u;
+                             (uint32_t)((lane & 7) ^ (lane >> 3)) * 16u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             ar, (__attribute__((address_space(3))) void*)(base + q * 1024), 16, off, (uint32_t)ks * 128u, 0, 0);
       }
@@ -908,15 +911,15 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
         if constexpr (!FP8) {
 #pragma unroll
           for (int kk = 0; kk < KS; ++kk) {
-            const bf16x8_t fa = *reinterpret_cast<const bf16x8_t*>(sa + swz_a(r, kk * 4 + lhi));
+            const bf16x8_t fa = *reinterpret_cast<const bf16x8_t*>(sa + swz_a<false>(r, kk * 4 + lhi));
 #pragma unroll
             for (int tn = 0; tn < TN; ++tn)
               acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                   __builtin_bit_cast(bf16x8_t, rb[bb][tn][kk]), fa, acc[tm][tn], 0, 0, 0);
           }
         } else {
-          const u32x4 lo = *reinterpret_cast<const u32x4*>(sa + swz_a(r, 2 * lhi));
-          const u32x4 hi = *reinterpret_cast<const u32x4*>(sa + swz_a(r, 2 * lhi + 1));
+          const u32x4 lo = *reinterpret_cast<const u32x4*>(sa + swz_a<true>(r, 2 * lhi));
+          const u32x4 hi = *reinterpret_cast<const u32x4*>(sa + swz_a<true>(r, 2 * lhi + 1));
           const i32x8_t fa = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
           // acc is kept in units of this K block's scale: rescale by old/new, then
           // accumulate the block's integer-grid product in place
@@ -962,8 +965,8 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
       const float wr1 = sbq[1] * __builtin_amdgcn_rcpf(sbc1);
       auto rd_a = [&](int tm) {
         const int r = tm * 16 + l16;
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(sa + swz_a(r, 2 * lhi));
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(sa + swz_a(r, 2 * lhi + 1));
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(sa + swz_a<true>(r, 2 * lhi));
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(sa + swz_a<true>(r, 2 * lhi + 1));
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       };
       // fragments and row ratios are read one group ahead
@@ -1035,8 +1038,8 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       auto rd_a = [&](int tm) {
         const int r = tm * 16 + l16;
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(sa + swz_a(r, lhi));
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(sa + swz_a(r, lhi + 4));
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(sa + swz_a<true>(r, lhi));
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(sa + swz_a<true>(r, lhi + 4));
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       };
       u32x8_t fa_cur = rd_a(0);
@@ -1092,14 +1095,14 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
       const int ka = ks + 2 < nk ? ks + 2 : nk - 1;
       const uint8_t* sa = &s_a[bb][0];
       __builtin_amdgcn_sched_barrier(0);
-      bf16x8_t fa_cur = *reinterpret_cast<const bf16x8_t*>(sa + swz_a(l16, lhi));
+      bf16x8_t fa_cur = *reinterpret_cast<const bf16x8_t*>(sa + swz_a<false>(l16, lhi));
 #pragma unroll
       for (int g = 0; g < 2 * TM; ++g) {
         const int kk = g / TM, tm = g % TM;
         bf16x8_t fa_next = fa_cur;
         if (g + 1 < 2 * TM) {
           const int kk1 = (g + 1) / TM, tm1 = (g + 1) % TM;
-          fa_next = *reinterpret_cast<const bf16x8_t*>(sa + swz_a(tm1 * 16 + l16, kk1 * 4 + lhi));
+          fa_next = *reinterpret_cast<const bf16x8_t*>(sa + swz_a<false>(tm1 * 16 + l16, kk1 * 4 + lhi));
         }
         if (g == 0) load_a(std::integral_constant<int, bb>{}, ka);
         if (g >= 1 && g <= TN) load_b1(NB{}, g - 1, 0, kn);
@@ -1127,14 +1130,14 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
       const int kd = ks + 3 < nk ? ks + 3 : nk - 1;   // past the end: reload the last step (unread)
       const uint8_t* sa = ring(ST);
       __builtin_amdgcn_sched_barrier(0);
-      bf16x8_t fa_cur = *reinterpret_cast<const bf16x8_t*>(sa + swz_a(l16, lhi));
+      bf16x8_t fa_cur = *reinterpret_cast<const bf16x8_t*>(sa + swz_a<false>(l16, lhi));
 #pragma unroll
       for (int g = 0; g < 2 * TM; ++g) {
         const int kk = g / TM, tm = g % TM;
         bf16x8_t fa_next = fa_cur;
         if (g + 1 < 2 * TM) {
           const int kk1 = (g + 1) / TM, tm1 = (g + 1) % TM;
-          fa_next = *reinterpret_cast<const bf16x8_t*>(sa + swz_a(tm1 * 16 + l16, kk1 * 4 + lhi));
+          fa_next = *reinterpret_cast<const bf16x8_t*>(sa + swz_a<false>(tm1 * 16 + l16, kk1 * 4 + lhi));
         }
         if (g == 0) dma_r(SN{}, kd);
         if (g >= 1 && g <= TN) load_b1(NB{}, g - 1, 0, kn);
