@@ -1,6 +1,7 @@
 """bench.py's host logic on the CPU: the algorithmic work it divides by (closed forms of a
 hand-built routing), the rocprofv3 summary (kernel table, copy-calibrated counter scales,
-FFN sums), the traffic figure's source-hash gate, and the refusal of more than one GPU."""
+FFN sums), the traffic figure's source-hash gate, the oracle sample's sizing, and the refusal
+of more than one GPU."""
 import csv
 import json
 import os
@@ -87,3 +88,31 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120, cwd=ROOT)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_cpu_baseline_sizing(monkeypatch):
+    # a stand-in oracle whose time per token falls with the sample size (as the real one's
+    # matrix products do): the two probes size a first sample, which finishes in under half
+    # the target, so it is grown once by the ratio and timed again
+    import types
+
+    clock = {"t": 0.0}
+
+    def moe_layer(inp, tokens):
+        n = len(tokens)
+        clock["t"] += 0.5 + n * (0.004 if n <= 256 else 0.001)
+        return types.SimpleNamespace(out=np.zeros((n, 4)))
+
+    fake = types.SimpleNamespace(moe_layer=moe_layer, bf16_to_f64=lambda x: x, max_norm_rel_err=lambda a, b: 0.0)
+    monkeypatch.setitem(sys.modules, "oracle", fake)
+    monkeypatch.setattr(bench.time, "perf_counter", lambda: clock["t"])
+    out = bench.cpu_baseline(None, max_tokens=100000, target_s=15.0)
+    # probes: 64 -> 0.756 s, 256 -> 1.524 s: 4 ms per token, 0.5 s fixed -> 3624 tokens (14.5 / 0.004,
+    # rounded down), which take 4.124 s (< 7.5 s) -> grown to 3624 * 15 / 4.124 = 13181 tokens, 13.68 s
+    assert out["sample"].startswith("tokens 0..13180 ")
+    assert "3624 tokens took 4.1 s" in out["sample"]
+    assert out["value"] == pytest.approx(13181 / (0.5 + 13.181))
+    # a sample capped by the workload is not grown
+    clock["t"] = 0.0
+    capped = bench.cpu_baseline(None, max_tokens=2000, target_s=15.0)
+    assert capped["sample"].startswith("tokens 0..1999 ") and "took" not in capped["sample"]
