@@ -21,9 +21,12 @@ struct SqUnit {
 // before e. Within expert e, units go in groups of `group` row units; inside a group,
 // N block by N block, the group's row units back to back: units that run together
 // share weight panels and pool rows.
-__device__ __attribute__((always_inline)) inline SqUnit sq_unit(const SqArgs& a, const int32_t* s_ru, int u) {
+// Each expert's first pool tile comes from a table (t0s[e] = min(offsets[e] / 128,
+// max_tiles) for e <= E, in LDS), so that decoding a unit reads no global memory.
+__device__ __attribute__((always_inline)) inline SqUnit sq_unit(const SqArgs& a, const int32_t* s_ru,
+                                                                    const int32_t* t0s, int u) {
   int lo = 0, hi = a.n_experts - 1;
-  while (lo < hi) {  // the last expert whose first unit is <= u (empty experts share a start)
+  while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (s_ru[mid] * a.NB <= u) lo = mid;
     else hi = mid - 1;
@@ -37,12 +40,8 @@ __device__ __attribute__((always_inline)) inline SqUnit sq_unit(const SqArgs& a,
   const int l2 = l - g * a.group * a.NB;
   r.j = l2 / gsz;
   const int ru = g * a.group + (l2 - r.j * gsz);
-  const int t0 = min(a.offsets[lo] >> 7, a.max_tiles);
-  const int t1 = min(a.offsets[lo + 1] >> 7, a.max_tiles);
-  r.m = t0 + 2 * ru;
-  r.two = r.m + 1 < t1;
-  // uniform over the wave (all lanes read the same LDS words): keep the unit in scalar
-  // registers, so that its buffer resources stay scalar too
+  r.m = t0s[lo] + 2 * ru;
+  r.two = r.m + 1 < t0s[lo + 1];
   r.e = __builtin_amdgcn_readfirstlane(r.e);
   r.m = __builtin_amdgcn_readfirstlane(r.m);
   r.two = __builtin_amdgcn_readfirstlane(r.two);

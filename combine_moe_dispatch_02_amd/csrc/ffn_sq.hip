@@ -1,58 +1,58 @@
-// A3 + A4 on 256 x 256 work units: the expert FFN's grouped GEMMs (bf16, MFMA-tiled
-// weights, pool tile 128) with both operands brought into LDS by DMA.
+// A3 + A4 on 256 x 256 work units: the expert FFN's grouped GEMMs (bf16, MFMA-tiled weights,
+// pool tile 128) with both operands brought into LDS by DMA, four waves, one per SIMD.
 //
-// StreamEP README, "How it works": the forward grouped GEMMs "A" (w1, gate|up, then
-// the activation) and "Y" (w2) read the expert-major, tile-padded pool as it stands
-// and start on a pool tile once dispatch has marked it (per-tile streaming). The
-// arithmetic is that of the 128 x 512 big-tile kernel (ffn.hip): one chain of
-// v_mfma_f32_16x16x32_bf16 per output element over K in ascending order, the same
-// SwiGLU epilogue, so h and y carry the same bits whichever kernel ran.
+// StreamEP README, "How it works": the forward grouped GEMMs "A" (w1, gate|up, then the
+// activation) and "Y" (w2) read the expert-major, tile-padded pool as it stands and start
+// on a pool tile once dispatch has marked it (per-tile streaming). The arithmetic is that
+// of the 128 x 512 big-tile kernel (ffn.hip): one chain of v_mfma_f32_16x16x32_bf16 per
+// output element over K in ascending order, the same SwiGLU epilogue, so h and y carry the
+// same bits whichever kernel ran.
 //
 // Work unit = (expert e, two consecutive pool tiles m, m+1 of e, N block j of 256
-// columns); an expert with an odd tile count ends with a one-tile unit, whose second
-// row half (rows of the next segment, outside the DMA range) is computed from zeros and
-// not stored. GEMM A's N block is 128 gate columns and
-// the matching 128 up columns of w1, so SwiGLU stays in the lane that holds both.
-// 8 waves: wave w computes rows 128 (w / 4) .. +128 and 64 of the 256 columns
-// (w % 4), i.e. 8 x 4 MFMA tiles, 128 accumulators per lane.
+// columns); an expert with an odd tile count ends with a one-tile unit, whose second row
+// half (rows of the next segment, outside the DMA range) is computed from zeros and not
+// stored. GEMM A's N block is 128 gate columns and the matching 128 up columns of w1. Wave
+// w computes rows 128 (w / 2) .. +128 and 128 of the 256 columns (w % 2; in GEMM A 64 gate
+// and the matching 64 up columns, so SwiGLU stays in the lane that holds both): 8 x 8 MFMA
+// tiles, 256 accumulators per lane, kept in the accumulation registers. Per 32-wide K step
+// a wave reads 16 fragments from LDS for 64 MFMAs.
 //
-// Operands. The pool (or h) rows move in K stages of 64 values, 128 bytes a row (one
-// cache line): 256 rows, 32 KiB. They are stored row by row, their eight 16-byte chunks
-// XOR-permuted by row % 8: the eight lanes of a DMA that fill one row fetch its whole
-// line, and the eight lanes of a fragment read that share a chunk index (eight rows)
-// land on eight distinct 16-byte slots of a 128-byte bank row. The weights move in K
-// stages of 32 values: the tiled layout already holds MFMA fragments as contiguous 1 KiB
-// blocks (lane l's 16 bytes = row l % 16, K values 8 (l / 16) .. +8 of a 32-wide K tile),
-// 16 of them per stage (16 KiB), which the DMA copies as they are. Rows past the unit's
-// real rows (a segment's padding) lie outside the DMA's buffer range: they are not
-// fetched and land as zeros. Each wave issues its share by LDS-DMA (buffer_load ... lds),
-// so no register holds a load in flight, and every request covers whole cache lines.
+// Operands. The pool (or h) rows move in K stages of 64 values, 128 bytes a row (one cache
+// line): 256 rows, 32 KiB, stored row by row with their eight 16-byte chunks XOR-permuted
+// by row % 8, so that the eight lanes of a DMA that fill one row fetch its whole line and
+// the lanes of a fragment read that share a chunk index land on distinct banks. The weights
+// move in K stages of 32 values: the tiled layout already holds MFMA fragments as
+// contiguous 1 KiB blocks, 16 of them per stage (16 KiB), which the DMA copies as they
+// are. Rows past the unit's real rows lie outside the DMA's buffer range: they are not
+// fetched and land as zeros. Every wave issues its share by LDS-DMA (buffer_load ... lds).
 //
-// Pipeline, in steps of 32 K values. Weights: a ring of four 16 KiB stages, three steps
-// ahead. Pool rows: two 32 KiB stages of 64 K values, the next one loaded during the
-// current one (issued at its first step, used two steps later). About 80 KiB per CU are
-// in flight. Step s: wait for this wave's DMAs that step s reads (vmcnt), barrier (every
-// wave's are in; the stages step s - 1 read are free), issue the DMAs of weight stage
-// s + 3 and, on even steps, of pool-row stage s / 2 + 1, then the MFMAs of step s. The
-// stages run on across units: the last steps of a unit load the next unit's first
-// stages, so a unit's epilogue overlaps them. The last MFMA group of each step is
-// issued after the next barrier, while the next step's first fragment reads are in
-// flight. The stages are separate LDS objects used with constant indices (the K loop
-// runs four steps per round), so the compiler can tell a step's reads from the DMA
-// writes in flight to the other stages and adds no wait of its own.
+// Pipeline, in steps of 32 K values. Weights: four 16 KiB stages, stage s loaded during
+// step s - 4 into the stage that step s - 1 read. Pool rows: two 32 KiB stages, stage d
+// loaded during step 2d - 3. With one wave per SIMD no other wave covers a wait, so the
+// fragments of step s + 1 are read during step s (two register sets). Step s: the first
+// kPre MFMAs; wait for this wave's DMAs of the stages read during s; barrier (every wave's
+// are in, and every wave has finished reading the stages of step s, which the DMAs of this
+// step overwrite); then the remaining MFMAs with the step's memory operations between them
+// (sq_op): the fragment reads of step s + 1 and the DMAs of weight stage s + 4 and, on odd
+// steps, pool-row stage (s + 3) / 2. The stage count runs on across units: a unit's last
+// steps load the next unit's first stages, and its first step's fragments are read again
+// after the epilogue. The stages are separate LDS objects used with constant indices (the K
+// loop runs four steps per round), so the compiler can tell a step's reads from the DMA
+// writes in flight and adds no wait of its own.
 //
-// Output. Each wave stages one 16-row MFMA tile row at a time in its own 2 KiB of LDS
-// (no barrier: a wave's LDS accesses complete in order) and stores whole row segments:
-// 128 bytes (y, or G in training) or 64 bytes (h) per row.
+// Output. Each wave stages one 16-row MFMA tile row at a time in its own 4 KiB of LDS (no
+// barrier: a wave's LDS accesses complete in order) and stores whole row segments (256
+// bytes of y or G a row, 128 bytes of h) through a buffer resource over the unit's rows.
 //
-// Ready flags. GEMM A starts on a tile once dispatch has marked it. If dispatch's
-// count of marked tiles already equals the tile count when a wave starts (dispatch
-// ran before, e.g. on the same stream), one acquire covers every tile; otherwise the
-// wave waits on the flags of each unit's tiles before it loads them. A wait that
-// outlasts the timeout records MOE_ERR_TIMEOUT and marks the call's epoch aborted,
-// which ends the call's other waits; the unit is then computed from whatever the pool
-// holds (the error says the results are invalid).
+// Ready flags. GEMM A starts on a tile once dispatch has marked it. If dispatch's count of
+// marked tiles already equals the tile count when a workgroup starts (dispatch ran before,
+// e.g. on the same stream), one acquire covers every tile; otherwise each wave waits on the
+// flags of each unit's tiles before it loads them. A wait that outlasts the timeout records
+// MOE_ERR_TIMEOUT and marks the call's epoch aborted, which ends the call's other waits; the
+// unit is then computed from whatever the pool holds (the error says the results are
+// invalid).
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 #include "ffn_sq.h"
@@ -65,31 +65,89 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kSqWaves = 8;
+constexpr int kSqWaves = 4;
+constexpr int kPre = 2;            // MFMAs of a step issued before its barrier
 constexpr int kAStage = 32768;   // 256 pool rows x 128 bytes (64 K values)
 constexpr int kBStage = 16384;   // 16 weight row blocks x 1 KiB (32 K values)
 
 __device__ inline float sq_silu_mul(float g, float u) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u; }
 
-// DMA sources of one unit for this wave: the unit's rows (A) and its expert's tiled
-// weights (B), and the byte offsets of the wave's two B row blocks
+// DMA sources of one unit for this wave: the unit's rows (base and bytes), its expert's
+// tiled weights and the byte offset of the first of the wave's four weight row blocks (the
+// next three follow at ktiles KiB each). Kept as plain pointers and sizes: the buffer
+// resources are made where they are used.
 struct SqSrc {
-  __amdgpu_buffer_rsrc_t ar, br;
-  uint32_t b0, b1;
+  const uint8_t* abase;
+  const uint8_t* bbase;
+  uint32_t abytes, b0;
 };
 
 template <bool GEMM_A>
-__device__ __attribute__((always_inline)) inline SqSrc sq_src(const SqArgs& a, const SqUnit& U, int w) {
+__device__ __attribute__((always_inline)) inline SqSrc sq_src(const SqArgs& a, const SqUnit& U, const int32_t* s_end,
+                                                           int w) {
   SqSrc s;
-  // the unit's real rows only: padding rows are not fetched
-  const int real = __builtin_amdgcn_readfirstlane(min(U.two ? 256 : 128, a.offsets[U.e] + a.counts[U.e] - U.m * 128));
-  s.ar = make_rsrc(a.A + (int64_t)U.m * 128 * a.lda, (uint32_t)(max(real, 0) * a.lda));
-  s.br = make_rsrc(a.B + (int64_t)U.e * a.b_expert, (uint32_t)a.b_expert);
-  // B blocks 2w, 2w + 1 of the unit's 16: GEMM A gate blocks 0..7, up blocks 8..15
-  const int rb = GEMM_A ? (w < 4 ? U.j * 8 + 2 * w : a.up_rb + U.j * 8 + 2 * (w - 4)) : U.j * 16 + 2 * w;
+  const int real = __builtin_amdgcn_readfirstlane(min(U.two ? 256 : 128, s_end[U.e] - U.m * 128));
+  s.abase = a.A + (int64_t)U.m * 128 * a.lda;
+  s.abytes = (uint32_t)(max(real, 0) * a.lda);
+  s.bbase = a.B + (int64_t)U.e * a.b_expert;
+  // B blocks 4w .. 4w + 3 of the unit's 16: GEMM A gate blocks 0..7, up blocks 8..15
+  const int rb = GEMM_A ? (w < 2 ? U.j * 8 + 4 * w : a.up_rb + U.j * 8 + 4 * (w - 2)) : U.j * 16 + 4 * w;
   s.b0 = (uint32_t)rb * (uint32_t)a.ktiles * 1024u;
-  s.b1 = s.b0 + (uint32_t)a.ktiles * 1024u;
   return s;
+}
+
+// c += a x b on the matrix core, with c kept in the accumulation registers and updated in
+// place. (Left to the compiler, the 256 accumulators of a wave do not stay put: it moves some
+// of them through the vector registers between steps.) The compiler does not see this as an
+// MFMA, so the wait states around it are the caller's: the accumulators are set to zero a
+// few instructions before the first MFMA reads them (s_nop 4 after the writes), and read
+// back only after 24 wait states (three s_nop 7) behind the last MFMA. The 64 MFMAs of a
+// step update 64 different accumulators, so no MFMA reads one that the one before wrote.
+__device__ __attribute__((always_inline)) inline void mfma_acc(f32x4_t& c, bf16x8_t a, bf16x8_t b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+
+// the four accumulators of c into vector registers, where the caller asks for them (left to
+// itself, the compiler copies all 256 out at once when the K loop ends)
+__device__ __attribute__((always_inline)) inline f32x4_t acc_read(const f32x4_t& c) {
+  float x, y, z, w;
+  asm volatile("v_accvgpr_read_b32 %0, %4\n\tv_accvgpr_read_b32 %1, %5\n\tv_accvgpr_read_b32 %2, %6\n\tv_accvgpr_read_b32 %3, %7"
+               : "=v"(x), "=v"(y), "=v"(z), "=v"(w)
+               : "a"(c[0]), "a"(c[1]), "a"(c[2]), "a"(c[3]));
+  return f32x4_t{x, y, z, w};
+}
+
+// The memory operation issued after MFMA i of a step (i >= kPre; MFMA i is that of
+// accumulator row i / 8, column tile i % 8), as kind << 4 | index: 1 pool-row fragment read,
+// 2 weight fragment read, 3 pool-row DMA, 4 weight DMA, 0 none. In each of the first four
+// rows (the first one's shifted past the kPre MFMAs issued before the barrier): two pairs of
+// fragment reads, with a DMA after each pair on odd steps (pool rows) and after the first
+// pair of every other row on even steps (weights); on odd steps the weight DMAs follow in
+// rows 4 .. 7. Six operations back to back, then two MFMAs without one, measured faster
+// than the operations spread evenly or issued one per MFMA from the barrier on.
+static_assert(kPre <= 2, "the first row keeps six slots");
+constexpr int sq_op(bool odd, int i) {
+  const int g = i >> 3;
+  const int tn = (i & 7) - (g == 0 ? kPre : 0);
+  if (tn < 0) return 0;
+  if (g < 4) {
+    if (tn == 0 || tn == 3) return 1 << 4 | (2 * g + (tn == 3));
+    if (tn == 1 || tn == 4) return 2 << 4 | (2 * g + (tn == 4));
+    if (odd && (tn == 2 || tn == 5)) return 3 << 4 | (2 * g + (tn == 5));
+    if (!odd && (g & 1) == 0 && tn == 2) return 4 << 4 | (g >> 1);
+    return 0;
+  }
+  if (tn != 2) return 0;
+  if (odd) return 4 << 4 | (g - 4);
+  return (g & 1) == 0 ? (4 << 4 | (g >> 1)) : 0;
+}
+
+// c ? x : y on values: the next unit's or this unit's source. (A conditional on the two
+// structs' members would select between their addresses, and the compiler then keeps every
+// variable the K loop touches in memory.)
+template <typename V>
+__device__ __attribute__((always_inline)) inline V pick(bool c, V x, V y) {
+  return c ? x : y;
 }
 
 }  // namespace
@@ -103,8 +161,10 @@ __global__ __launch_bounds__(64 * kSqWaves, 1) void ffn_sq_kernel(SqArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_b1[kBStage];
   __shared__ __attribute__((aligned(16))) uint8_t s_b2[kBStage];
   __shared__ __attribute__((aligned(16))) uint8_t s_b3[kBStage];
-  __shared__ __attribute__((aligned(16))) uint8_t s_out[kSqWaves * 2048];
+  __shared__ __attribute__((aligned(16))) uint8_t s_out[kSqWaves * 4096];
   __shared__ int32_t s_ru[kMaxExpertsSq + 1];
+  __shared__ int32_t s_t0[kMaxExpertsSq + 1];   // first pool tile of each expert (and the end)
+  __shared__ int32_t s_end[kMaxExpertsSq];      // end of each expert's rows in the pool
   __shared__ int s_sel;
   auto aring = [&](auto ST) __attribute__((always_inline)) -> uint8_t* {
     if constexpr (decltype(ST)::value == 0) return s_a0;
@@ -125,15 +185,19 @@ __global__ __launch_bounds__(64 * kSqWaves, 1) void ffn_sq_kernel(SqArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rg = w >> 2;   // row half of the unit
-  const int cg = w & 3;    // column quarter of the unit
+  const int rg = w >> 1;   // row half of the unit
+  const int cg = w & 1;    // column half of the unit
 
   int ntiles = a.num_tiles[0];
   if (ntiles > a.max_tiles) {
     if (blockIdx.x == 0 && tid == 0) record_error(a.err, MOE_ERR_INVALID);
     ntiles = a.max_tiles;
   }
-  // row units per expert, prefix-summed; whether this launch is the call's GEMM A
+  for (int e = tid; e <= a.n_experts; e += 64 * kSqWaves) {
+    const int o = a.offsets[e];
+    s_t0[e] = min(o >> 7, a.max_tiles);
+    if (e < a.n_experts) s_end[e] = o + a.counts[e];
+  }
   if (w == 0) {
     sq_row_units(a, s_ru, lane);
     if (a.select) {
@@ -148,7 +212,6 @@ __global__ __launch_bounds__(64 * kSqWaves, 1) void ffn_sq_kernel(SqArgs a) {
   int u = unit_slot(blockIdx.x, G);
   if (u >= total) return;
 
-  // one acquire for every tile when dispatch has already marked them all
   bool poll_each = false;
   if (a.wait_ready) {
     const uint32_t done = __hip_atomic_load(a.tiles_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -157,142 +220,164 @@ __global__ __launch_bounds__(64 * kSqWaves, 1) void ffn_sq_kernel(SqArgs a) {
   }
 
   const int KS = a.KS;
-  // this wave's DMA lanes: pool rows 32w .. 32w + 31 of the unit, 8 rows per DMA; lane i fills
-  // LDS bytes 16i .. 16i + 15 of a DMA's 1 KiB, i.e. row i / 8, chunk slot i % 8, which holds
-  // the row's chunk (i % 8) ^ (row % 8)
+  const int KH = KS >> 1;   // pool-row stages per unit
+  // this wave's DMA lanes: pool rows 64w .. 64w + 63 of the unit, 8 rows per DMA; lane i
+  // fills LDS bytes 16i .. 16i + 15 of a DMA's 1 KiB, i.e. row i / 8, chunk slot i % 8,
+  // which holds the row's chunk (i % 8) ^ (row % 8)
   const uint32_t lda = (uint32_t)a.lda;
-  const uint32_t a_vo = (uint32_t)(32 * w + (lane >> 3)) * lda + 16u * (uint32_t)((lane & 7) ^ ((lane >> 3) & 7));
+  const uint32_t a_vo = (uint32_t)(64 * w + (lane >> 3)) * lda + 16u * (uint32_t)((lane & 7) ^ ((lane >> 3) & 7));
   const uint32_t b_vo = 16u * (uint32_t)lane;
-  // fragment read of pool rows: lane l takes row l % 16, chunk 4 kk + l / 16 of the stage
-  const int a_frag0 = (lane & 15) * 128 + ((((lane >> 4)) ^ (lane & 7)) << 4);
-  const int a_frag1 = (lane & 15) * 128 + (((4 + (lane >> 4)) ^ (lane & 7)) << 4);
+  const uint32_t bstr = (uint32_t)a.ktiles * 1024u;
+  // fragment read of pool rows: lane l takes row l % 16, chunk 4 h + l / 16 of the stage
+  // (h: the stage's K half)
+  const int a_frag0 = (lane & 15) * 128 + ((((lane >> 4)) ^ (lane & 7)) << 4) + rg * 128 * 128;
+  const int a_frag1 = (lane & 15) * 128 + (((4 + (lane >> 4)) ^ (lane & 7)) << 4) + rg * 128 * 128;
   typedef __attribute__((address_space(3))) void* lds_t;
-  // one DMA of pool-row stage kd (64 K values): rows 32w + 8q .. +8
-  auto dma_a1 = [&](auto ST, const SqSrc& s, int kd, int q) __attribute__((always_inline)) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(s.ar, (lds_t)(aring(ST) + (4 * w + q) * 1024), 16, a_vo + 8u * q * lda,
-                                             (uint32_t)kd * 128u, 0, 0);
-  };
-  // one DMA of weight stage kb (32 K values): this wave's row block 2w + q
-  auto dma_b1 = [&](auto ST, const SqSrc& s, int kb, int q) __attribute__((always_inline)) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(s.br, (lds_t)(bring(ST) + (2 * w + q) * 1024), 16, b_vo,
-                                             (q ? s.b1 : s.b0) + (uint32_t)kb * 1024u, 0, 0);
-  };
-  auto dma_a = [&](auto ST, const SqSrc& s, int kd) __attribute__((always_inline)) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) dma_a1(ST, s, kd, q);
-  };
-  auto dma_b = [&](auto ST, const SqSrc& s, int kb) __attribute__((always_inline)) {
-    dma_b1(ST, s, kb, 0);
-    dma_b1(ST, s, kb, 1);
-  };
-  // B row blocks of this wave's MFMA column tiles: GEMM A gate 2cg, 2cg + 1, up 8 + 2cg, 8 + 2cg + 1
-  auto bblk = [&](int tn) __attribute__((always_inline)) { return GEMM_A ? (tn < 2 ? 2 * cg + tn : 8 + 2 * cg + (tn - 2)) : 4 * cg + tn; };
+  // B row blocks of this wave's MFMA column tiles: GEMM A gate 4cg .. +3, up 8 + 4cg .. +3
+  auto bblk = [&](int tn) __attribute__((always_inline)) { return GEMM_A ? (tn < 4 ? 4 * cg + tn : 8 + 4 * cg + (tn - 4)) : 8 * cg + tn; };
 
-  SqUnit cur = sq_unit(a, s_ru, u);
+  SqUnit cur = sq_unit(a, s_ru, s_t0, u);
   if (poll_each) sq_wait_tiles(a, cur);
-  SqSrc cs = sq_src<GEMM_A>(a, cur, w);
-  // the first unit's stages in the order the steady state issues them: weights 0, pool rows
-  // 0 and weights 1 (as at step -2), weights 2 (step -1)
-  dma_b(I0{}, cs, 0);
-  dma_a(I0{}, cs, 0);
-  dma_b(I1{}, cs, 1);
-  dma_b(I2{}, cs, 2);
+  SqSrc cs = sq_src<GEMM_A>(a, cur, s_end, w);
+  // the first unit's stages in the order the steady state issues them: weights 0 (step
+  // -4), pool rows 0 and weights 1 (step -3), weights 2 (step -2), pool rows 1 and weights 3
+  // (step -1)
+  {
+    const __amdgpu_buffer_rsrc_t car = make_rsrc(cs.abase, cs.abytes), cbr = make_rsrc(cs.bbase, (uint32_t)a.b_expert);
+    // one pool-row stage (8 DMAs) and one weight stage (4 DMAs) of this wave
+    auto pa = [&](uint8_t* dst, uint32_t koff) __attribute__((always_inline)) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(car, (lds_t)(dst + (8 * w + q) * 1024), 16, a_vo + 8u * q * lda,
+                                                 koff, 0, 0);
+    };
+    auto pb = [&](uint8_t* dst, uint32_t boff) __attribute__((always_inline)) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(cbr, (lds_t)(dst + (4 * w + q) * 1024), 16, b_vo,
+                                                 boff + (uint32_t)q * bstr, 0, 0);
+    };
+    pb(s_b0, cs.b0);
+    pa(s_a0, 0u);
+    pb(s_b1, cs.b0 + 1024u);
+    pb(s_b2, cs.b0 + 2048u);
+    pa(s_a1, 128u);
+    pb(s_b3, cs.b0 + 3072u);
+  }
 
-  f32x4_t acc[8][4];
-  bf16x8_t fbp[4], fap;   // the previous stage's last MFMA group, issued after the next barrier
+  f32x4_t acc[8][8];
+  bf16x8_t fa[2][8], fb[2][8];
 
   for (;;) {
+    // this unit's stage 0 fragments. Its DMAs were issued at steps -4 and -3 of the unit (in
+    // the previous unit's last steps, or above for the first unit), with 20 DMAs behind them
+    // (and the previous unit's output stores, which the count does not rely on). (The last
+    // step of the previous unit read them too; reading them again here keeps no fragment
+    // register live across the epilogue.)
+    __builtin_amdgcn_s_waitcnt(vmcnt_enc(20));
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      fa[0][t] = *reinterpret_cast<const bf16x8_t*>(s_a0 + a_frag0 + t * 16 * 128);
+      fb[0][t] = *reinterpret_cast<const bf16x8_t*>(s_b0 + bblk(t) * 1024 + 16 * lane);
+    }
     const int un = u + G;
     const bool has_next = un < total;
-    const SqUnit nx = has_next ? sq_unit(a, s_ru, un) : cur;
-    const SqSrc ns = sq_src<GEMM_A>(a, nx, w);
+    const SqUnit nx = has_next ? sq_unit(a, s_ru, s_t0, un) : cur;
+    const SqSrc ns = sq_src<GEMM_A>(a, nx, s_end, w);
     const bool store = rg == 0 || cur.two;   // a one-tile unit's second row half is not stored
-#pragma unroll
-    for (int tm = 0; tm < 8; ++tm)
-#pragma unroll
-      for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int tn = 0; tn < 4; ++tn) fbp[tn] = bf16x8_t{};
-    fap = bf16x8_t{};   // zero operands: the first step's deferred group adds exactly 0
 
-    // step ks (32 K values), ks % 4 = ST: weights from stage ST, pool rows from stage ST / 2,
-    // K half ST % 2 of it
+    // step ks (32 K values), ks % 4 = ST: MFMAs on the fragments of register set ST % 2;
+    // reads of step ks + 1 into the other set
     auto step = [&](auto ST, int ks) __attribute__((always_inline)) {
       constexpr int st = decltype(ST)::value;
-      using AS = std::integral_constant<int, st / 2>;          // pool-row stage read
-      using AN = std::integral_constant<int, (st / 2) ^ 1>;    // pool-row stage loaded (even steps)
-      using BN = std::integral_constant<int, (st + 3) & 3>;    // weight stage loaded
-      constexpr bool EVEN = (st & 1) == 0;
+      constexpr int P = st & 1, PN = P ^ 1;
+      constexpr bool ODD = P == 1;
+      using AR = std::integral_constant<int, ((st + 1) >> 1) & 1>;   // pool-row stage read (for step ks + 1)
+      using BR = std::integral_constant<int, (st + 1) & 3>;          // weight stage read
+      using AD = std::integral_constant<int, st == 1 ? 0 : 1>;       // pool-row stage loaded (odd steps)
+      constexpr bool H1 = ((st + 1) & 1) != 0;                       // K half of the pool-row stage read
       __builtin_amdgcn_sched_barrier(0);
-      // this wave's DMAs that step ks reads are in (even steps: pool rows ks / 2 and weights
-      // ks, with weights ks + 1, ks + 2 in flight behind them; odd steps: weights ks, with
-      // weights ks + 1, pool rows ks / 2 + 1 and weights ks + 2 behind them); its reads of
-      // step ks - 1 are done
-      __builtin_amdgcn_s_waitcnt(vmcnt_enc(EVEN ? 4 : 8));
+      // the sources of this step's DMAs (scalar work, issued while the previous step's last
+      // MFMAs run): weight stage ks + 4 and, on odd steps, pool-row stage (ks + 3) / 2, this
+      // unit's, the next unit's first ones, or a reload nobody reads when there is no next unit
+      const int kb = ks + 4;
+      const bool b_nx = kb >= KS;
+      const bool bn = b_nx && has_next;
+      const __amdgpu_buffer_rsrc_t d_br = make_rsrc(pick(bn, ns.bbase, cs.bbase), (uint32_t)a.b_expert);
+      const uint32_t d_b = pick(bn, ns.b0, cs.b0) + (uint32_t)(b_nx ? (has_next ? kb - KS : KS - 1) : kb) * 1024u;
+      __amdgpu_buffer_rsrc_t d_ar;
+      uint32_t d_a = 0;
+      if constexpr (ODD) {
+        const int kd = (ks + 3) >> 1;
+        const bool a_nx = kd >= KH;
+        if constexpr (st == 1) {
+          if (kd == KH && has_next && poll_each) sq_wait_tiles(a, nx);
+        }
+        const bool an = a_nx && has_next;
+        d_ar = make_rsrc(pick(an, ns.abase, cs.abase), pick(an, ns.abytes, cs.abytes));
+        d_a = (uint32_t)(a_nx ? (has_next ? kd - KH : KH - 1) : kd) * 128u;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // the step's first kPre MFMAs need nothing the barrier guards: they keep the matrix core
+      // busy while the wave waits at it
+#pragma unroll
+      for (int i = 0; i < kPre; ++i) mfma_acc(acc[i >> 3][i & 7], fb[P][i & 7], fa[P][i >> 3]);
+      __builtin_amdgcn_sched_barrier(0);
+      // this wave's DMAs of the stages read during this step are in (even steps: weights
+      // ks + 1 and pool rows ks / 2, issued at step ks - 3, with 16 DMAs behind them; odd
+      // steps: pool rows (ks + 1) / 2, issued first at step ks - 2, with 8 behind them); its
+      // fragment reads of the previous step are done. (In a unit's first steps the previous
+      // unit's output stores lie behind them too and count against the same budget: the
+      // counter can retire stores before older loads, so only loads may be counted on.)
+      __builtin_amdgcn_s_waitcnt(vmcnt_enc(ODD ? 8 : 16));
       __builtin_amdgcn_s_waitcnt(kLgkm0);
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      // even steps: pool-row stage ks / 2 + 1 (this unit's, the next unit's first, or a reload
-      // nobody reads when there is no next unit); every step: weight stage ks + 3, likewise.
-      // The DMAs go out one per MFMA group, pool rows first (the wait counts above rely on
-      // that order), so that issuing them never holds the wave off its MFMAs for long.
-      const int kd0 = (ks >> 1) + 1;
-      const bool a_next = kd0 >= (KS >> 1);
-      if constexpr (EVEN) {
-        if (a_next && has_next && poll_each) sq_wait_tiles(a, nx);
-      }
-      const bool an = a_next && has_next;
-      __amdgpu_buffer_rsrc_t d_ar = cs.ar;
-      if (an) d_ar = ns.ar;
-      const uint32_t d_ak = (uint32_t)(a_next ? (has_next ? 0 : (KS >> 1) - 1) : kd0) * 128u;
-      const int kb0 = ks + 3;
-      const bool b_next = kb0 >= KS;
-      const bool bn = b_next && has_next;
-      __amdgpu_buffer_rsrc_t d_br = cs.br;
-      if (bn) d_br = ns.br;
-      const uint32_t d_bk = (uint32_t)(b_next ? (has_next ? kb0 - KS : KS - 1) : kb0) * 1024u;
-      const uint32_t d_b0 = (bn ? ns.b0 : cs.b0) + d_bk, d_b1 = (bn ? ns.b1 : cs.b1) + d_bk;
-      // the DMA of group g (0 .. 5 on even steps, 0 .. 1 on odd ones)
-      auto dma_g = [&](int g) __attribute__((always_inline)) {
-        if (EVEN && g < 4) {
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(d_ar, (lds_t)(aring(AN{}) + (4 * w + g) * 1024), 16,
-                                                   a_vo + 8u * (uint32_t)g * lda, d_ak, 0, 0);
-        } else {
-          const int q = EVEN ? g - 4 : g;
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(d_br, (lds_t)(bring(BN{}) + (2 * w + q) * 1024), 16, b_vo,
-                                                   q ? d_b1 : d_b0, 0, 0);
-        }
+      const uint8_t* ra = aring(AR{}) + (H1 ? a_frag1 : a_frag0);
+      const uint8_t* rb = bring(BR{}) + 16 * lane;
+      // the step's memory operations, spread over the MFMAs from the barrier on (a wave waits
+      // while a memory instruction issues, and the MFMA just issued keeps the matrix core busy
+      // meanwhile): the 16 fragment reads of step ks + 1 into the other register set, and the
+      // DMAs, weight stage ks + 4 into the stage of ks (read during step ks - 1) and, on odd
+      // steps, pool-row stage (ks + 3) / 2 before it (the wait counts above rely on that order)
+      auto read_a = [&](int t) __attribute__((always_inline)) {
+        fa[PN][t] = *reinterpret_cast<const bf16x8_t*>(ra + t * 16 * 128);
       };
-      constexpr int NDMA = EVEN ? 6 : 2;
-      __builtin_amdgcn_sched_barrier(0);
-      {
-        const uint8_t* sa = aring(AS{}) + (rg * 128) * 128 + (EVEN ? a_frag0 : a_frag1);
-        const uint8_t* sb = bring(ST) + 16 * lane;
-        bf16x8_t fb[4];
-#pragma unroll
-        for (int tn = 0; tn < 4; ++tn) fb[tn] = *reinterpret_cast<const bf16x8_t*>(sb + bblk(tn) * 1024);
-        bf16x8_t fa = *reinterpret_cast<const bf16x8_t*>(sa);
-        // the previous step's last group
-#pragma unroll
-        for (int tn = 0; tn < 4; ++tn)
-          acc[7][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fbp[tn], fap, acc[7][tn], 0, 0, 0);
+      auto read_b = [&](int t) __attribute__((always_inline)) {
+        fb[PN][t] = *reinterpret_cast<const bf16x8_t*>(rb + bblk(t) * 1024);
+      };
+      auto dma_a = [&](int q) __attribute__((always_inline)) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d_ar, (lds_t)(aring(AD{}) + (8 * w + q) * 1024), 16,
+                                                 a_vo + 8u * (uint32_t)q * lda, d_a, 0, 0);
+      };
+      auto dma_b = [&](int q) __attribute__((always_inline)) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d_br, (lds_t)(bring(ST) + (4 * w + q) * 1024), 16, b_vo,
+                                                 d_b + (uint32_t)q * bstr, 0, 0);
+      };
+      // MFMA i of the step (group i / 8, column tile i % 8), then its memory operation
+      auto one = [&](auto II) __attribute__((always_inline)) {
+        constexpr int i = decltype(II)::value;
+        constexpr int g = i >> 3, tn = i & 7;
+        mfma_acc(acc[g][tn], fb[P][tn], fa[P][g]);
+        constexpr int c = sq_op(ODD, i);
+        if constexpr (c >> 4 == 1) read_a(c & 15);
+        else if constexpr (c >> 4 == 2) read_b(c & 15);
+        else if constexpr (c >> 4 == 3) dma_a(c & 15);
+        else if constexpr (c >> 4 == 4) dma_b(c & 15);
         __builtin_amdgcn_sched_barrier(0);
-#pragma clang loop unroll(full)
-        for (int tm = 0; tm < 7; ++tm) {
-          if (tm < NDMA) dma_g(tm);
-          const bf16x8_t fn = *reinterpret_cast<const bf16x8_t*>(sa + ((tm + 1) * 16) * 128);
-#pragma unroll
-          for (int tn = 0; tn < 4; ++tn)
-            acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[tn], fa, acc[tm][tn], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-          fa = fn;
-        }
-        fap = fa;
-#pragma unroll
-        for (int tn = 0; tn < 4; ++tn) fbp[tn] = fb[tn];
-      }
+      };
+      [&]<int... Is>(std::integer_sequence<int, Is...>) __attribute__((always_inline)) {
+        (one(std::integral_constant<int, Is + kPre>{}), ...);
+      }(std::make_integer_sequence<int, 64 - kPre>{});
     };
 
+#pragma unroll
+    for (int tm = 0; tm < 8; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < 8; ++tn) acc[tm][tn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    asm volatile("s_nop 4");   // the zeros are in before an MFMA reads them
+    __builtin_amdgcn_sched_barrier(0);
     for (int ks = 0; ks < KS; ks += 4) {
       step(I0{}, ks);
       step(I1{}, ks + 1);
@@ -300,69 +385,82 @@ __global__ __launch_bounds__(64 * kSqWaves, 1) void ffn_sq_kernel(SqArgs a) {
       step(I3{}, ks + 3);
     }
 
-#pragma unroll
-    for (int tn = 0; tn < 4; ++tn)
-      acc[7][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fbp[tn], fap, acc[7][tn], 0, 0, 0);
-    if (store) {
-      // ---- epilogue: lane holds row tm*16 + (lane & 15), columns 4 (lane >> 4) + (0..3) of each tile
-      uint8_t* so = s_out + w * 2048;
+    {
+      // ---- epilogue: lane holds row tm*16 + (lane & 15), columns 4 (lane >> 4) + (0..3) of
+      // each tile; the wave's 4 KiB of s_out stage 16 rows at a time. A wave whose rows are
+      // not stored (the second half of a one-tile unit) stores into an empty range, which
+      // drops them.
+      // the lane index as a value computed here, so that the compiler derives the epilogue's
+      // addresses from it inside the unit loop rather than keeping them live across the K loop
+      int el;
+      asm volatile("" : "=v"(el) : "0"(lane));
+      // the last MFMAs' results are in before the first read of an accumulator
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+      __builtin_amdgcn_sched_barrier(0);
+      uint8_t* so = s_out + w * 4096;
       const int64_t row0 = (int64_t)cur.m * 128 + rg * 128;
-      const int r = lane & 15;
-      if constexpr (GEMM_A) {
+      const int r = el & 15;
+      const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.out + row0 * a.ldo, store ? (uint32_t)(128 * a.ldo) : 0u);
+      const uint32_t ldo = (uint32_t)a.ldo;
+      // 256-byte staging rows, 16-byte chunks permuted by row
+      auto st256 = [&](int row, int b) __attribute__((always_inline)) {
+        return row * 256 + ((((b >> 4) ^ row) & 15) << 4) + (b & 15);
+      };
 #pragma unroll
-        for (int tm = 0; tm < 8; ++tm) {
+      for (int tm = 0; tm < 8; ++tm) {
+        // one MFMA row at a time: its accumulators are read only here
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4_t cv[8];
+#pragma unroll
+        for (int tn = 0; tn < 8; ++tn) cv[tn] = acc_read(acc[tm][tn]);
+        if constexpr (GEMM_A) {
           if constexpr (GSAVE) {
-            // G = [gate | up] before the activation: the wave's 32 gate and 32 up columns
-            // as one 128-byte staging row, then 64-byte segments of the gate and up halves
+            // G = [gate | up] before the activation: 64 gate and 64 up columns as one
+            // 256-byte staging row, stored as 128-byte segments of the gate and up halves
 #pragma unroll
-            for (int tn = 0; tn < 4; ++tn) {
+            for (int tn = 0; tn < 8; ++tn) {
               u32x2 v;
-              v.x = pack_bf16x2(acc[tm][tn][0], acc[tm][tn][1]);
-              v.y = pack_bf16x2(acc[tm][tn][2], acc[tm][tn][3]);
-              const int b = tn * 32 + 8 * (lane >> 4);
-              *reinterpret_cast<u32x2*>(so + r * 128 + ((((b >> 4) ^ (r & 7))) << 4) + (b & 15)) = v;
+              v.x = pack_bf16x2(cv[tn][0], cv[tn][1]);
+              v.y = pack_bf16x2(cv[tn][2], cv[tn][3]);
+              *reinterpret_cast<u32x2*>(so + st256(r, tn * 32 + 8 * (el >> 4))) = v;
             }
+            const __amdgpu_buffer_rsrc_t rg_ = make_rsrc(a.g_save + row0 * a.g_ld, store ? (uint32_t)(128 * a.g_ld) : 0u);
 #pragma unroll
-            for (int p = 0; p < 2; ++p) {
-              const int rr = p * 8 + (lane >> 3), c = lane & 7;
-              const u32x4 v = *reinterpret_cast<const u32x4*>(so + rr * 128 + ((c ^ (rr & 7)) << 4));
-              const int64_t col = (c < 4 ? 0 : a.g_up) + (int64_t)(cur.j * 128 + cg * 32) * 2 + (c & 3) * 16;
-              *reinterpret_cast<u32x4*>(a.g_save + (row0 + tm * 16 + rr) * a.g_ld + col) = v;
+            for (int p = 0; p < 4; ++p) {
+              const int rr = p * 4 + (el >> 4), c = el & 15;
+              const u32x4 v = *reinterpret_cast<const u32x4*>(so + st256(rr, c * 16));
+              const uint32_t col = (uint32_t)((c < 8 ? 0 : a.g_up) + (cur.j * 128 + cg * 64) * 2 + (c & 7) * 16);
+              buf_store16(v, rg_, (uint32_t)(tm * 16 + rr) * (uint32_t)a.g_ld + col);
             }
           }
-          // h = silu(gate) * up: 16 rows x 32 columns, staged as 64-byte rows
-#pragma unroll
-          for (int tn = 0; tn < 2; ++tn) {
-            u32x2 v;
-            v.x = pack_bf16x2(sq_silu_mul(acc[tm][tn][0], acc[tm][tn + 2][0]),
-                              sq_silu_mul(acc[tm][tn][1], acc[tm][tn + 2][1]));
-            v.y = pack_bf16x2(sq_silu_mul(acc[tm][tn][2], acc[tm][tn + 2][2]),
-                              sq_silu_mul(acc[tm][tn][3], acc[tm][tn + 2][3]));
-            const int b = tn * 32 + 8 * (lane >> 4);
-            *reinterpret_cast<u32x2*>(so + r * 64 + ((((b >> 4) ^ ((r >> 2) & 3))) << 4) + (b & 15)) = v;
-          }
-          {
-            const int rr = lane >> 2, c = lane & 3;
-            const u32x4 v = *reinterpret_cast<const u32x4*>(so + rr * 64 + ((c ^ ((rr >> 2) & 3)) << 4));
-            *reinterpret_cast<u32x4*>(a.out + (row0 + tm * 16 + rr) * a.ldo + (cur.j * 128 + cg * 32) * 2 + c * 16) = v;
-          }
-        }
-      } else {
-#pragma unroll
-        for (int tm = 0; tm < 8; ++tm) {
+          // h = silu(gate) * up: 16 rows x 64 columns, staged as 128-byte rows
 #pragma unroll
           for (int tn = 0; tn < 4; ++tn) {
             u32x2 v;
-            v.x = pack_bf16x2(acc[tm][tn][0], acc[tm][tn][1]);
-            v.y = pack_bf16x2(acc[tm][tn][2], acc[tm][tn][3]);
-            const int b = tn * 32 + 8 * (lane >> 4);
-            *reinterpret_cast<u32x2*>(so + r * 128 + ((((b >> 4) ^ (r & 7))) << 4) + (b & 15)) = v;
+            v.x = pack_bf16x2(sq_silu_mul(cv[tn][0], cv[tn + 4][0]), sq_silu_mul(cv[tn][1], cv[tn + 4][1]));
+            v.y = pack_bf16x2(sq_silu_mul(cv[tn][2], cv[tn + 4][2]), sq_silu_mul(cv[tn][3], cv[tn + 4][3]));
+            const int b = tn * 32 + 8 * (el >> 4);
+            *reinterpret_cast<u32x2*>(so + 2048 + r * 128 + ((((b >> 4) ^ (r & 7))) << 4) + (b & 15)) = v;
           }
 #pragma unroll
           for (int p = 0; p < 2; ++p) {
-            const int rr = p * 8 + (lane >> 3), c = lane & 7;
-            const u32x4 v = *reinterpret_cast<const u32x4*>(so + rr * 128 + ((c ^ (rr & 7)) << 4));
-            *reinterpret_cast<u32x4*>(a.out + (row0 + tm * 16 + rr) * a.ldo + (cur.j * 256 + cg * 64) * 2 + c * 16) = v;
+            const int rr = p * 8 + (el >> 3), c = el & 7;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(so + 2048 + rr * 128 + ((c ^ (rr & 7)) << 4));
+            buf_store16(v, ro, (uint32_t)(tm * 16 + rr) * ldo + (uint32_t)((cur.j * 128 + cg * 64) * 2 + c * 16));
+          }
+        } else {
+#pragma unroll
+          for (int tn = 0; tn < 8; ++tn) {
+            u32x2 v;
+            v.x = pack_bf16x2(cv[tn][0], cv[tn][1]);
+            v.y = pack_bf16x2(cv[tn][2], cv[tn][3]);
+            *reinterpret_cast<u32x2*>(so + st256(r, tn * 32 + 8 * (el >> 4))) = v;
+          }
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const int rr = p * 4 + (el >> 4), c = el & 15;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(so + st256(rr, c * 16));
+            buf_store16(v, ro, (uint32_t)(tm * 16 + rr) * ldo + (uint32_t)((cur.j * 256 + cg * 128) * 2 + c * 16));
           }
         }
       }
