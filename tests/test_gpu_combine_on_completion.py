@@ -2,8 +2,9 @@
 combine kernel: the same bits in out and y_pool, on the big-tile GEMM Y kernel (bf16,
 fp8, mxfp4; where each GEMM Y unit publishes its tile and the kernel's workgroups
 combine the tokens once their tiles are done) and on a shape where GEMM Y takes the
-general kernel (the combine kernel then follows the FFN). The separate path is held
-to the oracle by test_gpu_layer.py."""
+general kernel (the combine kernel then follows the FFN). Each case is also held to the
+oracle: small shapes on every output element, the full-size skew workload on one token per
+pool tile."""
 import numpy as np
 import pytest
 import torch
@@ -12,7 +13,7 @@ import combine_moe_dispatch_02_amd as moe
 import oracle
 from synth import MoEConfig, config_by_name, make_inputs
 
-from _gpu import TOL, dev_inputs, make_layer, out_rows_f64, rel_err, run_layer, say
+from _gpu import TOL, dev_inputs, make_layer, out_rows_f64, rel_err, run_layer, say, tile_covering_tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -52,8 +53,10 @@ def test_fused_combine_matches_separate(cfg):
 def test_fused_combine_two_streams():
     cfg = CASES[1]
     say("combine on completion, two streams", cfg.name)
-    _, _, _, a, _, b = _pair(cfg, streams=True)
+    inp, _, _, a, _, b = _pair(cfg, streams=True)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    ref = oracle.moe_layer(inp)
+    assert rel_err(out_rows_f64(b), ref.out) <= TOL[cfg.dtype]
 
 
 def test_fused_combine_repeated_calls():
@@ -75,3 +78,11 @@ def test_fused_combine_full_size_skew():
     say("combine on completion, full size", cfg.name)
     inp, sep, fused, a, ya, b = _pair(cfg)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    # against the oracle on the token of every pool tile's last real row (every GEMM Y unit,
+    # hence every tile the fused tail waits on, has a compared pair)
+    p = oracle.plan(inp.topk_idx, cfg.expert_begin, cfg.num_local_experts, cfg.tile)
+    toks = tile_covering_tokens(cfg, inp, p)
+    ref = oracle.moe_layer(inp, tokens=toks, p=p)
+    err = rel_err(out_rows_f64(b, toks), ref.out)
+    print(f"fused combine, {len(toks)} tokens covering all {p.num_tiles} tiles: max-norm rel err {err:.3e}")
+    assert err <= TOL[cfg.dtype]
