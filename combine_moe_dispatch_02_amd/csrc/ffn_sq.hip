@@ -99,12 +99,18 @@ __device__ __attribute__((always_inline)) inline SqSrc sq_src(const SqArgs& a, c
 // c += a x b on the matrix core, with c kept in the accumulation registers and updated in
 // place. (Left to the compiler, the 256 accumulators of a wave do not stay put: it moves some
 // of them through the vector registers between steps.) The compiler does not see this as an
-// MFMA, so the wait states around it are the caller's: the accumulators are set to zero a
-// few instructions before the first MFMA reads them (s_nop 4 after the writes), and read
-// back only after 24 wait states (three s_nop 7) behind the last MFMA. The 64 MFMAs of a
-// step update 64 different accumulators, so no MFMA reads one that the one before wrote.
+// MFMA, so the wait states around it are the caller's: the accumulators are read back only
+// after 24 wait states (three s_nop 7) behind the last MFMA. The 64 MFMAs of a step update 64
+// different accumulators, so no MFMA reads one that the one before wrote. A unit's first
+// step uses mfma_first, which reads no accumulator.
 __device__ __attribute__((always_inline)) inline void mfma_acc(f32x4_t& c, bf16x8_t a, bf16x8_t b) {
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+
+// c = a x b (the accumulator input is the constant 0): a unit's first K step, so that the
+// accumulators need no zeroing writes between units. Same wait-state rules as mfma_acc.
+__device__ __attribute__((always_inline)) inline void mfma_first(f32x4_t& c, bf16x8_t a, bf16x8_t b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(c) : "v"(a), "v"(b));
 }
 
 // the four accumulators of c into vector registers, where the caller asks for them (left to
@@ -289,8 +295,13 @@ __global__ __launch_bounds__(64 * kSqWaves, 1) void ffn_sq_kernel(SqArgs a) {
 
     // step ks (32 K values), ks % 4 = ST: MFMAs on the fragments of register set ST % 2;
     // reads of step ks + 1 into the other set
-    auto step = [&](auto ST, int ks) __attribute__((always_inline)) {
+    auto step = [&](auto ST, auto Z, int ks) __attribute__((always_inline)) {
       constexpr int st = decltype(ST)::value;
+      constexpr bool FIRST = decltype(Z)::value;   // the unit's first K step: c = a x b
+      auto mfma = [&](f32x4_t& c, bf16x8_t x, bf16x8_t y) __attribute__((always_inline)) {
+        if constexpr (FIRST) mfma_first(c, x, y);
+        else mfma_acc(c, x, y);
+      };
       constexpr int P = st & 1, PN = P ^ 1;
       constexpr bool ODD = P == 1;
       using AR = std::integral_constant<int, ((st + 1) >> 1) & 1>;   // pool-row stage read (for step ks + 1)
@@ -322,7 +333,7 @@ __global__ __launch_bounds__(64 * kSqWaves, 1) void ffn_sq_kernel(SqArgs a) {
       // the step's first kPre MFMAs need nothing the barrier guards: they keep the matrix core
       // busy while the wave waits at it
 #pragma unroll
-      for (int i = 0; i < kPre; ++i) mfma_acc(acc[i >> 3][i & 7], fb[P][i & 7], fa[P][i >> 3]);
+      for (int i = 0; i < kPre; ++i) mfma(acc[i >> 3][i & 7], fb[P][i & 7], fa[P][i >> 3]);
       __builtin_amdgcn_sched_barrier(0);
       // this wave's DMAs of the stages read during this step are in (even steps: weights
       // ks + 1 and pool rows ks / 2, issued at step ks - 3, with 16 DMAs behind them; odd
@@ -359,7 +370,7 @@ __global__ __launch_bounds__(64 * kSqWaves, 1) void ffn_sq_kernel(SqArgs a) {
       auto one = [&](auto II) __attribute__((always_inline)) {
         constexpr int i = decltype(II)::value;
         constexpr int g = i >> 3, tn = i & 7;
-        mfma_acc(acc[g][tn], fb[P][tn], fa[P][g]);
+        mfma(acc[g][tn], fb[P][tn], fa[P][g]);
         constexpr int c = sq_op(ODD, i);
         if constexpr (c >> 4 == 1) read_a(c & 15);
         else if constexpr (c >> 4 == 2) read_b(c & 15);
@@ -372,17 +383,18 @@ __global__ __launch_bounds__(64 * kSqWaves, 1) void ffn_sq_kernel(SqArgs a) {
       }(std::make_integer_sequence<int, 64 - kPre>{});
     };
 
-#pragma unroll
-    for (int tm = 0; tm < 8; ++tm)
-#pragma unroll
-      for (int tn = 0; tn < 8; ++tn) acc[tm][tn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    asm volatile("s_nop 4");   // the zeros are in before an MFMA reads them
-    __builtin_amdgcn_sched_barrier(0);
-    for (int ks = 0; ks < KS; ks += 4) {
-      step(I0{}, ks);
-      step(I1{}, ks + 1);
-      step(I2{}, ks + 2);
-      step(I3{}, ks + 3);
+    // K steps in rounds of four (KS is a multiple of four, at least four); the first step's
+    // MFMAs start the accumulators from the constant 0
+    using F = std::false_type;
+    step(I0{}, std::true_type{}, 0);
+    step(I1{}, F{}, 1);
+    step(I2{}, F{}, 2);
+    step(I3{}, F{}, 3);
+    for (int ks = 4; ks < KS; ks += 4) {
+      step(I0{}, F{}, ks);
+      step(I1{}, F{}, ks + 1);
+      step(I2{}, F{}, ks + 2);
+      step(I3{}, F{}, ks + 3);
     }
 
     {
