@@ -17,14 +17,14 @@ struct SqUnit {
   int j;     // N block of 256 columns
 };
 
-// Unit u -> coordinates. s_ru[e] = row units (tile pairs, rounded up) of the experts
+// Unit u -> coordinates (sq_unit_lane: u may differ between lanes). s_ru[e] = row units (tile pairs, rounded up) of the experts
 // before e. Within expert e, units go in groups of `group` row units; inside a group,
 // N block by N block, the group's row units back to back: units that run together
 // share weight panels and pool rows.
 // Each expert's first pool tile comes from a table (t0s[e] = min(offsets[e] / 128,
 // max_tiles) for e <= E, in LDS), so that decoding a unit reads no global memory.
-__device__ __attribute__((always_inline)) inline SqUnit sq_unit(const SqArgs& a, const int32_t* s_ru,
-                                                                    const int32_t* t0s, int u) {
+__device__ __attribute__((always_inline)) inline SqUnit sq_unit_lane(const SqArgs& a, const int32_t* s_ru,
+                                                                         const int32_t* t0s, int u) {
   int lo = 0, hi = a.n_experts - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -42,6 +42,13 @@ __device__ __attribute__((always_inline)) inline SqUnit sq_unit(const SqArgs& a,
   const int ru = g * a.group + (l2 - r.j * gsz);
   r.m = t0s[lo] + 2 * ru;
   r.two = r.m + 1 < t0s[lo + 1];
+  return r;
+}
+
+// The same, for a unit index that is the same in every lane (the result in scalar registers).
+__device__ __attribute__((always_inline)) inline SqUnit sq_unit(const SqArgs& a, const int32_t* s_ru,
+                                                                    const int32_t* t0s, int u) {
+  SqUnit r = sq_unit_lane(a, s_ru, t0s, u);
   r.e = __builtin_amdgcn_readfirstlane(r.e);
   r.m = __builtin_amdgcn_readfirstlane(r.m);
   r.two = __builtin_amdgcn_readfirstlane(r.two);

@@ -69,6 +69,7 @@ constexpr int kSqWaves = 4;
 constexpr int kPre = 2;            // MFMAs of a step issued before its barrier
 constexpr int kAStage = 32768;   // 256 pool rows x 128 bytes (64 K values)
 constexpr int kBStage = 16384;   // 16 weight row blocks x 1 KiB (32 K values)
+constexpr int kUnitSlots = 64;   // units of a workgroup decoded up front (later ones one by one)
 
 __device__ inline float sq_silu_mul(float g, float u) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u; }
 
@@ -172,6 +173,7 @@ __global__ __launch_bounds__(64 * kSqWaves, 1) void ffn_sq_kernel(SqArgs a) {
   __shared__ int32_t s_t0[kMaxExpertsSq + 1];   // first pool tile of each expert (and the end)
   __shared__ int32_t s_end[kMaxExpertsSq];      // end of each expert's rows in the pool
   __shared__ int s_sel;
+  __shared__ int4 s_units[kUnitSlots];        // this workgroup's first units, decoded
   auto aring = [&](auto ST) __attribute__((always_inline)) -> uint8_t* {
     if constexpr (decltype(ST)::value == 0) return s_a0;
     else return s_a1;
@@ -217,6 +219,18 @@ __global__ __launch_bounds__(64 * kSqWaves, 1) void ffn_sq_kernel(SqArgs a) {
   const int G = gridDim.x;
   int u = unit_slot(blockIdx.x, G);
   if (u >= total) return;
+  // the workgroup's units u, u + G, ... decoded once, one per lane of wave 0 (each a search
+  // over the experts' row-unit prefix), so that moving to the next unit reads one table
+  // entry instead of searching between two units while the matrix core idles
+  if (w == 0) {
+    const int uu = u + lane * G;
+    if (lane < kUnitSlots && uu < total) {
+      const SqUnit U = sq_unit_lane(a, s_ru, s_t0, uu);
+      s_units[lane] = int4{U.e, U.m, U.two, U.j};
+    }
+  }
+  __syncthreads();
+  int it = 0;   // index of the current unit among the workgroup's
 
   bool poll_each = false;
   if (a.wait_ready) {
@@ -289,7 +303,18 @@ __global__ __launch_bounds__(64 * kSqWaves, 1) void ffn_sq_kernel(SqArgs a) {
     }
     const int un = u + G;
     const bool has_next = un < total;
-    const SqUnit nx = has_next ? sq_unit(a, s_ru, s_t0, un) : cur;
+    SqUnit nx = cur;
+    if (has_next) {
+      if (it + 1 < kUnitSlots) {
+        const int4 t = s_units[it + 1];
+        nx.e = __builtin_amdgcn_readfirstlane(t.x);
+        nx.m = __builtin_amdgcn_readfirstlane(t.y);
+        nx.two = __builtin_amdgcn_readfirstlane(t.z);
+        nx.j = __builtin_amdgcn_readfirstlane(t.w);
+      } else {
+        nx = sq_unit(a, s_ru, s_t0, un);
+      }
+    }
     const SqSrc ns = sq_src<GEMM_A>(a, nx, s_end, w);
     const bool store = rg == 0 || cur.two;   // a one-tile unit's second row half is not stored
 
@@ -479,6 +504,7 @@ __global__ __launch_bounds__(64 * kSqWaves, 1) void ffn_sq_kernel(SqArgs a) {
     }
     if (!has_next) break;
     u = un;
+    ++it;
     cur = nx;
     cs = ns;
   }
