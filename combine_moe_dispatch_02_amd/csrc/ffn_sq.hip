@@ -443,17 +443,50 @@ __global__ __launch_bounds__(64 * kSqWaves, 1) void ffn_sq_kernel(SqArgs a) {
       auto st256 = [&](int row, int b) __attribute__((always_inline)) {
         return row * 256 + ((((b >> 4) ^ row) & 15) << 4) + (b & 15);
       };
+      if constexpr (GSAVE) {
 #pragma unroll
-      for (int tm = 0; tm < 8; ++tm) {
-        // one MFMA row at a time: its accumulators are read only here
-        __builtin_amdgcn_sched_barrier(0);
-        f32x4_t cv[8];
+        for (int tm = 0; tm < 8; ++tm) {
+          // one MFMA row at a time: its accumulators are read only here
+          __builtin_amdgcn_sched_barrier(0);
+          f32x4_t cv[8];
 #pragma unroll
-        for (int tn = 0; tn < 8; ++tn) cv[tn] = acc_read(acc[tm][tn]);
-        if constexpr (GEMM_A) {
-          if constexpr (GSAVE) {
-            // G = [gate | up] before the activation: 64 gate and 64 up columns as one
-            // 256-byte staging row, stored as 128-byte segments of the gate and up halves
+          for (int tn = 0; tn < 8; ++tn) cv[tn] = acc_read(acc[tm][tn]);
+          if constexpr (GEMM_A) {
+            if constexpr (GSAVE) {
+              // G = [gate | up] before the activation: 64 gate and 64 up columns as one
+              // 256-byte staging row, stored as 128-byte segments of the gate and up halves
+#pragma unroll
+              for (int tn = 0; tn < 8; ++tn) {
+                u32x2 v;
+                v.x = pack_bf16x2(cv[tn][0], cv[tn][1]);
+                v.y = pack_bf16x2(cv[tn][2], cv[tn][3]);
+                *reinterpret_cast<u32x2*>(so + st256(r, tn * 32 + 8 * (el >> 4))) = v;
+              }
+              const __amdgpu_buffer_rsrc_t rg_ = make_rsrc(a.g_save + row0 * a.g_ld, store ? (uint32_t)(128 * a.g_ld) : 0u);
+#pragma unroll
+              for (int p = 0; p < 4; ++p) {
+                const int rr = p * 4 + (el >> 4), c = el & 15;
+                const u32x4 v = *reinterpret_cast<const u32x4*>(so + st256(rr, c * 16));
+                const uint32_t col = (uint32_t)((c < 8 ? 0 : a.g_up) + (cur.j * 128 + cg * 64) * 2 + (c & 7) * 16);
+                buf_store16(v, rg_, (uint32_t)(tm * 16 + rr) * (uint32_t)a.g_ld + col);
+              }
+            }
+            // h = silu(gate) * up: 16 rows x 64 columns, staged as 128-byte rows
+#pragma unroll
+            for (int tn = 0; tn < 4; ++tn) {
+              u32x2 v;
+              v.x = pack_bf16x2(sq_silu_mul(cv[tn][0], cv[tn + 4][0]), sq_silu_mul(cv[tn][1], cv[tn + 4][1]));
+              v.y = pack_bf16x2(sq_silu_mul(cv[tn][2], cv[tn + 4][2]), sq_silu_mul(cv[tn][3], cv[tn + 4][3]));
+              const int b = tn * 32 + 8 * (el >> 4);
+              *reinterpret_cast<u32x2*>(so + 2048 + r * 128 + ((((b >> 4) ^ (r & 7))) << 4) + (b & 15)) = v;
+            }
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+              const int rr = p * 8 + (el >> 3), c = el & 7;
+              const u32x4 v = *reinterpret_cast<const u32x4*>(so + 2048 + rr * 128 + ((c ^ (rr & 7)) << 4));
+              buf_store16(v, ro, (uint32_t)(tm * 16 + rr) * ldo + (uint32_t)((cur.j * 128 + cg * 64) * 2 + c * 16));
+            }
+          } else {
 #pragma unroll
             for (int tn = 0; tn < 8; ++tn) {
               u32x2 v;
@@ -461,45 +494,87 @@ __global__ __launch_bounds__(64 * kSqWaves, 1) void ffn_sq_kernel(SqArgs a) {
               v.y = pack_bf16x2(cv[tn][2], cv[tn][3]);
               *reinterpret_cast<u32x2*>(so + st256(r, tn * 32 + 8 * (el >> 4))) = v;
             }
-            const __amdgpu_buffer_rsrc_t rg_ = make_rsrc(a.g_save + row0 * a.g_ld, store ? (uint32_t)(128 * a.g_ld) : 0u);
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
               const int rr = p * 4 + (el >> 4), c = el & 15;
               const u32x4 v = *reinterpret_cast<const u32x4*>(so + st256(rr, c * 16));
-              const uint32_t col = (uint32_t)((c < 8 ? 0 : a.g_up) + (cur.j * 128 + cg * 64) * 2 + (c & 7) * 16);
-              buf_store16(v, rg_, (uint32_t)(tm * 16 + rr) * (uint32_t)a.g_ld + col);
+              buf_store16(v, ro, (uint32_t)(tm * 16 + rr) * ldo + (uint32_t)((cur.j * 256 + cg * 128) * 2 + c * 16));
             }
           }
-          // h = silu(gate) * up: 16 rows x 64 columns, staged as 128-byte rows
-#pragma unroll
-          for (int tn = 0; tn < 4; ++tn) {
-            u32x2 v;
-            v.x = pack_bf16x2(sq_silu_mul(cv[tn][0], cv[tn + 4][0]), sq_silu_mul(cv[tn][1], cv[tn + 4][1]));
-            v.y = pack_bf16x2(sq_silu_mul(cv[tn][2], cv[tn + 4][2]), sq_silu_mul(cv[tn][3], cv[tn + 4][3]));
-            const int b = tn * 32 + 8 * (el >> 4);
-            *reinterpret_cast<u32x2*>(so + 2048 + r * 128 + ((((b >> 4) ^ (r & 7))) << 4) + (b & 15)) = v;
-          }
-#pragma unroll
-          for (int p = 0; p < 2; ++p) {
-            const int rr = p * 8 + (el >> 3), c = el & 7;
-            const u32x4 v = *reinterpret_cast<const u32x4*>(so + 2048 + rr * 128 + ((c ^ (rr & 7)) << 4));
-            buf_store16(v, ro, (uint32_t)(tm * 16 + rr) * ldo + (uint32_t)((cur.j * 128 + cg * 64) * 2 + c * 16));
-          }
-        } else {
-#pragma unroll
-          for (int tn = 0; tn < 8; ++tn) {
-            u32x2 v;
-            v.x = pack_bf16x2(cv[tn][0], cv[tn][1]);
-            v.y = pack_bf16x2(cv[tn][2], cv[tn][3]);
-            *reinterpret_cast<u32x2*>(so + st256(r, tn * 32 + 8 * (el >> 4))) = v;
-          }
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            const int rr = p * 4 + (el >> 4), c = el & 15;
-            const u32x4 v = *reinterpret_cast<const u32x4*>(so + st256(rr, c * 16));
-            buf_store16(v, ro, (uint32_t)(tm * 16 + rr) * ldo + (uint32_t)((cur.j * 256 + cg * 128) * 2 + c * 16));
-          }
         }
+      } else {
+        // Software-pipelined over the eight MFMA rows: row tm's accumulators are read and
+        // converted while the staging reads of row tm - 1 are in flight; then row tm - 1 is
+        // stored and row tm staged. (A wave's LDS accesses execute in order, so row tm's
+        // staging writes cannot overtake row tm - 1's reads of the same bytes.)
+        // GEMM A: h = silu(gate) * up, 16 rows x 64 columns as 128-byte staging rows (4 x 8
+        // bytes a lane, read back as 2 x 16); GEMM Y: 16 rows x 128 columns as 256-byte rows
+        // (8 x 8 bytes a lane, read back as 4 x 16).
+        constexpr int NP = GEMM_A ? 4 : 8;
+        constexpr int NR = GEMM_A ? 2 : 4;
+        auto prep = [&](int tm, u32x2(&pk)[NP]) __attribute__((always_inline)) {
+          f32x4_t cv[8];
+#pragma unroll
+          for (int tn = 0; tn < 8; ++tn) cv[tn] = acc_read(acc[tm][tn]);
+#pragma unroll
+          for (int tn = 0; tn < NP; ++tn) {
+            if constexpr (GEMM_A) {
+              pk[tn].x = pack_bf16x2(sq_silu_mul(cv[tn][0], cv[tn + 4][0]), sq_silu_mul(cv[tn][1], cv[tn + 4][1]));
+              pk[tn].y = pack_bf16x2(sq_silu_mul(cv[tn][2], cv[tn + 4][2]), sq_silu_mul(cv[tn][3], cv[tn + 4][3]));
+            } else {
+              pk[tn].x = pack_bf16x2(cv[tn][0], cv[tn][1]);
+              pk[tn].y = pack_bf16x2(cv[tn][2], cv[tn][3]);
+            }
+          }
+        };
+        auto stage = [&](const u32x2(&pk)[NP]) __attribute__((always_inline)) {
+#pragma unroll
+          for (int tn = 0; tn < NP; ++tn) {
+            const int b = tn * 32 + 8 * (el >> 4);
+            if constexpr (GEMM_A)
+              *reinterpret_cast<u32x2*>(so + 2048 + r * 128 + ((((b >> 4) ^ (r & 7))) << 4) + (b & 15)) = pk[tn];
+            else
+              *reinterpret_cast<u32x2*>(so + st256(r, b)) = pk[tn];
+          }
+        };
+        auto fetch = [&](u32x4(&v)[NR]) __attribute__((always_inline)) {
+#pragma unroll
+          for (int p = 0; p < NR; ++p) {
+            if constexpr (GEMM_A) {
+              const int rr = p * 8 + (el >> 3), c = el & 7;
+              v[p] = *reinterpret_cast<const u32x4*>(so + 2048 + rr * 128 + ((c ^ (rr & 7)) << 4));
+            } else {
+              const int rr = p * 4 + (el >> 4), c = el & 15;
+              v[p] = *reinterpret_cast<const u32x4*>(so + st256(rr, c * 16));
+            }
+          }
+        };
+        auto put = [&](int tm, const u32x4(&v)[NR]) __attribute__((always_inline)) {
+#pragma unroll
+          for (int p = 0; p < NR; ++p) {
+            if constexpr (GEMM_A) {
+              const int rr = p * 8 + (el >> 3), c = el & 7;
+              buf_store16(v[p], ro, (uint32_t)(tm * 16 + rr) * ldo + (uint32_t)((cur.j * 128 + cg * 64) * 2 + c * 16));
+            } else {
+              const int rr = p * 4 + (el >> 4), c = el & 15;
+              buf_store16(v[p], ro, (uint32_t)(tm * 16 + rr) * ldo + (uint32_t)((cur.j * 256 + cg * 128) * 2 + c * 16));
+            }
+          }
+        };
+        u32x2 pk[NP];
+        u32x4 v[NR];
+        prep(0, pk);
+        stage(pk);
+        fetch(v);
+#pragma unroll
+        for (int tm = 1; tm < 8; ++tm) {
+          __builtin_amdgcn_sched_barrier(0);
+          prep(tm, pk);
+          put(tm - 1, v);
+          stage(pk);
+          fetch(v);
+        }
+        put(7, v);
       }
     }
     if (!has_next) break;
