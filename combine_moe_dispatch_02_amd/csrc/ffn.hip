@@ -119,6 +119,9 @@ __device__ inline float silu_mul(float g, float u) { return g * __builtin_amdgcn
 // pairs). Persistent workgroups are dealt to XCDs
 // round-robin by the dispatcher (workgroup g runs on XCD g % 8), so slot(g)
 // gives each XCD a contiguous run of units and its L2 sees the shared panel.
+// units of a big-tile workgroup whose coordinates are found up front (later ones one by one)
+constexpr int kBigUnitSlots = 64;
+
 __device__ inline void unit_coords(const FfnArgs& a, int u, int order, int& m, int& j) {
   if (order == 1) {
     m = u / a.n_units;
@@ -588,6 +591,7 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
   __shared__ float s_red[FP8 && GEMM_A && !MX ? NW : 1][FP8 && GEMM_A && !MX ? BM : 1];
   __shared__ int s_go;
   __shared__ int s_sel;
+  __shared__ int2 s_uc[kBigUnitSlots];   // (tile, N block) of this workgroup's first units
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -614,10 +618,29 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
   const int slot = unit_slot(blockIdx.x, gridDim.x);
   const int nk = a.ksteps;  // even
   if (GEMM_A && a.cq != nullptr && blockIdx.x == 0 && tid == 0) *a.cq = 0u;
+  // the coordinates of the workgroup's units slot, slot + G, ... found once, one per lane
+  // of wave 0 (each a search over the experts' offsets), so that a unit starts with one LDS
+  // read instead of a chain of dependent loads while the matrix cores idle
+  if (tid < 64) {
+    const int uu = slot + lane * (int)gridDim.x;
+    if (lane < kBigUnitSlots && uu < total) {
+      int m, j;
+      unit_coords(a, uu, order, m, j);
+      s_uc[lane] = int2{m, j};
+    }
+  }
+  __syncthreads();
 
-  for (int u = slot; u < total; u += gridDim.x) {
+  int it = 0;   // index of the unit among the workgroup's
+  for (int u = slot; u < total; u += gridDim.x, ++it) {
     int m, j;
-    unit_coords(a, u, order, m, j);
+    if (it < kBigUnitSlots) {
+      const int2 c = s_uc[it];
+      m = __builtin_amdgcn_readfirstlane(c.x);
+      j = __builtin_amdgcn_readfirstlane(c.y);
+    } else {
+      unit_coords(a, u, order, m, j);
+    }
     const int m0 = m * BM;
     const int e = a.tile_expert[m];
     if (a.wait_ready && !wait_tile_ready(a, m, &s_go)) continue;
