@@ -82,6 +82,9 @@ struct FfnArgs {
   uint32_t* abort_epoch;     // epoch of a call whose ready-flag wait timed out (its other waits end)
   uint64_t timeout;
   int32_t wait_ready;
+  // dispatch's count of raised ready flags (reset by the plan), or null: when it already
+  // equals the tile count as the big-tile kernel starts, one acquire covers every tile
+  const uint32_t* tiles_done;
   const uint8_t* A_e8;       // mxfp4: activation E8M0 scales, tile-major 4-byte words
   const uint8_t* B_e8;       // mxfp4: weight E8M0 scales in tile order, expert-major
   uint8_t* out_e8;           // mxfp4 GEMM A: h E8M0 scales, tile-major 4-byte words
@@ -592,6 +595,7 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
   __shared__ int s_go;
   __shared__ int s_sel;
   __shared__ int2 s_uc[kBigUnitSlots];   // (tile, N block) of this workgroup's first units
+  __shared__ int s_all;                  // every tile was flagged before the workgroup started
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -629,7 +633,16 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
       s_uc[lane] = int2{m, j};
     }
   }
+  // ready flags: if dispatch had raised every tile's before this workgroup started (it ran
+  // before this launch, e.g. on the same stream), one acquire covers them all and no unit
+  // polls; otherwise each unit waits on its tile's flag. One thread reads the count, so the
+  // whole workgroup takes the same branch.
+  if (tid == 0)
+    s_all = a.wait_ready && a.tiles_done != nullptr &&
+            __hip_atomic_load(a.tiles_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (uint32_t)ntiles;
   __syncthreads();
+  const bool poll_each = a.wait_ready && !s_all;
+  if (a.wait_ready && !poll_each) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
   int it = 0;   // index of the unit among the workgroup's
   for (int u = slot; u < total; u += gridDim.x, ++it) {
@@ -643,7 +656,7 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
     }
     const int m0 = m * BM;
     const int e = a.tile_expert[m];
-    if (a.wait_ready && !wait_tile_ready(a, m, &s_go)) continue;
+    if (poll_each && !wait_tile_ready(a, m, &s_go)) continue;
     if (GEMM_A && a.ydone != nullptr && j == 0 && tid == 0) a.ydone[m] = 0u;  // for GEMM Y's combine
 
     // buffer resources: uniform bases, 32-bit lane offsets, uniform per-tile/step offsets
@@ -1789,6 +1802,7 @@ int launch_expert_ffn(const FfnLaunch& f, const WsLayout& L, char* ws, hipStream
   a.bs_expert = (int64_t)(2 * I / 128) * (H / 128);
   a.out_groups = I / 128;
   a.wait_ready = 1;
+  a.tiles_done = reinterpret_cast<const uint32_t*>(ws + L.tiles_done);
   a.unit_order = bn_a == 512 ? (f.unit_order ? f.unit_order : mx ? 1 : 3) : 1;   // mxfp4: tiles then N blocks measured 1% faster
   const bool packed = f.weight_layout == MOE_WEIGHTS_MFMA_TILED;
   a.ktiles = H / (fp8 || mx ? 128 : 32);
