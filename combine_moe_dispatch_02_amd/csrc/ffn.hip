@@ -594,7 +594,7 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
   __shared__ float s_red[FP8 && GEMM_A && !MX ? NW : 1][FP8 && GEMM_A && !MX ? BM : 1];
   __shared__ int s_go;
   __shared__ int s_sel;
-  __shared__ int2 s_uc[kBigUnitSlots];   // (tile, N block) of this workgroup's first units
+  __shared__ int4 s_uc[kBigUnitSlots];   // (tile, N block, expert) of this workgroup's first units
   __shared__ int s_all;                  // every tile was flagged before the workgroup started
 
   const int tid = threadIdx.x;
@@ -622,15 +622,15 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
   const int slot = unit_slot(blockIdx.x, gridDim.x);
   const int nk = a.ksteps;  // even
   if (GEMM_A && a.cq != nullptr && blockIdx.x == 0 && tid == 0) *a.cq = 0u;
-  // the coordinates of the workgroup's units slot, slot + G, ... found once, one per lane
-  // of wave 0 (each a search over the experts' offsets), so that a unit starts with one LDS
-  // read instead of a chain of dependent loads while the matrix cores idle
+  // the coordinates and expert of the workgroup's units slot, slot + G, ... found once, one
+  // per lane of wave 0 (each a search over the experts' offsets), so that a unit starts with
+  // one LDS read instead of a chain of dependent loads while the matrix cores idle
   if (tid < 64) {
     const int uu = slot + lane * (int)gridDim.x;
     if (lane < kBigUnitSlots && uu < total) {
       int m, j;
       unit_coords(a, uu, order, m, j);
-      s_uc[lane] = int2{m, j};
+      s_uc[lane] = int4{m, j, a.tile_expert[m], 0};
     }
   }
   // ready flags: if dispatch had raised every tile's before this workgroup started (it ran
@@ -646,16 +646,17 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
 
   int it = 0;   // index of the unit among the workgroup's
   for (int u = slot; u < total; u += gridDim.x, ++it) {
-    int m, j;
+    int m, j, e;
     if (it < kBigUnitSlots) {
-      const int2 c = s_uc[it];
+      const int4 c = s_uc[it];
       m = __builtin_amdgcn_readfirstlane(c.x);
       j = __builtin_amdgcn_readfirstlane(c.y);
+      e = __builtin_amdgcn_readfirstlane(c.z);
     } else {
       unit_coords(a, u, order, m, j);
+      e = a.tile_expert[m];
     }
     const int m0 = m * BM;
-    const int e = a.tile_expert[m];
     if (poll_each && !wait_tile_ready(a, m, &s_go)) continue;
     if (GEMM_A && a.ydone != nullptr && j == 0 && tid == 0) a.ydone[m] = 0u;  // for GEMM Y's combine
 
