@@ -633,15 +633,24 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_big_kernel(FfnArgs a) {
       s_uc[lane] = int4{m, j, a.tile_expert[m], 0};
     }
   }
-  // ready flags: if dispatch had raised every tile's before this workgroup started (it ran
-  // before this launch, e.g. on the same stream), one acquire covers them all and no unit
-  // polls; otherwise each unit waits on its tile's flag. One thread reads the count, so the
-  // whole workgroup takes the same branch.
+  // ready flags: if the producer had raised every tile's before this workgroup started (it
+  // ran before this launch, e.g. on the same stream), one acquire covers them all and no
+  // unit polls; otherwise each unit waits on its tile's flag. Forward GEMM A reads
+  // dispatch's count of raised flags (one thread, so the whole workgroup takes the same
+  // branch); without a count (the backward's flags) the workgroup reads every tile's flag
+  // once and takes the shortcut only if all of them carry this call's epoch.
   if (tid == 0)
     s_all = a.wait_ready && a.tiles_done != nullptr &&
             __hip_atomic_load(a.tiles_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (uint32_t)ntiles;
   __syncthreads();
-  const bool poll_each = a.wait_ready && !s_all;
+  bool all_ready = s_all != 0;
+  if (a.wait_ready && a.tiles_done == nullptr) {
+    int mine = 1;
+    for (int t = tid; t < ntiles; t += 64 * NW)
+      mine &= __hip_atomic_load(&a.tile_ready[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch;
+    all_ready = __syncthreads_and(mine) != 0;
+  }
+  const bool poll_each = a.wait_ready && !all_ready;
   if (a.wait_ready && !poll_each) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
   int it = 0;   // index of the unit among the workgroup's
