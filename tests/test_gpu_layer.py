@@ -218,3 +218,26 @@ def test_layer_unit_rows_agree(cfg):
     err = rel_err(out_rows_f64(got), oracle.moe_layer(inp).out)
     print(f"{cfg.name}: max-norm rel err {err:.3e}")
     assert err <= TOL[cfg.dtype]
+
+
+MANY_UNITS = [
+    MoEConfig("sq_many", 2000, 1024, 512, 8, 0, 8, 4, 128),            # 256-row units, ~140 per GEMM
+    MoEConfig("fp8_many", 2000, 1024, 512, 8, 0, 8, 4, 128, "fp8"),    # big-tile kernel, ~250 GEMM A units
+    MoEConfig("mx_many", 2000, 1024, 512, 8, 0, 8, 4, 128, "mxfp4"),
+]
+
+
+@pytest.mark.parametrize("cfg", MANY_UNITS, ids=[c.name for c in MANY_UNITS])
+def test_layer_one_workgroup_walks_every_unit(cfg):
+    # with a one-workgroup GEMM grid the workgroup walks more units than its table of units
+    # decoded at start holds (64), so the later ones are found one by one: the same bits as
+    # the full grid, and within tolerance of the oracle
+    import combine_moe_dispatch_02_amd as moe
+    inp = make_inputs(cfg)
+    d = dev_inputs(inp)
+    say("one-workgroup grid", cfg.name)
+    ref = run_layer(make_layer(cfg), d).clone()
+    got = run_layer(make_layer(cfg, cfg=moe.TileConfig(0, 1, 0, 0, 0)), d)
+    assert torch.equal(ref.view(torch.int16), got.view(torch.int16))
+    want = oracle.moe_layer(inp)
+    assert rel_err(out_rows_f64(got), want.out) <= TOL[cfg.dtype]
